@@ -1,0 +1,203 @@
+"""fp64 CPU oracle for the Mamba-2 SSD chunked prefill.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library never
+imports, links or calls it, and it shares no code with the HIP library.
+
+* ``recurrence``  -- the definition: the sequential per-token recurrence (C, fp64).
+* ``chunked``     -- the five-step chunked algorithm with its intermediates (C, fp64).
+* ``quadratic``   -- the brute-force masked-matrix form (numpy, fp64, tiny inputs).
+
+Inputs may be torch CPU tensors or numpy arrays; 16-bit tensors are passed to C
+as their raw bits and widened exactly there.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from .quadratic import ssd_quadratic  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB = os.path.join(_HERE, "libssd_oracle.so")
+
+_DT_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def build(force=False):
+    """Compile the C oracle with gcc (OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared",
+               "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int), ("seqlen", ctypes.c_int), ("nheads", ctypes.c_int),
+        ("headdim", ctypes.c_int), ("dstate", ctypes.c_int), ("ngroups", ctypes.c_int),
+        ("in_dtype", ctypes.c_int), ("state_dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int),
+        ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p), ("D", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p), ("h0", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.ssd_oracle_recurrence.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(ctypes.c_int),
+                                              ctypes.c_int, dp, dp, ctypes.c_int, dp]
+        lib.ssd_oracle_recurrence.restype = ctypes.c_int
+        lib.ssd_oracle_chunked.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int, dp, dp, dp, dp, dp, dp, dp]
+        lib.ssd_oracle_chunked.restype = ctypes.c_int
+        lib.ssd_oracle_widen.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_long, dp]
+        lib.ssd_oracle_widen.restype = None
+        lib.ssd_oracle_num_threads.argtypes = []
+        lib.ssd_oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads():
+    return _load().ssd_oracle_num_threads()
+
+
+def _dtype_name(a):
+    """Element dtype name of a torch tensor or numpy array."""
+    s = str(a.dtype)
+    if "bfloat16" in s:
+        return "bf16"
+    if "float16" in s:
+        return "f16"
+    if "float32" in s:
+        return "f32"
+    raise TypeError("unsupported dtype %s" % s)
+
+
+def _raw(a, keep):
+    """Contiguous host buffer holding the element bits of ``a``; returns its address."""
+    if a is None:
+        return None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            t = a.detach().cpu().contiguous()
+            if t.dtype in (torch.bfloat16, torch.float16):
+                arr = t.view(torch.int16).numpy()
+            else:
+                arr = t.numpy()
+            keep.append(arr)
+            return arr.ctypes.data
+    except ImportError:  # pragma: no cover
+        pass
+    arr = np.ascontiguousarray(a)
+    keep.append(arr)
+    return arr.ctypes.data
+
+
+def _f32(a, keep):
+    if a is None:
+        return None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            arr = a.detach().cpu().to(torch.float32).contiguous().numpy()
+            keep.append(arr)
+            return arr.ctypes.data
+    except ImportError:  # pragma: no cover
+        pass
+    arr = np.ascontiguousarray(a, dtype=np.float32)
+    keep.append(arr)
+    return arr.ctypes.data
+
+
+def _problem(x, dt, A, B, C, D, dt_bias, h0, dt_softplus, keep):
+    Bt, L, H, P = (int(s) for s in x.shape)
+    G, N = int(B.shape[2]), int(B.shape[3])
+    in_dt = _dtype_name(x)
+    for t in (dt, B, C):
+        if _dtype_name(t) != in_dt:
+            raise TypeError("x, dt, B and C must share one dtype")
+    st_dt = _dtype_name(h0) if h0 is not None else "f32"
+    pr = _Problem(Bt, L, H, P, N, G, _DT_CODE[in_dt], _DT_CODE[st_dt], 1 if dt_softplus else 0,
+                  _raw(x, keep), _raw(dt, keep), _f32(A, keep), _raw(B, keep), _raw(C, keep),
+                  _f32(D, keep), _f32(dt_bias, keep), _raw(h0, keep))
+    return pr, (Bt, L, H, P, N, G)
+
+
+def _dptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def recurrence(x, dt, A, B, C, D=None, dt_bias=None, h0=None, dt_softplus=True,
+               bh=None, snap_q=0, want_y=True):
+    """Sequential fp64 recurrence for the (b, h) pairs in ``bh`` (default: all).
+
+    Returns ``(y[nbh, L, P], final[nbh, P, N], snaps)``; ``snaps`` is
+    ``[nbh, ceil(L/snap_q), P, N]`` (state after each snap_q tokens) or None."""
+    keep = []
+    pr, (Bt, L, H, P, N, G) = _problem(x, dt, A, B, C, D, dt_bias, h0, dt_softplus, keep)
+    if bh is None:
+        bh = [(b, h) for b in range(Bt) for h in range(H)]
+    flat = np.ascontiguousarray([b * H + h for (b, h) in bh], dtype=np.int32)
+    nbh = len(flat)
+    y = np.empty((nbh, L, P)) if want_y else None
+    fin = np.empty((nbh, P, N))
+    snaps = np.empty((nbh, (L + snap_q - 1) // snap_q, P, N)) if snap_q > 0 else None
+    rc = _load().ssd_oracle_recurrence(ctypes.byref(pr), flat.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+                                       nbh, _dptr(y), _dptr(fin), int(snap_q), _dptr(snaps))
+    if rc != 0:
+        raise ValueError("ssd_oracle_recurrence rejected its arguments")
+    return y, fin, snaps
+
+
+def recurrence_full(x, dt, A, B, C, D=None, dt_bias=None, h0=None, dt_softplus=True):
+    """All (b, h) pairs, reshaped to y[B, L, H, P] and final[B, H, P, N]."""
+    Bt, L, H, P = (int(s) for s in x.shape)
+    N = int(B.shape[3])
+    y, fin, _ = recurrence(x, dt, A, B, C, D, dt_bias, h0, dt_softplus)
+    return y.reshape(Bt, H, L, P).transpose(0, 2, 1, 3).copy(), fin.reshape(Bt, H, P, N)
+
+
+def chunked(x, dt, A, B, C, D=None, dt_bias=None, h0=None, dt_softplus=True, chunk_size=64):
+    """Five-step chunked fp64 evaluation; returns a dict of every intermediate."""
+    keep = []
+    pr, (Bt, L, H, P, N, G) = _problem(x, dt, A, B, C, D, dt_bias, h0, dt_softplus, keep)
+    Q = int(chunk_size)
+    nc = (L + Q - 1) // Q
+    out = {
+        "dt": np.empty((Bt, nc, H, Q)),
+        "acs": np.empty((Bt, nc, H, Q)),
+        "cb": np.empty((Bt, nc, G, Q, Q)),
+        "s": np.empty((Bt, nc, H, P, N)),
+        "states": np.empty((Bt, nc + 1, H, P, N)),
+        "y": np.empty((Bt, L, H, P)),
+        "final": np.empty((Bt, H, P, N)),
+    }
+    rc = _load().ssd_oracle_chunked(ctypes.byref(pr), Q, _dptr(out["dt"]), _dptr(out["acs"]), _dptr(out["cb"]),
+                                    _dptr(out["s"]), _dptr(out["states"]), _dptr(out["y"]), _dptr(out["final"]))
+    if rc != 0:
+        raise ValueError("ssd_oracle_chunked rejected its arguments")
+    return out
+
+
+def widen(t):
+    """Exact fp64 values of a 16-bit or fp32 tensor, decoded by the oracle's own C code."""
+    keep = []
+    code = _DT_CODE[_dtype_name(t)]
+    ptr = _raw(t, keep)
+    n = int(np.prod(t.shape))
+    out = np.empty(n)
+    _load().ssd_oracle_widen(ctypes.c_void_p(ptr), code, n, _dptr(out))
+    return out.reshape(tuple(t.shape))

@@ -1,0 +1,306 @@
+"""Pins for the fp64 oracle, each against something other than the oracle itself.
+
+Sources: the recurrence h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t,
+y_t = C_t h_t + D x_t ("Mamba-2状态空间模型的编译器优化与实现", section 1.1); the
+chunk decomposition ("Mamba 硬件感知算法", section "块分解与状态传递"); the
+quadratic / attention-like form ("Mamba 硬件感知算法", section "结构化状态空间对偶性");
+the linear-attention special case ("Mamba-2炸裂升级！…", section "未来展望与应用拓展").
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from mamba_ssd_prefill_amd.inputs import make_inputs
+
+REL = 1e-12
+
+
+def f64(t):
+    """Independent widening through torch (not the oracle's decoder)."""
+    return None if t is None else t.detach().to(torch.float64).numpy()
+
+
+def rel_err(a, b):
+    scale = max(np.max(np.abs(b)), 1e-300)
+    return np.max(np.abs(a - b)) / scale
+
+
+def small(seed=0, Bt=2, L=37, H=4, P=3, N=5, G=2, dtype="f32", h0=True, dt_scale=1.0, **kw):
+    inp = make_inputs(Bt, L, H, P, N, G, dtype=dtype, state_dtype="f32", has_h0=h0, seed=seed, **kw)
+    if dt_scale != 1.0:
+        # push the per-head step sizes up so decays inside a chunk are substantial
+        inp.dt_bias = inp.dt_bias + math.log(dt_scale)
+    return inp
+
+
+def quad(inp):
+    return __import__("oracle").ssd_quadratic(
+        f64(inp.x), f64(inp.dt), f64(inp.A), f64(inp.B), f64(inp.C), f64(inp.D), f64(inp.dt_bias),
+        f64(inp.h0), inp.dt_softplus)
+
+
+# ---------------------------------------------------------------------------------------------
+def test_widening_matches_torch(oracle_mod):
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    for tdt in (torch.float16, torch.bfloat16):
+        t = bits.view(tdt)
+        got = oracle_mod.widen(t)
+        ref = t.to(torch.float64).numpy()
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("softplus", [True, False])
+def test_recurrence_matches_quadratic_form(oracle_mod, dtype, softplus):
+    inp = small(seed=3, dtype=dtype, dt_scale=5.0)
+    inp.dt_softplus = softplus
+    if not softplus:  # keep dt positive and moderate without softplus
+        inp.dt = (0.5 * inp.dt.float().abs()).to(inp.dt.dtype)
+        inp.dt_bias = torch.full_like(inp.dt_bias, 0.05)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    yq, finq = quad(inp)
+    assert rel_err(y, yq) < REL
+    assert rel_err(fin, finq) < REL
+
+
+@pytest.mark.parametrize("Q", [1, 2, 3, 7, 8, 16, 64, 50])
+def test_chunked_is_chunk_size_independent(oracle_mod, Q):
+    inp = small(seed=5, L=50, dt_scale=3.0)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    ch = oracle_mod.chunked(**inp.args(), chunk_size=Q)
+    assert rel_err(ch["y"], y) < REL
+    assert rel_err(ch["final"], fin) < REL
+
+
+@pytest.mark.parametrize("Q", [4, 7, 16])
+def test_chunk_entry_states_are_recurrence_states(oracle_mod, Q):
+    inp = small(seed=6, L=45, dt_scale=2.0)
+    Bt, L, H = inp.x.shape[:3]
+    ch = oracle_mod.chunked(**inp.args(), chunk_size=Q)
+    _, _, snaps = oracle_mod.recurrence(**inp.args(), snap_q=Q)
+    nc = (L + Q - 1) // Q
+    st = ch["states"]  # [B, nc+1, H, P, N]; slot c+1 = state after chunk c
+    for k, (b, h) in enumerate([(b, h) for b in range(Bt) for h in range(H)]):
+        for c in range(nc):
+            assert rel_err(st[b, c + 1, h], snaps[k, c]) < REL
+        assert rel_err(st[b, 0, h], f64(inp.h0)[b, h]) == 0.0
+
+
+def test_local_chunk_state_is_zero_start_recurrence(oracle_mod):
+    """s_c is the state a chunk reaches when the recurrence restarts from zero at its start."""
+    Q = 8
+    inp = small(seed=7, L=29, dt_scale=2.0)
+    Bt, L, H = inp.x.shape[:3]
+    ch = oracle_mod.chunked(**inp.args(), chunk_size=Q)
+    for c in range((L + Q - 1) // Q):
+        sl = slice(c * Q, min(L, (c + 1) * Q))
+        part = dict(inp.args())
+        for k in ("x", "dt", "B", "C"):
+            part[k] = part[k][:, sl].contiguous()
+        part["h0"] = None
+        _, fin, _ = oracle_mod.recurrence(**part)
+        fin = fin.reshape(Bt, H, *fin.shape[1:])
+        assert rel_err(ch["s"][:, c], fin) < REL
+
+
+def test_cumsum_and_bmm_steps_match_library_routines(oracle_mod):
+    Q = 8
+    inp = small(seed=8, L=30, dt_scale=2.0)
+    Bt, L, H = inp.x.shape[:3]
+    G = inp.B.shape[2]
+    ch = oracle_mod.chunked(**inp.args(), chunk_size=Q)
+    nc = (L + Q - 1) // Q
+    pad = nc * Q - L
+    z = f64(inp.dt) + f64(inp.dt_bias)[None, None, :]
+    d = np.logaddexp(0.0, z)
+    d = np.concatenate([d, np.zeros((Bt, pad, H))], axis=1).reshape(Bt, nc, Q, H).transpose(0, 1, 3, 2)
+    assert rel_err(ch["dt"], d) < REL
+    acs = np.cumsum(d * f64(inp.A)[None, None, :, None], axis=-1)
+    assert rel_err(ch["acs"], acs) < REL
+    Bp = np.concatenate([f64(inp.B), np.zeros((Bt, pad, G, inp.B.shape[3]))], axis=1)
+    Cp = np.concatenate([f64(inp.C), np.zeros((Bt, pad, G, inp.C.shape[3]))], axis=1)
+    for b in range(Bt):
+        for c in range(nc):
+            for g in range(G):
+                ref = Cp[b, c * Q:(c + 1) * Q, g] @ Bp[b, c * Q:(c + 1) * Q, g].T
+                assert np.max(np.abs(ch["cb"][b, c, g] - ref)) < 1e-14
+
+
+def test_decay_only_closed_form(oracle_mod):
+    """x = 0, h0 != 0: final = exp(A sum dt) h0 and y_t = exp(A sum_{k<=t} dt_k) (h0 C_t)."""
+    inp = small(seed=9, dt_scale=4.0)
+    inp.x = torch.zeros_like(inp.x)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    d = np.logaddexp(0.0, f64(inp.dt) + f64(inp.dt_bias)[None, None, :])  # [B, L, H]
+    A = f64(inp.A)
+    cum = np.cumsum(d, axis=1) * A[None, None, :]
+    h0 = f64(inp.h0)
+    G = inp.B.shape[2]
+    H = inp.x.shape[2]
+    Cg = np.repeat(f64(inp.C), H // G, axis=2)  # [B, L, H, N]
+    yref = np.exp(cum)[..., None] * np.einsum("bhpn,blhn->blhp", h0, Cg)
+    finref = np.exp(cum[:, -1])[..., None, None] * h0
+    assert rel_err(y, yref) < REL
+    assert rel_err(fin, finref) < REL
+
+
+def test_zero_step_leaves_state_unchanged(oracle_mod):
+    """dt = 0 (no softplus, zero bias): final = h0 and y_t = h0 C_t + D x_t."""
+    inp = small(seed=10)
+    inp.dt = torch.zeros_like(inp.dt)
+    inp.dt_bias = torch.zeros_like(inp.dt_bias)
+    inp.dt_softplus = False
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    H, G = inp.x.shape[2], inp.B.shape[2]
+    Cg = np.repeat(f64(inp.C), H // G, axis=2)
+    yref = np.einsum("bhpn,blhn->blhp", f64(inp.h0), Cg) + f64(inp.D)[None, None, :, None] * f64(inp.x)
+    assert np.array_equal(fin, f64(inp.h0))
+    assert rel_err(y, yref) < REL
+
+
+def test_zero_input_gives_exact_zero(oracle_mod):
+    inp = small(seed=11, h0=False)
+    inp.x = torch.zeros_like(inp.x)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    assert np.all(y == 0.0) and np.all(fin == 0.0)
+    ch = oracle_mod.chunked(**inp.args(), chunk_size=8)
+    assert np.all(ch["y"] == 0.0) and np.all(ch["final"] == 0.0)
+
+
+def test_geometric_series(oracle_mod):
+    """Constant x, B, C, dt and h0 = 0: S_t = dt x (outer) B (1 - a^t) / (1 - a), a = exp(dt A)."""
+    Bt, L, H, P, N = 1, 40, 2, 3, 4
+    x = torch.randn(1, 1, H, P, generator=torch.Generator().manual_seed(1)).expand(Bt, L, H, P).contiguous()
+    Bm = torch.randn(1, 1, 1, N, generator=torch.Generator().manual_seed(2)).expand(Bt, L, 1, N).contiguous()
+    Cm = torch.randn(1, 1, 1, N, generator=torch.Generator().manual_seed(3)).expand(Bt, L, 1, N).contiguous()
+    dt = torch.full((Bt, L, H), 0.3)
+    A = torch.tensor([-0.7, -2.5])
+    D = torch.tensor([0.5, -1.5])
+    y, fin = oracle_mod.recurrence_full(x, dt, A, Bm, Cm, D=D, dt_softplus=False)
+    dv = float(dt[0, 0, 0])  # the fp32 value actually stored
+    for h in range(H):
+        a = math.exp(dv * float(A[h]))
+        outer = dv * np.outer(f64(x)[0, 0, h], f64(Bm)[0, 0, 0])
+        for t in range(1, L + 1):
+            S = outer * (1 - a ** t) / (1 - a)
+            yt = S @ f64(Cm)[0, 0, 0] + float(D[h]) * f64(x)[0, 0, h]
+            assert rel_err(y[0, t - 1, h], yt) < 1e-11
+        assert rel_err(fin[0, h], outer * (1 - a ** L) / (1 - a)) < 1e-11
+
+
+def test_linear_attention_special_case(oracle_mod):
+    """No decay (A = 0) and dt = 1: y = tril(C B^T) x + D x, causal linear attention."""
+    inp = small(seed=12, h0=False, G=1, H=3)
+    inp.A = torch.zeros_like(inp.A)
+    inp.dt = torch.ones_like(inp.dt)
+    inp.dt_bias = torch.zeros_like(inp.dt_bias)
+    inp.dt_softplus = False
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    X, Bm, Cm = f64(inp.x), f64(inp.B), f64(inp.C)
+    for b in range(X.shape[0]):
+        M = np.tril(Cm[b, :, 0] @ Bm[b, :, 0].T)
+        for h in range(X.shape[2]):
+            ref = M @ X[b, :, h] + float(inp.D[h]) * X[b, :, h]
+            assert rel_err(y[b, :, h], ref) < REL
+            assert rel_err(fin[b, h], X[b, :, h].T @ Bm[b, :, 0]) < REL
+
+
+def test_linear_in_x_and_initial_state(oracle_mod):
+    """y and the final state are jointly linear in (x, h0).  Integer-valued x and h0 keep the
+    mixed inputs exactly representable, so the check is at fp64 rounding level."""
+    base = small(seed=13, dt_scale=2.0)
+    gen = torch.Generator().manual_seed(99)
+    ints = lambda t: torch.randint(-8, 9, t.shape, generator=gen).float()  # noqa: E731
+    x1, x2, h1, h2 = ints(base.x), ints(base.x), ints(base.h0), ints(base.h0)
+    al, be = 3.0, -2.0
+
+    def run(x, h0):
+        a = dict(base.args())
+        a["x"], a["h0"] = x, h0
+        return oracle_mod.recurrence_full(**a)
+
+    y1, f1 = run(x1, h1)
+    y2, f2 = run(x2, h2)
+    ym, fm = run(al * x1 + be * x2, al * h1 + be * h2)
+    assert rel_err(ym, al * y1 + be * y2) < 1e-11
+    assert rel_err(fm, al * f1 + be * f2) < 1e-11
+
+
+def test_state_carry_equals_one_run(oracle_mod):
+    inp = small(seed=15, L=48, dt_scale=2.0)
+    L1 = 19
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    first = dict(inp.args())
+    second = dict(inp.args())
+    for k in ("x", "dt", "B", "C"):
+        first[k] = first[k][:, :L1].contiguous()
+        second[k] = second[k][:, L1:].contiguous()
+    y1, f1 = oracle_mod.recurrence_full(**first)
+    # the carried state enters as fp32 (the state dtype): its rounding (2^-24 relative)
+    # bounds the difference, far below any error a wrong carry would make
+    second["h0"] = torch.from_numpy(f1).float()
+    y2, f2 = oracle_mod.recurrence_full(**second)
+    assert rel_err(y1, y[:, :L1]) == 0.0
+    assert rel_err(y2, y[:, L1:]) < 1e-6
+    assert rel_err(f2, fin) < 1e-6
+
+
+def test_grouped_bc_equals_replicated_per_head(oracle_mod):
+    inp = small(seed=16, H=6, G=3, dt_scale=2.0)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    rep = dict(inp.args())
+    rep["B"] = inp.B.repeat_interleave(2, dim=2).contiguous()
+    rep["C"] = inp.C.repeat_interleave(2, dim=2).contiguous()
+    yr, fr = oracle_mod.recurrence_full(**rep)
+    assert np.array_equal(y, yr) and np.array_equal(fin, fr)
+
+
+def test_batch_rows_are_independent(oracle_mod):
+    inp = small(seed=17, Bt=3, dt_scale=2.0)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    perm = [2, 0, 1]
+    pa = dict(inp.args())
+    for k in ("x", "dt", "B", "C", "h0"):
+        pa[k] = pa[k][perm].contiguous()
+    yp, fp = oracle_mod.recurrence_full(**pa)
+    assert np.array_equal(yp, y[perm]) and np.array_equal(fp, fin[perm])
+
+
+def test_single_token_by_hand(oracle_mod):
+    """L = 1: y = dt (B.C) x + exp(dt A) (h0 C) + D x, final = exp(dt A) h0 + dt x (outer) B."""
+    inp = small(seed=18, Bt=1, L=1, H=2, G=1, dt_scale=3.0)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    d = np.logaddexp(0.0, f64(inp.dt)[0, 0] + f64(inp.dt_bias))
+    for h in range(2):
+        a = math.exp(d[h] * float(inp.A[h]))
+        xv, Bv, Cv, h0 = f64(inp.x)[0, 0, h], f64(inp.B)[0, 0, 0], f64(inp.C)[0, 0, 0], f64(inp.h0)[0, h]
+        yref = d[h] * float(Bv @ Cv) * xv + a * (h0 @ Cv) + float(inp.D[h]) * xv
+        fref = a * h0 + d[h] * np.outer(xv, Bv)
+        assert rel_err(y[0, 0, h], yref) < REL
+        assert rel_err(fin[0, h], fref) < REL
+
+
+def test_sampled_pairs_match_full_run(oracle_mod):
+    inp = small(seed=19, Bt=2, H=4)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    ys, fs, _ = oracle_mod.recurrence(**inp.args(), bh=[(1, 3), (0, 2)])
+    assert np.array_equal(ys[0], y[1, :, 3]) and np.array_equal(ys[1], y[0, :, 2])
+    assert np.array_equal(fs[0], fin[1, 3]) and np.array_equal(fs[1], fin[0, 2])
+
+
+def test_golden_hand_example(oracle_mod):
+    """The fixture in tests/golden/hand_example.json is worked out by hand from the recurrence."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+    with open(path) as f:
+        g = json.load(f)
+    t = lambda k: torch.tensor(g[k], dtype=torch.float32)  # noqa: E731
+    y, fin = oracle_mod.recurrence_full(t("x"), t("dt"), t("A"), t("B"), t("C"), D=t("D"),
+                                        dt_softplus=False)
+    assert np.allclose(y, np.array(g["y"]), rtol=0, atol=1e-12)
+    assert np.allclose(fin, np.array(g["final"]), rtol=0, atol=1e-12)
