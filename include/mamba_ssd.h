@@ -1,0 +1,183 @@
+/*
+ * mamba_ssd.h -- C ABI of libmamba_ssd.so: the Mamba-2 SSD (state space duality)
+ * chunked prefill forward on AMD MI355X (gfx950).
+ *
+ * What it computes ("Mamba-2状态空间模型的编译器优化与实现", section 1.1, with the
+ * Mamba-2 input term): for every batch row b and head h, over t = 0 .. L-1,
+ *
+ *     dt_t = softplus(dt_raw[b,t,h] + dt_bias[h])            (dt_softplus = 1)
+ *     S    = exp(dt_t * A[h]) * S + dt_t * x[b,t,h,:] (outer) B[b,t,g,:]      S is [P, N]
+ *     y[b,t,h,:] = S . C[b,t,g,:] + D[h] * x[b,t,h,:]
+ *
+ * starting from S = initial_state[b,h] (or 0) and ending with final_state[b,h] = S.
+ * Head h reads B/C group g = h / (H / G).  The library evaluates it with the chunked
+ * algorithm ("Mamba 硬件感知算法", section "块分解与状态传递"; the five steps of
+ * "Mamba-2炸裂升级！…", section "Mamba-2核心操作与融合的必要性"): chunk_cumsum, bmm,
+ * chunk_state, state_passing, chunk_scan, either as five kernels (SSD_IMPL_UNFUSED)
+ * or as one kernel whose workgroups claim cumsum and bmm work first and then
+ * chunk_state -> state_passing -> chunk_scan work, ordered by per-chunk flags
+ * (SSD_IMPL_FUSED; same write-up, section "高效内核融合技术揭秘").
+ *
+ * Conventions for every entry point:
+ *   - every tensor pointer is a DEVICE pointer to a contiguous row-major array
+ *     owned by the caller; the library never allocates, frees or keeps them;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream); all
+ *     GPU work is enqueued on it asynchronously and nothing synchronises, except
+ *     ssd_check_device_status;
+ *   - arguments are validated on the host before any HIP call; a failed check
+ *     returns an error status and enqueues nothing;
+ *   - the library never aborts or throws across this ABI;
+ *   - calls are thread-safe; two calls in flight at once need distinct workspaces.
+ */
+#ifndef MAMBA_SSD_H
+#define MAMBA_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+/* Element types.  x, dt, B, C and y share `in_dtype`; initial_state, final_state
+ * and the inter-chunk states use `state_dtype`; A, D and dt_bias are always fp32. */
+typedef enum { SSD_F32 = 0, SSD_F16 = 1, SSD_BF16 = 2 } ssd_dtype_t;
+
+typedef enum { SSD_IMPL_UNFUSED = 0, SSD_IMPL_FUSED = 1 } ssd_impl_t;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+    SSD_ERR_INVALID_SHAPE = 2,       /* a size is < 1, or nheads % ngroups != 0, or an index would overflow */
+    SSD_ERR_UNSUPPORTED = 3,         /* a legal but unsupported headdim / dstate / chunk_size / dtype combination */
+    SSD_ERR_MISALIGNED = 4,          /* a pointer breaks the alignment rule below */
+    SSD_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < ssd_prefill_workspace_size() */
+    SSD_ERR_HIP = 6,                 /* a HIP runtime call or kernel launch failed */
+    SSD_ERR_SYNC_TIMEOUT = 7,        /* fused kernel: a cross-workgroup wait hit its spin limit (results invalid) */
+    SSD_ERR_INVALID_ARGUMENT = 8     /* an enum field is out of range, or struct_size is too small */
+} ssd_status_t;
+
+/* Problem description.  Set struct_size = sizeof(ssd_params_t). */
+typedef struct {
+    size_t struct_size;
+    int batch;        /* B  >= 1 */
+    int seqlen;       /* L  >= 1; need not be a multiple of chunk_size (the last chunk is masked) */
+    int nheads;       /* H  >= 1 */
+    int headdim;      /* P in {16, 32, 64, 128} */
+    int dstate;       /* N in {32, 64, 128} (also 16 when in_dtype is SSD_F32) */
+    int ngroups;      /* G >= 1, H % G == 0 */
+    int chunk_size;   /* Q in {64, 128, 192, 256} */
+    int in_dtype;     /* ssd_dtype_t */
+    int state_dtype;  /* ssd_dtype_t */
+    int dt_softplus;  /* 1: dt = softplus(dt_raw + dt_bias); 0: dt = dt_raw + dt_bias */
+    int impl;         /* ssd_impl_t */
+} ssd_params_t;
+
+/*
+ * Tensor arguments (all device pointers):
+ *   x             [B, L, H, P]  in_dtype     required, 16-byte aligned
+ *   dt            [B, L, H]     in_dtype     required (raw step, before bias / softplus)
+ *   A             [H]           fp32         required; A <= 0 is a precondition (not checked;
+ *                                            A = 0 gives causal linear attention)
+ *   B, C          [B, L, G, N]  in_dtype     required, 16-byte aligned
+ *   D             [H]           fp32         NULL means 0
+ *   dt_bias       [H]           fp32         NULL means 0
+ *   initial_state [B, H, P, N]  state_dtype  NULL means 0; 16-byte aligned
+ *   y             [B, L, H, P]  in_dtype     required output, 16-byte aligned
+ *   final_state   [B, H, P, N]  state_dtype  required output, 16-byte aligned
+ *   workspace     bytes         -            required, 256-byte aligned, at least
+ *                                            ssd_prefill_workspace_size() bytes; its contents
+ *                                            need no initialisation and are overwritten
+ */
+
+/* Bytes of workspace ssd_prefill needs for *p (0 if *p is invalid: see ssd_validate). */
+size_t ssd_prefill_workspace_size(const ssd_params_t* p);
+
+/* Host-only check of *p (shape, support and enum rules above).  Makes no HIP call. */
+ssd_status_t ssd_validate(const ssd_params_t* p);
+
+/* One SSD prefill: y and final_state from the inputs, enqueued on `stream`. */
+ssd_status_t ssd_prefill(const ssd_params_t* p,
+                         const void* x, const void* dt, const float* A,
+                         const void* B, const void* C,
+                         const float* D, const float* dt_bias,
+                         const void* initial_state,
+                         void* y, void* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronises `stream`, then reads the device status word the last fused
+ * ssd_prefill on `workspace` left: SSD_OK, or SSD_ERR_SYNC_TIMEOUT when one of its
+ * waits gave up (its outputs are then invalid).  SSD_ERR_HIP if a HIP call fails. */
+ssd_status_t ssd_check_device_status(const ssd_params_t* p, const void* workspace, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ssd_status_string(ssd_status_t s);
+
+/* ------------------------------------------------------------------------------------
+ * Workspace layout, for the per-step entry points below and for tests that read the
+ * intermediates.  Offsets are in bytes from the workspace start; nc = ceil(L / Q).
+ *   dt      fp32 [B][nc][H][Q]       step size per token (0 past seqlen)       chunk_cumsum
+ *   acs     fp32 [B][nc][H][Q]       inclusive in-chunk sum of dt * A            chunk_cumsum
+ *   cb      fp32 [B][nc][G][Q][Q]    CB[i][j] = C_i . B_j for j <= i; entries
+ *                                    with j > i are never written nor read      bmm
+ *   s       fp32 [B][nc][H][P][N]    chunk-end state from a zero start
+ *                                    (unfused only; 0 bytes when fused)          chunk_state
+ *   states  state_dtype [B][K][H][P][N]  state entering chunk c lives in slot c % K;
+ *                                    K = nc + 1 unfused, a small ring (K = 2) fused;
+ *                                    slot 0 holds the initial state and slot nc % K
+ *                                    the final state                            state_passing
+ *   sync    uint32 words: per-chain chunk flags, cumsum / bmm completion flags,
+ *           the work ticket and the abort word (fused only)
+ *   status  uint32 device status word
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+    size_t total_bytes;
+    size_t dt_offset, acs_offset, cb_offset, s_offset, states_offset, sync_offset, status_offset;
+    size_t dt_bytes, acs_bytes, cb_bytes, s_bytes, states_bytes, sync_bytes;
+    int nchunks;
+    int state_slots;  /* K */
+} ssd_workspace_layout_t;
+
+ssd_status_t ssd_workspace_layout(const ssd_params_t* p, ssd_workspace_layout_t* out);
+
+/* ------------------------------------------------------------------------------------
+ * The five steps of the unfused form, one entry point each, with the same argument
+ * rules as ssd_prefill (p->impl must be SSD_IMPL_UNFUSED).  Each reads the workspace
+ * intermediates the previous steps wrote and writes its own.  Calling them in this
+ * order equals ssd_prefill with impl = SSD_IMPL_UNFUSED.
+ * ------------------------------------------------------------------------------------ */
+
+/* chunk_cumsum ("Mamba-2炸裂升级！…", section "Mamba-2核心操作与融合的必要性", item 4):
+ * per-token dt and its in-chunk cumulative decay -> workspace dt, acs. */
+ssd_status_t ssd_step_chunk_cumsum(const ssd_params_t* p, const void* dt, const float* A,
+                                   const float* dt_bias, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* bmm (same section, item 7): CB = C B^T inside each chunk and group -> workspace cb. */
+ssd_status_t ssd_step_bmm(const ssd_params_t* p, const void* B, const void* C,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* chunk_state (item 5): each chunk's end state from a zero start, the decay to the
+ * chunk end applied to x (same write-up, section "性能瓶颈的深入分析") -> workspace s. */
+ssd_status_t ssd_step_chunk_state(const ssd_params_t* p, const void* x, const void* B,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* state_passing (item 6): copies initial_state into slot 0, runs
+ * S_{c+1} = exp(acs_c[Q-1]) S_c + s_c over the chunks, copies the last slot to
+ * final_state (the boundary split-out of section "性能瓶颈的深入分析"). */
+ssd_status_t ssd_step_state_passing(const ssd_params_t* p, const void* initial_state,
+                                    void* final_state, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* chunk_scan (item 8): y from x, C, the chunk-entry states and CB -> y. */
+ssd_status_t ssd_step_chunk_scan(const ssd_params_t* p, const void* x, const void* C,
+                                 const float* D, void* y, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SSD_H */

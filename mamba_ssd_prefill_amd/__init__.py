@@ -1,1 +1,242 @@
-"""MI355X-native Mamba-2 SSD chunked prefill (forward): Python binding over libmamba_ssd.so."""
+"""MI355X-native Mamba-2 SSD chunked prefill (forward).
+
+A thin ctypes binding over libmamba_ssd.so (C ABI in include/mamba_ssd.h).  Every step
+of the computation runs in the library's HIP kernels; this module only marshals
+arguments.  PyTorch provides device memory and the stream.  If the library is not
+built, every call raises: there is no fallback path.
+
+    y, final_state = ssd_prefill(x, dt, A, B, C, D, dt_bias, initial_state,
+                                 chunk_size=128, impl="fused")
+"""
+import ctypes
+import os
+
+__all__ = ["ssd_prefill", "workspace_size", "workspace_layout", "Params", "SSDError", "library_path",
+           "load_library", "step_chunk_cumsum", "step_bmm", "step_chunk_state", "step_state_passing",
+           "step_chunk_scan", "check_device_status", "make_params", "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("MAMBA_SSD_LIB", os.path.join(_HERE, "libmamba_ssd.so"))
+
+SSD_F32, SSD_F16, SSD_BF16 = 0, 1, 2
+DTYPE_CODES = {"f32": SSD_F32, "f16": SSD_F16, "bf16": SSD_BF16}
+IMPL_CODES = {"unfused": 0, "fused": 1}
+STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_INVALID_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
+                4: "SSD_ERR_MISALIGNED", 5: "SSD_ERR_WORKSPACE_TOO_SMALL", 6: "SSD_ERR_HIP",
+                7: "SSD_ERR_SYNC_TIMEOUT", 8: "SSD_ERR_INVALID_ARGUMENT"}
+EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill", "ssd_check_device_status",
+                    "ssd_status_string", "ssd_workspace_layout", "ssd_step_chunk_cumsum", "ssd_step_bmm",
+                    "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan"]
+
+
+class SSDError(RuntimeError):
+    def __init__(self, code, where=""):
+        self.code = code
+        msg = STATUS_NAMES.get(code, str(code))
+        try:
+            msg += ": " + load_library().ssd_status_string(code).decode()
+        except Exception:  # pragma: no cover
+            pass
+        super().__init__("%s%s" % (where + ": " if where else "", msg))
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_size_t), ("batch", ctypes.c_int), ("seqlen", ctypes.c_int),
+                ("nheads", ctypes.c_int), ("headdim", ctypes.c_int), ("dstate", ctypes.c_int),
+                ("ngroups", ctypes.c_int), ("chunk_size", ctypes.c_int), ("in_dtype", ctypes.c_int),
+                ("state_dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int), ("impl", ctypes.c_int)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("total_bytes", ctypes.c_size_t), ("dt_offset", ctypes.c_size_t), ("acs_offset", ctypes.c_size_t),
+                ("cb_offset", ctypes.c_size_t), ("s_offset", ctypes.c_size_t), ("states_offset", ctypes.c_size_t),
+                ("sync_offset", ctypes.c_size_t), ("status_offset", ctypes.c_size_t), ("dt_bytes", ctypes.c_size_t),
+                ("acs_bytes", ctypes.c_size_t), ("cb_bytes", ctypes.c_size_t), ("s_bytes", ctypes.c_size_t),
+                ("states_bytes", ctypes.c_size_t), ("sync_bytes", ctypes.c_size_t), ("nchunks", ctypes.c_int),
+                ("state_slots", ctypes.c_int)]
+
+
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmamba_ssd.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libmamba_ssd.so is not built (%s); run `python -m mamba_ssd_prefill_amd.build`"
+                           % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(Params)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.ssd_prefill_workspace_size.argtypes = [P]
+    lib.ssd_prefill_workspace_size.restype = sz
+    lib.ssd_validate.argtypes = [P]
+    lib.ssd_validate.restype = ctypes.c_int
+    lib.ssd_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_prefill.restype = ctypes.c_int
+    lib.ssd_check_device_status.argtypes = [P, vp, vp]
+    lib.ssd_check_device_status.restype = ctypes.c_int
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_workspace_layout.argtypes = [P, ctypes.POINTER(Layout)]
+    lib.ssd_workspace_layout.restype = ctypes.c_int
+    lib.ssd_step_chunk_cumsum.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.ssd_step_bmm.argtypes = [P, vp, vp, vp, sz, vp]
+    lib.ssd_step_chunk_state.argtypes = [P, vp, vp, vp, sz, vp]
+    lib.ssd_step_state_passing.argtypes = [P, vp, vp, vp, sz, vp]
+    lib.ssd_step_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("ssd_step_chunk_cumsum", "ssd_step_bmm", "ssd_step_chunk_state", "ssd_step_state_passing",
+              "ssd_step_chunk_scan"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t):
+    import torch
+    return {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[t.dtype]
+
+
+def make_params(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size=128, in_dtype="bf16",
+                state_dtype="f32", dt_softplus=True, impl="fused"):
+    code = lambda d: d if isinstance(d, int) else DTYPE_CODES[d]  # noqa: E731
+    return Params(ctypes.sizeof(Params), int(batch), int(seqlen), int(nheads), int(headdim), int(dstate),
+                  int(ngroups), int(chunk_size), code(in_dtype), code(state_dtype), 1 if dt_softplus else 0,
+                  IMPL_CODES[impl] if isinstance(impl, str) else int(impl))
+
+
+def _params_for(x, B, chunk_size, state_dtype_code, dt_softplus, impl):
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return make_params(Bt, L, H, P, N, G, chunk_size, _dtype_code(x), state_dtype_code, dt_softplus, impl)
+
+
+def workspace_size(params):
+    n = load_library().ssd_prefill_workspace_size(ctypes.byref(params))
+    if n == 0:
+        raise SSDError(load_library().ssd_validate(ctypes.byref(params)), "ssd_prefill_workspace_size")
+    return n
+
+
+def workspace_layout(params):
+    out = Layout()
+    rc = load_library().ssd_workspace_layout(ctypes.byref(params), ctypes.byref(out))
+    if rc:
+        raise SSDError(rc, "ssd_workspace_layout")
+    return out
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise SSDError(rc, where)
+
+
+def alloc_workspace(params, device):
+    import torch
+    return torch.empty(workspace_size(params), dtype=torch.uint8, device=device)
+
+
+def _check_tensors(x, dt, A, B, C, D, dt_bias, h0):
+    import torch
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_prefill needs device tensors (got %s)" % dev)
+    want = {"dt": (dt, (Bt, L, H)), "B": (B, (Bt, L, G, N)), "C": (C, (Bt, L, G, N)), "A": (A, (H,)),
+            "D": (D, (H,)), "dt_bias": (dt_bias, (H,)), "initial_state": (h0, (Bt, H, P, N))}
+    for name, (t, shape) in want.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+        if t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    for name, t in (("dt", dt), ("B", B), ("C", C)):
+        if t.dtype != x.dtype:
+            raise ValueError("%s must have x's dtype %s" % (name, x.dtype))
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("%s must be float32" % name)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+
+
+def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_size=128, state_dtype=None,
+                impl="fused", dt_softplus=True, workspace=None, y=None, final_state=None):
+    """Run one SSD prefill on the GPU; returns (y[B,L,H,P], final_state[B,H,P,N]).
+
+    ``state_dtype`` defaults to initial_state's dtype, else float32.  ``workspace``
+    (uint8 device tensor), ``y`` and ``final_state`` may be passed to avoid allocation."""
+    import torch
+    _check_tensors(x, dt, A, B, C, D, dt_bias, initial_state)
+    if state_dtype is None:
+        state_dtype = initial_state.dtype if initial_state is not None else torch.float32
+    sd = {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[state_dtype]
+    if initial_state is not None and initial_state.dtype != state_dtype:
+        raise ValueError("initial_state dtype %s != state_dtype %s" % (initial_state.dtype, state_dtype))
+    prm = _params_for(x, B, chunk_size, sd, dt_softplus, impl)
+    Bt, L, H, P = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None:
+        final_state = torch.empty((Bt, H, P, N), dtype=state_dtype, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(prm, x.device)
+    rc = load_library().ssd_prefill(ctypes.byref(prm), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(dt_bias), _ptr(initial_state), _ptr(y), _ptr(final_state),
+                                    _ptr(workspace), workspace.numel(), _stream(x.device))
+    _check(rc, "ssd_prefill")
+    return y, final_state
+
+
+def check_device_status(params, workspace):
+    rc = load_library().ssd_check_device_status(ctypes.byref(params), _ptr(workspace), _stream(workspace.device))
+    return rc
+
+
+# ---- per-step entry points (unfused form) ------------------------------------------------------
+def step_chunk_cumsum(params, dt, A, dt_bias, workspace):
+    _check(load_library().ssd_step_chunk_cumsum(ctypes.byref(params), _ptr(dt), _ptr(A), _ptr(dt_bias),
+                                                _ptr(workspace), workspace.numel(), _stream(dt.device)),
+           "ssd_step_chunk_cumsum")
+
+
+def step_bmm(params, B, C, workspace):
+    _check(load_library().ssd_step_bmm(ctypes.byref(params), _ptr(B), _ptr(C), _ptr(workspace), workspace.numel(),
+                                       _stream(B.device)), "ssd_step_bmm")
+
+
+def step_chunk_state(params, x, B, workspace):
+    _check(load_library().ssd_step_chunk_state(ctypes.byref(params), _ptr(x), _ptr(B), _ptr(workspace),
+                                               workspace.numel(), _stream(x.device)), "ssd_step_chunk_state")
+
+
+def step_state_passing(params, initial_state, final_state, workspace):
+    _check(load_library().ssd_step_state_passing(ctypes.byref(params), _ptr(initial_state), _ptr(final_state),
+                                                 _ptr(workspace), workspace.numel(), _stream(workspace.device)),
+           "ssd_step_state_passing")
+
+
+def step_chunk_scan(params, x, C, D, y, workspace):
+    _check(load_library().ssd_step_chunk_scan(ctypes.byref(params), _ptr(x), _ptr(C), _ptr(D), _ptr(y),
+                                              _ptr(workspace), workspace.numel(), _stream(x.device)),
+           "ssd_step_chunk_scan")

@@ -1,0 +1,353 @@
+// ssd_api.cpp -- the C ABI declared in include/mamba_ssd.h: argument validation (host
+// only, before any HIP call), workspace carve-up and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/mamba_ssd.h"
+#include "ssd_launch.h"
+
+#define SSD_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kRingSlots = 2;        // fused form: states ring depth
+constexpr size_t kAlign = 256;       // workspace region alignment
+constexpr uint32_t kDefaultSpin = 1u << 22;
+
+size_t elem_size(int dt) { return dt == SSD_F32 ? 4 : 2; }
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+uint32_t spin_limit() {
+    static const uint32_t v = [] {
+        const char* e = getenv("MAMBA_SSD_SPIN_LIMIT");
+        if (!e || !*e) return kDefaultSpin;
+        const unsigned long x = strtoul(e, nullptr, 10);
+        return x ? (uint32_t)(x > 0xffffffffUL ? 0xffffffffUL : x) : kDefaultSpin;
+    }();
+    return v;
+}
+
+struct Layout {
+    ssd_workspace_layout_t w;
+    size_t nflags, nsync;  // sync words: [flags | cs_done | bmm_done | ticket | abort | status]
+    size_t flags_w, cs_w, bmm_w, ticket_w, abort_w, status_w;
+    int tpg, wph;
+};
+
+ssd_status_t validate(const ssd_params_t* p) {
+    if (!p) return SSD_ERR_NULL_POINTER;
+    if (p->struct_size < sizeof(ssd_params_t)) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->in_dtype < SSD_F32 || p->in_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->state_dtype < SSD_F32 || p->state_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->impl != SSD_IMPL_UNFUSED && p->impl != SSD_IMPL_FUSED) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->dt_softplus != 0 && p->dt_softplus != 1) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->batch < 1 || p->seqlen < 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1 || p->ngroups < 1 ||
+        p->chunk_size < 1)
+        return SSD_ERR_INVALID_SHAPE;
+    if (p->nheads % p->ngroups) return SSD_ERR_INVALID_SHAPE;
+    const int P = p->headdim, N = p->dstate, Q = p->chunk_size;
+    if (P != 16 && P != 32 && P != 64 && P != 128) return SSD_ERR_UNSUPPORTED;
+    if (N != 32 && N != 64 && N != 128 && !(N == 16 && p->in_dtype == SSD_F32)) return SSD_ERR_UNSUPPORTED;
+    if (Q != 64 && Q != 128 && Q != 192 && Q != 256) return SSD_ERR_UNSUPPORTED;
+    // every grid and ticket count must fit a signed 32-bit index
+    const int64_t nc = ((int64_t)p->seqlen + Q - 1) / Q;
+    const int64_t hpg = p->nheads / p->ngroups;
+    const int64_t tpg = (hpg + ssd::heads_per_tile(P) - 1) / ssd::heads_per_tile(P);
+    const int64_t tickets = (int64_t)p->batch * nc * (1 + p->ngroups + (int64_t)p->ngroups * tpg);
+    if (tickets >= (int64_t)1 << 31) return SSD_ERR_INVALID_SHAPE;
+    if ((int64_t)p->batch * p->seqlen * p->nheads >= (int64_t)1 << 40) return SSD_ERR_INVALID_SHAPE;
+    return SSD_OK;
+}
+
+Layout layout(const ssd_params_t* p) {
+    Layout l{};
+    const size_t B = p->batch, L = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups;
+    const size_t Q = p->chunk_size, nc = (L + Q - 1) / Q;
+    const bool fused = p->impl == SSD_IMPL_FUSED;
+    l.wph = ssd::waves_per_head(p->headdim);
+    const int hpt = ssd::heads_per_tile(p->headdim);
+    l.tpg = (int)((H / G + hpt - 1) / hpt);
+    const size_t K = fused ? (nc + 1 < (size_t)kRingSlots ? nc + 1 : (size_t)kRingSlots) : nc + 1;
+    ssd_workspace_layout_t& w = l.w;
+    w.nchunks = (int)nc;
+    w.state_slots = (int)K;
+    w.dt_bytes = B * nc * H * Q * 4;
+    w.acs_bytes = w.dt_bytes;
+    w.cb_bytes = B * nc * G * Q * Q * 4;
+    w.s_bytes = fused ? 0 : B * nc * H * P * N * 4;
+    w.states_bytes = B * K * H * P * N * elem_size(p->state_dtype);
+    l.nflags = fused ? B * H * (size_t)l.wph * (nc + 1) : 0;
+    l.flags_w = 0;
+    l.cs_w = l.nflags;
+    l.bmm_w = l.cs_w + (fused ? B * nc : 0);
+    l.ticket_w = l.bmm_w + (fused ? B * nc * G : 0);
+    l.abort_w = l.ticket_w + 1;
+    l.status_w = l.abort_w + 1;
+    l.nsync = l.status_w + 1;
+    w.sync_bytes = l.nsync * 4;
+    size_t off = 0;
+    w.dt_offset = off;
+    off = align_up(off + w.dt_bytes);
+    w.acs_offset = off;
+    off = align_up(off + w.acs_bytes);
+    w.cb_offset = off;
+    off = align_up(off + w.cb_bytes);
+    w.s_offset = off;
+    off = align_up(off + w.s_bytes);
+    w.states_offset = off;
+    off = align_up(off + w.states_bytes);
+    w.sync_offset = off;
+    w.status_offset = off + 4 * l.status_w;
+    off = align_up(off + w.sync_bytes);
+    w.total_bytes = off;
+    return l;
+}
+
+ssd_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return SSD_OK;
+    if (e == hipErrorNotSupported) return SSD_ERR_UNSUPPORTED;
+    return SSD_ERR_HIP;
+}
+
+hipError_t dispatch(int step, const ssd_params_t* p, ssd::SsdArgs& a, hipStream_t st) {
+    switch (p->in_dtype) {
+    case SSD_F32: return ssd::launch_step_f32(step, p->headdim, p->dstate, a, st);
+    case SSD_F16: return ssd::launch_step_f16(step, p->headdim, p->dstate, a, st);
+    default: return ssd::launch_step_bf16(step, p->headdim, p->dstate, a, st);
+    }
+}
+
+// Kernel argument block with every workspace pointer filled in; tensor pointers are set
+// by the callers.
+ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
+    ssd::SsdArgs a{};
+    char* base = (char*)ws;
+    a.dtf = (float*)(base + l.w.dt_offset);
+    a.acs = (float*)(base + l.w.acs_offset);
+    a.cb = (float*)(base + l.w.cb_offset);
+    a.s = (float*)(base + l.w.s_offset);
+    a.states = base + l.w.states_offset;
+    uint32_t* sync = (uint32_t*)(base + l.w.sync_offset);
+    a.flags = sync + l.flags_w;
+    a.cs_done = sync + l.cs_w;
+    a.bmm_done = sync + l.bmm_w;
+    a.ticket = sync + l.ticket_w;
+    a.abort_word = sync + l.abort_w;
+    a.status = sync + l.status_w;
+    a.batch = p->batch;
+    a.seqlen = p->seqlen;
+    a.nheads = p->nheads;
+    a.ngroups = p->ngroups;
+    a.chunk = p->chunk_size;
+    a.nchunks = l.w.nchunks;
+    a.hpg = p->nheads / p->ngroups;
+    a.tpg = l.tpg;
+    a.slots = l.w.state_slots;
+    a.state_dtype = p->state_dtype;
+    a.softplus = p->dt_softplus;
+    a.spin_limit = spin_limit();
+    return a;
+}
+
+ssd_status_t check_ws(const ssd_params_t* p, void* ws, size_t ws_bytes, Layout* l) {
+    ssd_status_t s = validate(p);
+    if (s != SSD_OK) return s;
+    if (!ws) return SSD_ERR_NULL_POINTER;
+    if (!aligned(ws, kAlign)) return SSD_ERR_MISALIGNED;
+    *l = layout(p);
+    if (ws_bytes < l->w.total_bytes) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    return SSD_OK;
+}
+
+size_t state_bytes_per_b(const ssd_params_t* p) {
+    return (size_t)p->nheads * p->headdim * p->dstate * elem_size(p->state_dtype);
+}
+
+// Boundary copy into slot 0 (initial state or zeros); optionally resets sync words.
+hipError_t boundary_in(const ssd_params_t* p, const Layout& l, const ssd::SsdArgs& a, const void* h0,
+                       uint32_t* sync, size_t nsync, size_t nflags, hipStream_t st) {
+    const size_t per_b = state_bytes_per_b(p);
+    return ssd::launch_boundary(h0, per_b, a.states, per_b * l.w.state_slots, per_b, p->batch, sync, nsync, nflags,
+                                (uint32_t)(l.w.nchunks + 1), st);
+}
+
+hipError_t boundary_out(const ssd_params_t* p, const Layout& l, const ssd::SsdArgs& a, void* fin, hipStream_t st) {
+    const size_t per_b = state_bytes_per_b(p);
+    const int slot = l.w.nchunks % l.w.state_slots;
+    return ssd::launch_boundary((const char*)a.states + per_b * slot, per_b * l.w.state_slots, fin, per_b, per_b,
+                                p->batch, nullptr, 0, 0, 1, st);
+}
+
+}  // namespace
+
+SSD_EXPORT ssd_status_t ssd_validate(const ssd_params_t* p) { return validate(p); }
+
+SSD_EXPORT size_t ssd_prefill_workspace_size(const ssd_params_t* p) {
+    if (validate(p) != SSD_OK) return 0;
+    return layout(p).w.total_bytes;
+}
+
+SSD_EXPORT ssd_status_t ssd_workspace_layout(const ssd_params_t* p, ssd_workspace_layout_t* out) {
+    ssd_status_t s = validate(p);
+    if (s != SSD_OK) return s;
+    if (!out) return SSD_ERR_NULL_POINTER;
+    *out = layout(p).w;
+    return SSD_OK;
+}
+
+SSD_EXPORT const char* ssd_status_string(ssd_status_t s) {
+    switch (s) {
+    case SSD_OK: return "success";
+    case SSD_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case SSD_ERR_INVALID_SHAPE: return "invalid shape (size < 1, nheads % ngroups != 0, or index overflow)";
+    case SSD_ERR_UNSUPPORTED: return "unsupported headdim / dstate / chunk_size / dtype combination";
+    case SSD_ERR_MISALIGNED: return "a pointer is not aligned as required";
+    case SSD_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than ssd_prefill_workspace_size()";
+    case SSD_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case SSD_ERR_SYNC_TIMEOUT: return "a cross-workgroup wait hit its spin limit; outputs are invalid";
+    case SSD_ERR_INVALID_ARGUMENT: return "an enum field is out of range or struct_size is too small";
+    default: return "unknown status";
+    }
+}
+
+// ---- the five unfused steps ---------------------------------------------------------------
+
+static ssd_status_t unfused_guard(const ssd_params_t* p) {
+    if (p && p->struct_size >= sizeof(ssd_params_t) && p->impl != SSD_IMPL_UNFUSED) return SSD_ERR_INVALID_ARGUMENT;
+    return SSD_OK;
+}
+
+SSD_EXPORT ssd_status_t ssd_step_chunk_cumsum(const ssd_params_t* p, const void* dt, const float* A,
+                                              const float* dt_bias, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+    Layout l;
+    ssd_status_t s = unfused_guard(p);
+    if (s == SSD_OK) s = check_ws(p, workspace, workspace_bytes, &l);
+    if (s != SSD_OK) return s;
+    if (!dt || !A) return SSD_ERR_NULL_POINTER;
+    if (!aligned(dt, elem_size(p->in_dtype)) || !aligned(A, 4) || !aligned(dt_bias, 4)) return SSD_ERR_MISALIGNED;
+    ssd::SsdArgs a = make_args(p, l, workspace);
+    a.dt = dt;
+    a.A = A;
+    a.dt_bias = dt_bias;
+    return hip_status(dispatch(ssd::STEP_CUMSUM, p, a, (hipStream_t)stream));
+}
+
+SSD_EXPORT ssd_status_t ssd_step_bmm(const ssd_params_t* p, const void* B, const void* C, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    Layout l;
+    ssd_status_t s = unfused_guard(p);
+    if (s == SSD_OK) s = check_ws(p, workspace, workspace_bytes, &l);
+    if (s != SSD_OK) return s;
+    if (!B || !C) return SSD_ERR_NULL_POINTER;
+    if (!aligned(B, 16) || !aligned(C, 16)) return SSD_ERR_MISALIGNED;
+    ssd::SsdArgs a = make_args(p, l, workspace);
+    a.B = B;
+    a.C = C;
+    return hip_status(dispatch(ssd::STEP_BMM, p, a, (hipStream_t)stream));
+}
+
+SSD_EXPORT ssd_status_t ssd_step_chunk_state(const ssd_params_t* p, const void* x, const void* B, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+    Layout l;
+    ssd_status_t s = unfused_guard(p);
+    if (s == SSD_OK) s = check_ws(p, workspace, workspace_bytes, &l);
+    if (s != SSD_OK) return s;
+    if (!x || !B) return SSD_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(B, 16)) return SSD_ERR_MISALIGNED;
+    ssd::SsdArgs a = make_args(p, l, workspace);
+    a.x = x;
+    a.B = B;
+    return hip_status(dispatch(ssd::STEP_CHUNK_STATE, p, a, (hipStream_t)stream));
+}
+
+SSD_EXPORT ssd_status_t ssd_step_state_passing(const ssd_params_t* p, const void* initial_state, void* final_state,
+                                               void* workspace, size_t workspace_bytes, void* stream) {
+    Layout l;
+    ssd_status_t s = unfused_guard(p);
+    if (s == SSD_OK) s = check_ws(p, workspace, workspace_bytes, &l);
+    if (s != SSD_OK) return s;
+    if (!final_state) return SSD_ERR_NULL_POINTER;
+    if (!aligned(initial_state, 16) || !aligned(final_state, 16)) return SSD_ERR_MISALIGNED;
+    ssd::SsdArgs a = make_args(p, l, workspace);
+    hipStream_t st = (hipStream_t)stream;
+    // initial state into slot 0, and clear the status word (the unfused form never waits)
+    hipError_t e = boundary_in(p, l, a, initial_state, a.status, 1, 0, st);
+    if (e == hipSuccess) e = ssd::launch_state_passing(a, p->headdim * p->dstate, st);
+    if (e == hipSuccess) e = boundary_out(p, l, a, final_state, st);
+    return hip_status(e);
+}
+
+SSD_EXPORT ssd_status_t ssd_step_chunk_scan(const ssd_params_t* p, const void* x, const void* C, const float* D,
+                                            void* y, void* workspace, size_t workspace_bytes, void* stream) {
+    Layout l;
+    ssd_status_t s = unfused_guard(p);
+    if (s == SSD_OK) s = check_ws(p, workspace, workspace_bytes, &l);
+    if (s != SSD_OK) return s;
+    if (!x || !C || !y) return SSD_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(D, 4)) return SSD_ERR_MISALIGNED;
+    ssd::SsdArgs a = make_args(p, l, workspace);
+    a.x = x;
+    a.C = C;
+    a.D = D;
+    a.y = y;
+    return hip_status(dispatch(ssd::STEP_CHUNK_SCAN, p, a, (hipStream_t)stream));
+}
+
+// ---- the whole prefill ----------------------------------------------------------------------
+
+SSD_EXPORT ssd_status_t ssd_prefill(const ssd_params_t* p, const void* x, const void* dt, const float* A,
+                                   const void* B, const void* C, const float* D, const float* dt_bias,
+                                   const void* initial_state, void* y, void* final_state, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    Layout l;
+    ssd_status_t s = check_ws(p, workspace, workspace_bytes, &l);
+    if (s != SSD_OK) return s;
+    if (!x || !dt || !A || !B || !C || !y || !final_state) return SSD_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(final_state, 16) ||
+        !aligned(initial_state, 16) || !aligned(dt, elem_size(p->in_dtype)) || !aligned(A, 4) || !aligned(D, 4) ||
+        !aligned(dt_bias, 4))
+        return SSD_ERR_MISALIGNED;
+    hipStream_t st = (hipStream_t)stream;
+    ssd::SsdArgs a = make_args(p, l, workspace);
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.dt_bias = dt_bias;
+    a.y = y;
+    hipError_t e;
+    if (p->impl == SSD_IMPL_FUSED) {
+        // initial state into slot 0 and every sync word (flags, counters, status) reset
+        e = boundary_in(p, l, a, initial_state, a.flags, l.nsync, l.nflags, st);
+        if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED, p, a, st);
+        if (e == hipSuccess) e = boundary_out(p, l, a, final_state, st);
+        return hip_status(e);
+    }
+    e = dispatch(ssd::STEP_CUMSUM, p, a, st);
+    if (e == hipSuccess) e = dispatch(ssd::STEP_BMM, p, a, st);
+    if (e == hipSuccess) e = dispatch(ssd::STEP_CHUNK_STATE, p, a, st);
+    if (e == hipSuccess) e = boundary_in(p, l, a, initial_state, a.status, 1, 0, st);
+    if (e == hipSuccess) e = ssd::launch_state_passing(a, p->headdim * p->dstate, st);
+    if (e == hipSuccess) e = boundary_out(p, l, a, final_state, st);
+    if (e == hipSuccess) e = dispatch(ssd::STEP_CHUNK_SCAN, p, a, st);
+    return hip_status(e);
+}
+
+SSD_EXPORT ssd_status_t ssd_check_device_status(const ssd_params_t* p, const void* workspace, void* stream) {
+    ssd_status_t s = validate(p);
+    if (s != SSD_OK) return s;
+    if (!workspace) return SSD_ERR_NULL_POINTER;
+    const Layout l = layout(p);
+    uint32_t word = 0;
+    hipStream_t st = (hipStream_t)stream;
+    if (hipStreamSynchronize(st) != hipSuccess) return SSD_ERR_HIP;
+    if (hipMemcpy(&word, (const char*)workspace + l.w.status_offset, 4, hipMemcpyDeviceToHost) != hipSuccess)
+        return SSD_ERR_HIP;
+    return word == 0 ? SSD_OK : (ssd_status_t)word;
+}

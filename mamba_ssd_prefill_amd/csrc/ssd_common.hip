@@ -1,0 +1,68 @@
+// ssd_common.hip -- the dtype-independent kernels: state_passing of the unfused form and
+// the boundary copies shared by both forms.
+#include "ssd_device.h"
+
+namespace ssd {
+
+// state_passing ("Mamba-2炸裂升级！…", section "Mamba-2核心操作与融合的必要性", item 6):
+// one thread per 4 consecutive state elements of one (b, h), sequential over the chunks:
+// S_{c+1} = exp(acs_c[Q-1]) S_c + s_c, carried in fp32 and stored to slot c + 1 in the
+// state dtype.  Slot 0 holds the initial state (written by the boundary copy).
+__global__ __launch_bounds__(256) void k_state_passing(SsdArgs a, int PN) {
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= PN) return;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int H = a.nheads, nc = a.nchunks, Q = a.chunk, K = a.slots;
+    f32x4 S = load_state4(a.states, a.state_dtype, ((size_t)b * K * H + h) * PN + e);
+#pragma unroll 4
+    for (int c = 0; c < nc; ++c) {
+        const float dec = __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
+        const f32x4 sl = *(const f32x4*)(a.s + (((size_t)b * nc + c) * H + h) * PN + e);
+        S = dec * S + sl;
+        store_state4(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);
+    }
+}
+
+// Boundary copies (same write-up, section "性能瓶颈的深入分析": the initial state goes into
+// chunk 0's slot and the final state comes out of the last chunk's slot, outside the
+// fused kernel).  Copies bytes_per_b bytes per batch row from src (batch stride src_bs)
+// to dst (batch stride dst_bs), 16 bytes per thread; src == nullptr writes zeros.  Also
+// resets nsync sync words: word i becomes 1 when i < nflags and i % flag_period == 0
+// (chunk 0's flag of every chain: the initial state is ready), else 0.
+__global__ __launch_bounds__(256) void k_boundary(const char* src, size_t src_bs, char* dst, size_t dst_bs,
+                                                   size_t bytes_per_b, int batch, uint32_t* sync, size_t nsync,
+                                                   size_t nflags, uint32_t flag_period) {
+    const size_t n16 = bytes_per_b / 16;
+    const size_t total = n16 * (size_t)batch;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const size_t b = i / n16, k = i % n16;
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (src) v = *(const uint4*)(src + b * src_bs + k * 16);
+        *(uint4*)(dst + b * dst_bs + k * 16) = v;
+    }
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsync; i += stride)
+        sync[i] = (i < nflags && (i % flag_period) == 0) ? 1u : 0u;
+}
+
+hipError_t launch_state_passing(SsdArgs& a, int PN, hipStream_t st) {
+    void* args[] = {&a, &PN};
+    return hipLaunchKernel((const void*)&k_state_passing, dim3((PN / 4 + 255) / 256, a.nheads, a.batch),
+                           dim3(256), args, 0, st);
+}
+
+hipError_t launch_boundary(const void* src, size_t src_bs, void* dst, size_t dst_bs, size_t bytes_per_b,
+                           int batch, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
+                           hipStream_t st) {
+    const size_t work = (bytes_per_b / 16) * (size_t)batch;
+    const size_t big = work > nsync ? work : nsync;
+    size_t grid = (big + 255) / 256;
+    if (grid < 1) grid = 1;
+    if (grid > 4096) grid = 4096;
+    const char* s = (const char*)src;
+    char* d = (char*)dst;
+    void* args[] = {&s, &src_bs, &d, &dst_bs, &bytes_per_b, &batch, &sync, &nsync, &nflags, &flag_period};
+    return hipLaunchKernel((const void*)&k_boundary, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+
+}  // namespace ssd

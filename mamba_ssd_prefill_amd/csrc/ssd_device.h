@@ -1,0 +1,599 @@
+// ssd_device.h -- gfx950 device code for the Mamba-2 SSD chunked prefill.
+//
+// Page keys used in comments:
+//   [KF]  "Mamba-2炸裂升级！大模型推理飙升20%，效率翻2.5倍！" (repost of "Accelerating
+//         Mamba2 with Kernel Fusion"); sections "Mamba-2核心操作与融合的必要性" (the five
+//         SSD steps), "高效内核融合技术揭秘" (fused schedule), "性能瓶颈的深入分析"
+//         (boundary split-out, decay on x, chunk size).
+//   [HW]  "Mamba 硬件感知算法", sections "块分解与状态传递" (chunk decomposition) and
+//         "Mamba-2 Segsum 稳定化" (decay kept in log space).
+//   [XLA] "Mamba-2状态空间模型的编译器优化与实现", section 1.1 (the recurrence) and 2.2
+//         (decay exponent kept in fp32).
+//
+// Tensor layouts (row-major): x, y [B][L][H][P]; dt [B][L][H]; B, C [B][L][G][N];
+// states [B][K][H][P][N].  Workspace intermediates are described in mamba_ssd.h.
+//
+// MFMA conventions (16x16 output tiles, one 64-lane wave):
+//   A operand: lane l holds row (l & 15), KPL consecutive k starting at KPL * (l >> 4);
+//   B operand: lane l holds column (l & 15), the same k slots;
+//   accumulator: lane l holds rows 4 * (l >> 4) + r (r = 0..3) of column (l & 15).
+// Only the A/B symmetry of the k slots matters for a contraction, which lets the
+// state held in accumulator layout feed the C . S^T product directly (see y_off).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd_launch.h"
+
+namespace ssd {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// ---- element-type traits -------------------------------------------------------------
+template <typename T> struct TT;
+template <> struct TT<__bf16> {
+    static constexpr int KPL = 8;  // k values per lane in one MFMA
+    typedef bf16x8 frag;
+    typedef bf16x8 v8;  // 16 bytes
+    typedef bf16x4 v4;
+    typedef bf16x2 v2;
+    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct TT<_Float16> {
+    static constexpr int KPL = 8;
+    typedef f16x8 frag;
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    typedef f16x2 v2;
+    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct TT<float> {
+    static constexpr int KPL = 1;
+    typedef float frag;
+    typedef f32x4 v8;  // 16 bytes
+    typedef f32x4 v4;
+    typedef f32x2 v2;
+    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+template <typename V> __device__ inline V vzero() {
+    V v;
+    __builtin_memset(&v, 0, sizeof(V));
+    return v;
+}
+
+// ---- per-(T, P, N) geometry of a chunk tile --------------------------------------------
+// A chunk tile is (chunk c, batch b, group g, a run of HPT heads of g).  Its four waves
+// split as HPT heads x WPH p-slices of PW columns each.  Tokens are handled in windows
+// of W = 64 (chunk sizes are multiples of 64).
+template <typename T, int P, int N> struct Geo {
+    static constexpr int W = 64;
+    static constexpr int PW = P < 32 ? P : 32;
+    static constexpr int WPH = P / PW;
+    static constexpr int HPT = 4 / WPH;
+    static constexpr int MBP = PW / 16;
+    static constexpr int NB = N / 16;
+    static constexpr int WB = W / 16;
+    static constexpr int KPL = TT<T>::KPL;
+    static constexpr int KI = 4 * KPL;
+    static constexpr int VEC = 16 / (int)sizeof(T);
+    static constexpr int PADE = 16 / (int)sizeof(T);  // 16 bytes of row padding
+    static constexpr int LDW = W + PADE;
+    static constexpr int LDN = N + PADE;
+    static constexpr int QMAX = 256;
+    static constexpr int SZ_BT = N * LDW * (int)sizeof(T);
+    static constexpr int SZ_XW = HPT * P * LDW * (int)sizeof(T);
+    static constexpr int SZ_C = W * LDN * (int)sizeof(T);
+    static constexpr int SZ_L = HPT * W * LDW * (int)sizeof(T);
+    static constexpr int SZ_XT = HPT * P * LDW * (int)sizeof(T);
+    static constexpr int SZ_PHASE_S = SZ_BT + SZ_XW;
+    static constexpr int SZ_PHASE_Y = SZ_C + SZ_L + SZ_XT;
+    static constexpr int SZ_MAIN = SZ_PHASE_S > SZ_PHASE_Y ? SZ_PHASE_S : SZ_PHASE_Y;
+    static constexpr int SZ_VEC = 3 * HPT * QMAX * 4;  // dt, acs, chunk-state weights
+    static constexpr int SMEM = SZ_MAIN + SZ_VEC;
+    static_assert(P % 16 == 0 && N % 16 == 0, "P and N must be multiples of 16");
+    static_assert(KPL == 1 || N % 32 == 0, "16-bit inputs need N % 32 == 0");
+    static_assert(P <= 128, "P <= 128");
+};
+
+// ---- scalar helpers ------------------------------------------------------------------
+__device__ inline float softplus_f(float z) {
+    // log(1 + e^z) without overflow
+    return z > 0.f ? z + log1pf(__expf(-z)) : log1pf(__expf(z));
+}
+
+template <typename T> __device__ inline float f32of(T v) { return (float)v; }
+
+__device__ inline f32x4 load_state4(const void* base, int dtype, size_t off) {
+    if (dtype == DT_F32) return *(const f32x4*)((const float*)base + off);
+    if (dtype == DT_F16) {
+        f16x4 v = *(const f16x4*)((const _Float16*)base + off);
+        return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+    bf16x4 v = *(const bf16x4*)((const __bf16*)base + off);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+__device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) {
+    if (dtype == DT_F32) {
+        *(f32x4*)((float*)base + off) = v;
+    } else if (dtype == DT_F16) {
+        *(f16x4*)((_Float16*)base + off) =
+            f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    } else {
+        *(bf16x4*)((__bf16*)base + off) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    }
+}
+
+template <typename T> __device__ inline typename TT<T>::v4 cvt4(f32x4 v) {
+    typename TT<T>::v4 o;
+    o[0] = (T)v[0];
+    o[1] = (T)v[1];
+    o[2] = (T)v[2];
+    o[3] = (T)v[3];
+    return o;
+}
+
+template <typename T> __device__ inline typename TT<T>::frag load_frag(const T* p) {
+    if constexpr (TT<T>::KPL == 8)
+        return *(const typename TT<T>::frag*)p;
+    else
+        return *p;
+}
+
+// ---- cross-workgroup waits -------------------------------------------------------------
+// Poll a flag word until it is non-zero.  Bounded: after spin_limit polls (or once any
+// wait has given up) it raises the abort word and the status word and returns false, so
+// every workgroup still runs to completion.  All lanes of the calling wave(s) poll the
+// same address; the acquire fence after a successful poll orders the reads that follow.
+__device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        ++spins;
+        if ((spins & 31u) == 0u) {
+            if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
+            if (spins > a.spin_limit) {
+                __hip_atomic_store(a.abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.status, 7u /* SSD_ERR_SYNC_TIMEOUT */, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                return false;
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return true;
+}
+
+// Every lane: make its own prior global writes visible at agent scope, then set *f.
+__device__ inline void publish_flag_wave(uint32_t* f) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whole workgroup: all threads release their writes, then thread 0 sets *f.
+__device__ inline void publish_flag_block(uint32_t* f) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- step 1: chunk_cumsum ([KF] item 4; [HW] segsum section: decay in log space) ------
+// For one (b, c): dt = softplus(dt_raw + dt_bias) (0 past L) and the inclusive in-chunk
+// running sum of dt * A, both fp32.  One wave per head; each lane owns Q/64 consecutive
+// tokens, then a wave-wide exclusive scan of the lane totals.
+template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int Q = a.chunk, L = a.seqlen, H = a.nheads, nc = a.nchunks;
+    const int V = Q >> 6;  // 1..4
+    const T* dtr = (const T*)a.dt;
+    for (int h = wave; h < H; h += 4) {
+        const float bias = a.dt_bias ? a.dt_bias[h] : 0.f;
+        const float Ah = a.A[h];
+        float d[4], run[4];
+        float tot = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            d[k] = 0.f;
+            if (k < V) {
+                const int t = c * Q + lane * V + k;
+                if (t < L) {
+                    const float z = f32of(dtr[((size_t)b * L + t) * H + h]) + bias;
+                    d[k] = a.softplus ? softplus_f(z) : z;
+                }
+                tot += d[k] * Ah;
+            }
+            run[k] = tot;
+        }
+        float incl = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const float excl = incl - tot;
+        const size_t base = (((size_t)b * nc + c) * H + h) * Q + (size_t)lane * V;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (k < V) {
+                a.dtf[base + k] = d[k];
+                a.acs[base + k] = excl + run[k];
+            }
+    }
+}
+
+// ---- step 2: bmm ([KF] item 7) ---------------------------------------------------------
+// CB[i][j] = sum_n C_i[n] B_j[n] for one (b, c, g), computed as CB^T blocks (rows j,
+// columns i) so each lane stores 4 consecutive j of one row i.  Only blocks with
+// i-block >= j-block are formed: the scan step reads j <= i only.  Fragments come
+// straight from global memory (rows are n-contiguous).
+template <typename T, int N> __device__ void bmm_tile(const SsdArgs& a, int b, int c, int g) {
+    constexpr int KPL = TT<T>::KPL, KI = 4 * KPL;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int Q = a.chunk, L = a.seqlen, G = a.ngroups, nc = a.nchunks;
+    const int QB = Q >> 4;
+    const T* Bp = (const T*)a.B;
+    const T* Cp = (const T*)a.C;
+    typedef typename TT<T>::frag frag;
+    float* cbase = a.cb + (((size_t)b * nc + c) * G + g) * (size_t)Q * Q;
+    for (int jb = wave; jb < QB; jb += 4) {
+        const int tj = c * Q + jb * 16 + r16;
+        frag af[N / KI];
+#pragma unroll
+        for (int ks = 0; ks < N / KI; ++ks)
+            af[ks] = tj < L ? load_frag<T>(Bp + (((size_t)b * L + tj) * G + g) * N + ks * KI + q * KPL)
+                            : vzero<frag>();
+        for (int ib = jb; ib < QB; ++ib) {
+            const int ti = c * Q + ib * 16 + r16;
+            f32x4 acc = vzero<f32x4>();
+#pragma unroll
+            for (int ks = 0; ks < N / KI; ++ks) {
+                const frag bf = ti < L ? load_frag<T>(Cp + (((size_t)b * L + ti) * G + g) * N + ks * KI + q * KPL)
+                                       : vzero<frag>();
+                acc = TT<T>::mma(af[ks], bf, acc);
+            }
+            *(f32x4*)(cbase + (size_t)(ib * 16 + r16) * Q + jb * 16 + 4 * q) = acc;
+        }
+    }
+}
+
+// ---- LDS staging helpers ---------------------------------------------------------------
+// Rows [t0, t0 + W) of a row-major [token][COLS] slice (row stride `rs` elements), stored
+// transposed: dst[col][jj] with row length LDW, zeros for tokens >= L.  Two consecutive
+// tokens per item so each LDS write packs a (jj, jj+1) pair.  When `scale` is given,
+// row jj is multiplied by scale[jj] in fp32 before rounding.  nullptr src = zeros.
+template <typename T, int COLS, int W, int LDW>
+__device__ inline void stage_transposed(T* dst, const T* src, size_t rs, int t0, int L, const float* scale,
+                                        int item0, int nthreads) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    constexpr int NV = COLS / VEC;
+    constexpr int CL = NV < 4 ? NV : 4;
+    constexpr int ITEMS = (W / 2) * NV;
+    typedef typename TT<T>::v8 v8;
+    typedef typename TT<T>::v2 v2;
+    for (int it = item0; it < ITEMS; it += nthreads) {
+        const int cl = it % CL;
+        const int jp = (it / CL) % (W / 2);
+        const int ch = it / (CL * (W / 2));
+        const int cv = ch * CL + cl;
+        const int jj = 2 * jp;
+        v8 v0 = vzero<v8>(), v1 = vzero<v8>();
+        if (src) {
+            if (t0 + jj < L) v0 = *(const v8*)(src + (size_t)(t0 + jj) * rs + cv * VEC);
+            if (t0 + jj + 1 < L) v1 = *(const v8*)(src + (size_t)(t0 + jj + 1) * rs + cv * VEC);
+            if (scale) {
+                const float s0 = scale[jj], s1 = scale[jj + 1];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    v0[e] = (T)((float)v0[e] * s0);
+                    v1[e] = (T)((float)v1[e] * s1);
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            v2 pr;
+            pr[0] = v0[e];
+            pr[1] = v1[e];
+            *(v2*)(dst + (cv * VEC + e) * LDW + jj) = pr;
+        }
+    }
+}
+
+// Rows [t0, t0 + W) of a [token][COLS] slice stored as-is: dst[row][col], row length LD.
+template <typename T, int COLS, int W, int LD>
+__device__ inline void stage_rows(T* dst, const T* src, size_t rs, int t0, int L) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    constexpr int NV = COLS / VEC;
+    typedef typename TT<T>::v8 v8;
+    for (int it = threadIdx.x; it < W * NV; it += 256) {
+        const int cv = it % NV, r = it / NV;
+        v8 v = vzero<v8>();
+        if (t0 + r < L) v = *(const v8*)(src + (size_t)(t0 + r) * rs + cv * VEC);
+        *(v8*)(dst + r * LD + cv * VEC) = v;
+    }
+}
+
+// ---- steps 3-5 on one chunk tile ---------------------------------------------------------
+enum : int { MODE_STATE = 0, MODE_SCAN = 1, MODE_FUSED = 2 };
+
+// MODE_STATE  chunk_state ([KF] item 5): s_c = sum_j x_j w_j (outer) B_j with
+//             w_j = exp(acs[Q-1] - acs[j]) dt_j (decay applied to x, [KF] bottleneck
+//             section) -> workspace s.
+// MODE_SCAN   chunk_scan ([KF] item 8): y_i = exp(acs_i) C_i . S_c
+//             + sum_{j<=i} CB[i][j] exp(acs_i - acs_j) dt_j x_j + D x_i, with S_c read
+//             from the states slot of chunk c.
+// MODE_FUSED  chunk_state, then the state_passing hop ([KF] item 6; fused schedule of
+//             [KF] "高效内核融合技术揭秘"): wait for S_c, write S_{c+1} = exp(acs[Q-1]) S_c
+//             + s_c to the next ring slot and release it, then chunk_scan with S_c.
+template <typename T, int P, int N, int MODE>
+__device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char* smem) {
+    typedef Geo<T, P, N> G_;
+    constexpr int W = G_::W, PW = G_::PW, WPH = G_::WPH, HPT = G_::HPT, MBP = G_::MBP;
+    constexpr int NB = G_::NB, WB = G_::WB, KPL = G_::KPL, KI = G_::KI, LDW = G_::LDW, LDN = G_::LDN;
+    constexpr int QMAX = G_::QMAX;
+    typedef typename TT<T>::frag frag;
+    typedef typename TT<T>::v4 v4;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int hs = wave / WPH, ph = wave % WPH;
+    const int Q = a.chunk, L = a.seqlen, H = a.nheads, Gn = a.ngroups, nc = a.nchunks, hpg = a.hpg;
+    const int head0 = g * hpg + tig * HPT;
+    const int h = head0 + hs;
+    const bool hvalid = (tig * HPT + hs) < hpg;
+    const int tok0 = c * Q;
+    const T* xg = (const T*)a.x;
+    const T* Bg = (const T*)a.B;
+    const T* Cg = (const T*)a.C;
+
+    float* sDt = (float*)(smem + G_::SZ_MAIN);  // [HPT][QMAX]
+    float* sAcs = sDt + HPT * QMAX;             // [HPT][QMAX]
+    float* sW = sAcs + HPT * QMAX;              // [HPT][QMAX] chunk-state weights
+
+    for (int e = tid; e < HPT * Q; e += 256) {
+        const int hh = e / Q, i = e - hh * Q;
+        const bool ok = (tig * HPT + hh) < hpg;
+        const size_t off = (((size_t)b * nc + c) * H + head0 + hh) * Q + i;
+        sDt[hh * QMAX + i] = ok ? a.dtf[off] : 0.f;
+        sAcs[hh * QMAX + i] = ok ? a.acs[off] : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < HPT * Q; e += 256) {
+        const int hh = e / Q, i = e - hh * Q;
+        sW[hh * QMAX + i] = __expf(sAcs[hh * QMAX + Q - 1] - sAcs[hh * QMAX + i]) * sDt[hh * QMAX + i];
+    }
+    const float acs_last = sAcs[hs * QMAX + Q - 1];
+
+    // S_c in accumulator layout: tile (nb, pb), lane -> S[p = ph*PW + pb*16 + r16][n = nb*16 + 4q + r]
+    f32x4 sc[NB][MBP];
+
+    if constexpr (MODE != MODE_SCAN) {
+        f32x4 acc[NB][MBP];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb) acc[nb][pb] = vzero<f32x4>();
+        T* sBT = (T*)smem;
+        T* sXW = (T*)(smem + G_::SZ_BT);
+        for (int j0 = 0; j0 < Q; j0 += W) {
+            __syncthreads();  // sW ready / previous window's MFMAs done
+            stage_transposed<T, N, W, LDW>(sBT, Bg + ((size_t)b * L * Gn + g) * N, (size_t)Gn * N, tok0 + j0, L,
+                                           nullptr, tid, 256);
+            for (int hh = 0; hh < HPT; ++hh) {
+                const bool ok = (tig * HPT + hh) < hpg;
+                stage_transposed<T, P, W, LDW>(sXW + hh * P * LDW,
+                                               ok ? xg + ((size_t)b * L * H + head0 + hh) * P : nullptr,
+                                               (size_t)H * P, tok0 + j0, L, sW + hh * QMAX + j0, tid, 256);
+            }
+            __syncthreads();
+            if (hvalid) {
+                const T* xw = sXW + (hs * P + ph * PW) * LDW;
+#pragma unroll
+                for (int kk = 0; kk < W / KI; ++kk) {
+                    frag bfr[MBP];
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) bfr[pb] = load_frag<T>(xw + (pb * 16 + r16) * LDW + kk * KI + q * KPL);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const frag af = load_frag<T>(sBT + (nb * 16 + r16) * LDW + kk * KI + q * KPL);
+#pragma unroll
+                        for (int pb = 0; pb < MBP; ++pb) acc[nb][pb] = TT<T>::mma(af, bfr[pb], acc[nb][pb]);
+                    }
+                }
+            }
+        }
+        if constexpr (MODE == MODE_STATE) {
+            if (hvalid) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) {
+                        const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
+                        *(f32x4*)(a.s + ((((size_t)b * nc + c) * H + h) * P + p) * N + n) = acc[nb][pb];
+                    }
+            }
+            return;
+        } else {
+            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c
+            if (hvalid) {
+                const size_t chain = ((size_t)b * H + h) * WPH + ph;
+                uint32_t* fl = a.flags + chain * (nc + 1);
+                wait_flag(fl + c, a);
+                const int K = a.slots;
+                const int slot = c % K, nslot = (c + 1) % K;
+                const float dec = __expf(acs_last);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) {
+                        const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
+                        const size_t in = ((((size_t)b * K + slot) * H + h) * P + p) * N + n;
+                        const size_t out = ((((size_t)b * K + nslot) * H + h) * P + p) * N + n;
+                        sc[nb][pb] = load_state4(a.states, a.state_dtype, in);
+                        store_state4(a.states, a.state_dtype, out, dec * sc[nb][pb] + acc[nb][pb]);
+                    }
+                publish_flag_wave(fl + c + 1);
+            }
+        }
+    } else {
+        if (hvalid) {
+            const int K = a.slots, slot = c % K;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int pb = 0; pb < MBP; ++pb) {
+                    const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
+                    sc[nb][pb] = load_state4(a.states, a.state_dtype,
+                                             ((((size_t)b * K + slot) * H + h) * P + p) * N + n);
+                }
+        }
+    }
+
+    if constexpr (MODE != MODE_STATE) {
+        // ---- chunk_scan ----
+        T* sC = (T*)smem;
+        T* sL = (T*)(smem + G_::SZ_C);
+        T* sXT = (T*)(smem + G_::SZ_C + G_::SZ_L);
+        const float Dh = (a.D && hvalid) ? a.D[h] : 0.f;
+        const float* cbase = a.cb + (((size_t)b * nc + c) * Gn + g) * (size_t)Q * Q;
+        for (int i0 = 0; i0 < Q; i0 += W) {
+            __syncthreads();
+            stage_rows<T, N, W, LDN>(sC, Cg + ((size_t)b * L * Gn + g) * N, (size_t)Gn * N, tok0 + i0, L);
+            __syncthreads();
+            f32x4 accY[MBP][WB];
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb)
+#pragma unroll
+                for (int ib = 0; ib < WB; ++ib) accY[pb][ib] = vzero<f32x4>();
+            if (hvalid) {
+                // y_off^T[p][i] = sum_n S_c[p][n] C[i][n]: A from the state held in
+                // accumulator layout, B from C rows, with matching k-slot order.
+                if constexpr (KPL == 8) {
+#pragma unroll
+                    for (int ks = 0; ks < N / 32; ++ks) {
+                        frag af[MBP];
+#pragma unroll
+                        for (int pb = 0; pb < MBP; ++pb) {
+                            const v4 lo = cvt4<T>(sc[2 * ks][pb]);
+                            const v4 hi = cvt4<T>(sc[2 * ks + 1][pb]);
+                            af[pb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        }
+#pragma unroll
+                        for (int ib = 0; ib < WB; ++ib) {
+                            const T* crow = sC + (ib * 16 + r16) * LDN + ks * 32 + 4 * q;
+                            const v4 lo = *(const v4*)crow;
+                            const v4 hi = *(const v4*)(crow + 16);
+                            const frag bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                            for (int pb = 0; pb < MBP; ++pb) accY[pb][ib] = TT<T>::mma(af[pb], bf, accY[pb][ib]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+#pragma unroll
+                            for (int ib = 0; ib < WB; ++ib) {
+                                const frag bf = sC[(ib * 16 + r16) * LDN + nb * 16 + 4 * q + r];
+#pragma unroll
+                                for (int pb = 0; pb < MBP; ++pb)
+                                    accY[pb][ib] = TT<T>::mma(sc[nb][pb][r], bf, accY[pb][ib]);
+                            }
+                }
+#pragma unroll
+                for (int ib = 0; ib < WB; ++ib) {
+                    const float e = __expf(sAcs[hs * QMAX + i0 + ib * 16 + r16]);
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) accY[pb][ib] *= e;
+                }
+            }
+            for (int j0 = 0; j0 <= i0; j0 += W) {
+                if (j0 > 0) __syncthreads();
+                for (int hh = 0; hh < HPT; ++hh) {
+                    const bool ok = (tig * HPT + hh) < hpg;
+                    stage_transposed<T, P, W, LDW>(sXT + hh * P * LDW,
+                                                   ok ? xg + ((size_t)b * L * H + head0 + hh) * P : nullptr,
+                                                   (size_t)H * P, tok0 + j0, L, nullptr, tid, 256);
+                }
+                // L[i][j] = CB[i][j] exp(acs_i - acs_j) dt_j for j <= i, else 0 (log-space
+                // decay differences in fp32, [HW] segsum section, [XLA] 2.2)
+                for (int it = tid; it < W * (W / 4); it += 256) {
+                    const int jq = it % (W / 4), ii = it / (W / 4);
+                    const int i = i0 + ii, j = j0 + 4 * jq;
+                    const f32x4 cbv = *(const f32x4*)(cbase + (size_t)i * Q + j);
+#pragma unroll
+                    for (int hh = 0; hh < HPT; ++hh) {
+                        const float ai = sAcs[hh * QMAX + i];
+                        f32x4 lv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = cbv[e] * __expf(ai - sAcs[hh * QMAX + j + e]) * sDt[hh * QMAX + j + e];
+                            lv[e] = (j + e <= i) ? v : 0.f;
+                        }
+                        *(v4*)(sL + (hh * W + ii) * LDW + 4 * jq) = cvt4<T>(lv);
+                    }
+                }
+                __syncthreads();
+                if (hvalid) {
+                    const T* xt = sXT + (hs * P + ph * PW) * LDW;
+                    const T* lt = sL + hs * W * LDW;
+#pragma unroll
+                    for (int kk = 0; kk < W / KI; ++kk) {
+                        frag af[MBP];
+#pragma unroll
+                        for (int pb = 0; pb < MBP; ++pb) af[pb] = load_frag<T>(xt + (pb * 16 + r16) * LDW + kk * KI + q * KPL);
+#pragma unroll
+                        for (int ib = 0; ib < WB; ++ib) {
+                            if (j0 == i0 && kk * KI > ib * 16 + 15) continue;  // block above the diagonal
+                            const frag bf = load_frag<T>(lt + (ib * 16 + r16) * LDW + kk * KI + q * KPL);
+#pragma unroll
+                            for (int pb = 0; pb < MBP; ++pb) accY[pb][ib] = TT<T>::mma(af[pb], bf, accY[pb][ib]);
+                        }
+                    }
+                }
+            }
+            if (hvalid) {
+                T* yg = (T*)a.y;
+#pragma unroll
+                for (int ib = 0; ib < WB; ++ib) {
+                    const int t = tok0 + i0 + ib * 16 + r16;
+                    if (t < L) {
+#pragma unroll
+                        for (int pb = 0; pb < MBP; ++pb) {
+                            const int p = ph * PW + pb * 16 + 4 * q;
+                            const size_t off = (((size_t)b * L + t) * H + h) * P + p;
+                            const v4 xv = *(const v4*)(xg + off);
+                            f32x4 yv = accY[pb][ib];
+                            yv[0] += Dh * (float)xv[0];
+                            yv[1] += Dh * (float)xv[1];
+                            yv[2] += Dh * (float)xv[2];
+                            yv[3] += Dh * (float)xv[3];
+                            *(v4*)(yg + off) = cvt4<T>(yv);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace ssd

@@ -1,0 +1,63 @@
+// ssd_launch.h -- host-side interface between the C-ABI layer and the kernel
+// translation units: the kernel argument block and the launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Kernel argument block (passed by value).  Layouts are described in mamba_ssd.h.
+struct SsdArgs {
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* dt_bias;
+    void* y;
+    float* dtf;          // [B][nc][H][Q]
+    float* acs;          // [B][nc][H][Q]
+    float* cb;           // [B][nc][G][Q][Q]
+    float* s;            // [B][nc][H][P][N] (unfused form)
+    void* states;        // [B][K][H][P][N] in the state dtype
+    uint32_t* flags;     // [B][H][WPH][nc + 1]
+    uint32_t* cs_done;   // [B][nc]
+    uint32_t* bmm_done;  // [B][nc][G]
+    uint32_t* ticket;
+    uint32_t* abort_word;
+    uint32_t* status;
+    int batch, seqlen, nheads, ngroups, chunk, nchunks, hpg, tpg, slots;
+    int state_dtype, softplus;
+    uint32_t spin_limit;
+};
+
+enum : int {
+    STEP_CUMSUM = 0,
+    STEP_BMM = 1,
+    STEP_CHUNK_STATE = 2,
+    STEP_STATE_PASSING = 3,
+    STEP_CHUNK_SCAN = 4,
+    STEP_FUSED = 5,
+};
+
+// Work split of a chunk tile for headdim P: PW columns of P per wave, WPH waves per
+// head, HPT = 4 / WPH heads per 256-thread workgroup.
+inline int p_per_wave(int P) { return P < 32 ? P : 32; }
+inline int waves_per_head(int P) { return P / p_per_wave(P); }
+inline int heads_per_tile(int P) { return 4 / waves_per_head(P); }
+
+// Per-dtype launchers; hipErrorNotSupported when (P, N) has no instantiation.
+hipError_t launch_step_f32(int step, int P, int N, SsdArgs& a, hipStream_t st);
+hipError_t launch_step_f16(int step, int P, int N, SsdArgs& a, hipStream_t st);
+hipError_t launch_step_bf16(int step, int P, int N, SsdArgs& a, hipStream_t st);
+
+// Non-templated kernels (ssd_common.hip).
+hipError_t launch_state_passing(SsdArgs& a, int PN, hipStream_t st);
+hipError_t launch_boundary(const void* src, size_t src_bs, void* dst, size_t dst_bs, size_t bytes_per_b,
+                           int batch, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
+                           hipStream_t st);
+
+}  // namespace ssd

@@ -1,0 +1,62 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, compare with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import mamba_ssd_prefill_amd as ssd
+import oracle
+from parity import gate
+
+DT_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a ROCm GPU; none is visible")
+    ssd.load_library()  # raises if the HIP library is not built: no fallback exists
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp, chunk_size, impl, state_dtype=None, dev="cuda:0"):
+    g = inp.to(dev)
+    y, fin = ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=chunk_size,
+                             impl=impl, dt_softplus=inp.dt_softplus,
+                             state_dtype=state_dtype)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def f64(t):
+    return None if t is None else t.detach().cpu().to(torch.float64).numpy()
+
+
+def check_full(inp, y, fin, name=""):
+    """Every element of y and the final state against the fp64 recurrence."""
+    yr, fr = oracle.recurrence_full(**inp.args())
+    in_dt = DT_NAME[inp.x.dtype]
+    st_dt = DT_NAME[fin.dtype]
+    skip = (f64(inp.D)[None, None, :, None] * f64(inp.x)) if inp.D is not None else None
+    r1 = gate(f64(y), yr, in_dt, in_dt, skip=skip, name=name + " y")
+    r2 = gate(f64(fin), fr, st_dt, in_dt, name=name + " final")
+    return r1, r2
+
+
+def check_sampled(inp, y, fin, pairs, name=""):
+    """The chains (b, h) in `pairs`, all tokens, against the fp64 recurrence."""
+    yr, fr, _ = oracle.recurrence(**inp.args(), bh=pairs)
+    in_dt = DT_NAME[inp.x.dtype]
+    st_dt = DT_NAME[fin.dtype]
+    ys = np.stack([f64(y[b, :, h]) for (b, h) in pairs])
+    fs = np.stack([f64(fin[b, h]) for (b, h) in pairs])
+    skip = None
+    if inp.D is not None:
+        skip = np.stack([float(inp.D[h]) * f64(inp.x[b, :, h]) for (b, h) in pairs])
+    r1 = gate(ys, yr, in_dt, in_dt, skip=skip, name=name + " y")
+    r2 = gate(fs, fr, st_dt, in_dt, name=name + " final")
+    return r1, r2

@@ -1,0 +1,198 @@
+"""C-ABI tests that run without a GPU.
+
+The library must load, export every function include/mamba_ssd.h declares, and reject
+bad arguments on the host before any HIP call.  Every call here fails exactly one check
+with otherwise valid arguments (fake but aligned addresses), so no kernel is ever
+launched -- these tests are safe on a GPU machine too.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_prefill_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_ssd.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, WS_SMALL, HIP, TIMEOUT, BADARG = range(9)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ssd.load_library()
+
+
+def base(**kw):
+    p = dict(batch=2, seqlen=300, nheads=8, headdim=64, dstate=128, ngroups=2, chunk_size=128,
+             in_dtype="bf16", state_dtype="f32", dt_softplus=True, impl="fused")
+    p.update(kw)
+    return ssd.make_params(**p)
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(ssd.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_struct_sizes_match_header():
+    # ssd_params_t: size_t + 11 ints -> 8 + 44 = 52, padded to 56 on LP64
+    assert ctypes.sizeof(ssd.Params) == 56
+    assert ctypes.sizeof(ssd.Layout) == 14 * 8 + 2 * 4
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = lib.ssd_status_string(code)
+        assert s and len(s) > 3
+    assert lib.ssd_status_string(1234) == b"unknown status"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK),
+    (dict(batch=0), SHAPE), (dict(seqlen=0), SHAPE), (dict(nheads=0), SHAPE),
+    (dict(ngroups=3), SHAPE), (dict(ngroups=0), SHAPE), (dict(chunk_size=0), SHAPE),
+    (dict(headdim=48), UNSUP), (dict(headdim=256), UNSUP), (dict(dstate=16), UNSUP),
+    (dict(dstate=256), UNSUP), (dict(chunk_size=32), UNSUP), (dict(chunk_size=100), UNSUP),
+    (dict(chunk_size=512), UNSUP),
+    (dict(dstate=16, in_dtype="f32"), OK), (dict(chunk_size=192), OK), (dict(headdim=128), OK),
+    (dict(in_dtype=3), BADARG), (dict(state_dtype=-1), BADARG), (dict(impl=2), BADARG),
+    (dict(dt_softplus=True, impl="unfused"), OK),
+])
+def test_validate(lib, kw, code):
+    assert lib.ssd_validate(ctypes.byref(base(**kw))) == code
+
+
+def test_validate_rejects_short_struct_and_null(lib):
+    p = base()
+    p.struct_size = 8
+    assert lib.ssd_validate(ctypes.byref(p)) == BADARG
+    assert lib.ssd_validate(None) == NULLP
+    p = base()
+    p.dt_softplus = 2
+    assert lib.ssd_validate(ctypes.byref(p)) == BADARG
+
+
+def test_validate_rejects_ticket_overflow(lib):
+    p = base(batch=4096, seqlen=1 << 20, nheads=128, ngroups=128, chunk_size=64)
+    assert lib.ssd_validate(ctypes.byref(p)) == SHAPE
+
+
+@pytest.mark.parametrize("impl", ["fused", "unfused"])
+@pytest.mark.parametrize("state", ["f32", "f16"])
+def test_workspace_layout_arithmetic(lib, impl, state):
+    p = base(impl=impl, state_dtype=state)
+    lay = ssd.workspace_layout(p)
+    Bt, L, H, P, N, G, Q = 2, 300, 8, 64, 128, 2, 128
+    nc = -(-L // Q)
+    es = 4 if state == "f32" else 2
+    assert lay.nchunks == nc
+    K = 2 if impl == "fused" else nc + 1
+    assert lay.state_slots == K
+    assert lay.dt_bytes == Bt * nc * H * Q * 4 == lay.acs_bytes
+    assert lay.cb_bytes == Bt * nc * G * Q * Q * 4
+    assert lay.s_bytes == (0 if impl == "fused" else Bt * nc * H * P * N * 4)
+    assert lay.states_bytes == Bt * K * H * P * N * es
+    regions = sorted([(lay.dt_offset, lay.dt_bytes), (lay.acs_offset, lay.acs_bytes), (lay.cb_offset, lay.cb_bytes),
+                      (lay.s_offset, lay.s_bytes), (lay.states_offset, lay.states_bytes),
+                      (lay.sync_offset, lay.sync_bytes)])
+    for (o1, n1), (o2, _) in zip(regions, regions[1:]):
+        assert o1 % 256 == 0 and o1 + n1 <= o2
+    assert lay.sync_offset <= lay.status_offset < lay.sync_offset + lay.sync_bytes
+    assert lay.total_bytes >= lay.sync_offset + lay.sync_bytes
+    assert ssd.workspace_size(p) == lay.total_bytes
+    if impl == "fused":
+        # flags [B][H][P/32][nc+1] + cs_done [B][nc] + bmm_done [B][nc][G] + ticket + abort + status
+        assert lay.sync_bytes == 4 * (Bt * H * 2 * (nc + 1) + Bt * nc + Bt * nc * G + 3)
+
+
+def test_workspace_size_zero_for_invalid(lib):
+    assert lib.ssd_prefill_workspace_size(ctypes.byref(base(headdim=48))) == 0
+    assert lib.ssd_prefill_workspace_size(None) == 0
+
+
+FAKE = 1 << 40  # an aligned address that is never dereferenced
+
+
+def prefill_args(p, **over):
+    ws = ssd.workspace_size(p)
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=FAKE, dt_bias=FAKE, h0=FAKE, y=FAKE, fin=FAKE,
+             ws=FAKE, ws_bytes=ws, stream=None)
+    a.update(over)
+    return a
+
+
+def call_prefill(lib, p, a):
+    vp = ctypes.c_void_p
+    return lib.ssd_prefill(ctypes.byref(p), vp(a["x"]), vp(a["dt"]), vp(a["A"]), vp(a["B"]), vp(a["C"]),
+                           vp(a["D"]), vp(a["dt_bias"]), vp(a["h0"]), vp(a["y"]), vp(a["fin"]), vp(a["ws"]),
+                           a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("field", ["x", "dt", "A", "B", "C", "y", "fin", "ws"])
+def test_prefill_null_pointers(lib, field):
+    p = base()
+    assert call_prefill(lib, p, prefill_args(p, **{field: None})) == NULLP
+
+
+@pytest.mark.parametrize("field,off", [("x", 8), ("B", 4), ("C", 2), ("y", 8), ("fin", 8), ("h0", 8),
+                                       ("dt", 1), ("A", 2), ("D", 2), ("dt_bias", 2), ("ws", 128)])
+def test_prefill_misaligned(lib, field, off):
+    p = base()
+    assert call_prefill(lib, p, prefill_args(p, **{field: FAKE + off})) == MISAL
+
+
+def test_prefill_workspace_too_small(lib):
+    p = base()
+    assert call_prefill(lib, p, prefill_args(p, ws_bytes=ssd.workspace_size(p) - 1)) == WS_SMALL
+
+
+def test_prefill_invalid_params(lib):
+    p = base(headdim=48)
+    assert call_prefill(lib, p, prefill_args(base(), ws_bytes=1 << 30)) == UNSUP
+    p = base(ngroups=3)
+    assert call_prefill(lib, p, prefill_args(base(), ws_bytes=1 << 30)) == SHAPE
+
+
+def test_steps_require_unfused_params(lib):
+    p = base(impl="fused")
+    vp = ctypes.c_void_p
+    ws = ssd.workspace_size(p)
+    assert lib.ssd_step_bmm(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), ws, None) == BADARG
+    assert lib.ssd_step_chunk_cumsum(ctypes.byref(p), vp(FAKE), vp(FAKE), None, vp(FAKE), ws, None) == BADARG
+
+
+def test_steps_validate_before_launch(lib):
+    p = base(impl="unfused")
+    vp = ctypes.c_void_p
+    ws = ssd.workspace_size(p)
+    assert lib.ssd_step_bmm(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), ws - 1, None) == WS_SMALL
+    assert lib.ssd_step_bmm(ctypes.byref(p), None, vp(FAKE), vp(FAKE), ws, None) == NULLP
+    assert lib.ssd_step_chunk_state(ctypes.byref(p), vp(FAKE + 2), vp(FAKE), vp(FAKE), ws, None) == MISAL
+    assert lib.ssd_step_chunk_scan(ctypes.byref(p), vp(FAKE), vp(FAKE), None, None, vp(FAKE), ws, None) == NULLP
+    assert lib.ssd_step_state_passing(ctypes.byref(p), None, None, vp(FAKE), ws, None) == NULLP
+    assert lib.ssd_step_chunk_cumsum(ctypes.byref(p), vp(FAKE + 1), vp(FAKE), None, vp(FAKE), ws, None) == MISAL
+
+
+def test_check_device_status_validates_first(lib):
+    assert lib.ssd_check_device_status(ctypes.byref(base(headdim=48)), ctypes.c_void_p(FAKE), None) == UNSUP
+    assert lib.ssd_check_device_status(ctypes.byref(base()), None, None) == NULLP
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 64, 4, 16)
+    B = torch.zeros(1, 64, 1, 16)
+    with pytest.raises(ValueError):
+        ssd.ssd_prefill(x, torch.zeros(1, 64, 4), torch.zeros(4), B, B.clone())
