@@ -1,0 +1,220 @@
+"""Benchmark: Mamba-2 SSD chunked prefill on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--chunk Q] [--workload NAME] [--no-cpu-baseline]
+
+A step is one ssd_prefill call (the whole hot path: boundary copies + the fused SSD
+kernel) over one batch of seeded synthetic inputs already resident in HBM.  Prints ONE
+JSON line with tokens/s, the roofline of the fused kernel (timed live with HIP events
+the library records around it), the unfused five-kernel form timed the same way, a
+chunk-size sweep, and the fp64 CPU oracle timed on a bounded sample.
+
+Roofline bytes are the compulsory HBM traffic of the problem (read x, dt, B, C, the
+initial state and the per-head parameters once; write y and the final state once),
+the same for both forms; the figure that also counts one write and one read of every
+inter-chunk state is reported alongside as "achieved_with_state_exchange".
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+METRIC = "SSD prefill tokens/s per layer + % HBM/MFMA roofline (fused vs unfused)"
+ESZ = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, Q, has_h0):
+    """Compulsory bytes, state-exchange bytes and causal flops of one call."""
+    B, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    e, es = ESZ[w.dtype], ESZ[w.state_dtype]
+    T = B * L
+    nc = -(-L // Q)
+    compulsory = T * (2 * H * P * e + H * e + 2 * G * N * e) + (2 if has_h0 else 1) * B * H * P * N * es + 3 * H * 4
+    exchange = 2 * B * nc * H * P * N * es
+    flops = T * (G * (Q + 1) * N + H * ((Q + 1) * P + 4 * P * N + 2 * P))
+    return compulsory, exchange, flops
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mamba_ssd_prefill_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, Q):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "ssd_fused_%s_q%d_traffic.json" % (workload, Q))
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_impl(ssd, torch, g, w, Q, impl, steps, warmup):
+    """Warm up, then time `steps` calls; returns (ms per call, mean kernel ms)."""
+    prm = ssd.make_params(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, Q, w.dtype,
+                          w.state_dtype, True, impl)
+    ws = ssd.alloc_workspace(prm, g.x.device)
+    y = torch.empty_like(g.x)
+    sdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.state_dtype]
+    fin = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=sdt, device=g.x.device)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def call(ev=None):
+        ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=Q, impl=impl,
+                        state_dtype=sdt, workspace=ws, y=y, final_state=fin, kernel_events=ev)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    kms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    status = ssd.check_device_status(prm, ws)
+    if status != 0:
+        raise RuntimeError("device status %d after %s Q=%d" % (status, impl, Q))
+    del ws, y, fin
+    return wall, kms
+
+
+def cpu_baseline(inp, w, seconds):
+    """The fp64 oracle (as it stands) on whole (batch, head) chains of the same inputs,
+    `threads` chains per call, until ~`seconds` have passed (whole passes repeat)."""
+    import oracle
+    threads = oracle.num_threads()
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.nheads)]
+    done, t0 = 0, time.perf_counter()
+    while True:
+        k = done % len(pairs)
+        oracle.recurrence(**inp.args(), bh=pairs[k:k + threads])
+        done += len(pairs[k:k + threads])
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    layer_tokens = done * w.seqlen / w.nheads  # one layer token = all H heads of one (b, t)
+    return {"value": layer_tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d (batch, head) chains of the %d in the workload (%.2f passes), %d tokens each, "
+                      "fp64 recurrence with y stored, %.1f s" % (done, len(pairs), done / len(pairs), w.seqlen, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mamba2_2p7b_bf16")
+    ap.add_argument("--chunk", type=int, default=0, help="chunk size (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 1 GiB device copy (counter calibration), "
+                         "then --steps fused calls; prints nothing")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the SSD prefill here is a single-GPU kernel and no "
+              "multi-GPU path is built (see DESIGN.md for how it would shard); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mamba_ssd_prefill_amd as ssd
+    from mamba_ssd_prefill_amd.inputs import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    ssd.load_library()
+    w = WORKLOADS[args.workload]
+    Q = args.chunk or w.chunk_size
+    log("generating %s inputs" % w.name)
+    inp = workload_inputs(w)
+    g = inp.to("cuda:0")
+    torch.cuda.synchronize()
+
+    if args.counters:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)  # 1 GiB read + 1 GiB written per copy
+        torch.cuda.synchronize()
+        del src, dst
+        sdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.state_dtype]
+        for impl in ("fused", "unfused"):
+            for _ in range(args.steps):
+                ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=Q, impl=impl,
+                                state_dtype=sdt)
+            torch.cuda.synchronize()
+        return
+
+    log("timing fused Q=%d" % Q)
+    f_wall, f_kms = time_impl(ssd, torch, g, w, Q, "fused", args.steps, args.warmup)
+    log("timing unfused Q=%d" % Q)
+    u_wall, u_kms = time_impl(ssd, torch, g, w, Q, "unfused", args.steps, args.warmup)
+
+    comp, exch, flops = algorithmic(w, Q, inp.h0 is not None)
+    tokens = w.batch * w.seqlen
+    k_s = f_kms / 1e3
+    traffic = measured_traffic(w.name, Q)
+    roof = {"bound": "hbm", "achieved": comp / k_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": comp / k_s / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": "k_fused", "kernel_ms": f_kms, "bytes_per_launch": comp,
+            "achieved_with_state_exchange": (comp + exch) / k_s / 1e9,
+            "mfma_tflops": flops / k_s / 1e12,
+            "mfma_frac": flops / k_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]}
+    out = {
+        "metric": METRIC, "value": tokens / (f_wall / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": f_wall, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": Q,
+                   "state_dtype": w.state_dtype, "initial_state": inp.h0 is not None, "impl": "fused",
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "unfused": {"ms_per_step": u_wall, "value": tokens / (u_wall / 1e3), "kernels_ms": u_kms,
+                    "frac": comp / (u_kms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "speedup_fused_vs_unfused": u_wall / f_wall,
+    }
+    if not args.no_sweep:
+        sweep = {}
+        for q in (w.chunk_sweep or (Q,)):
+            if q == Q:
+                sweep[str(q)] = {"fused_ms": f_wall, "unfused_ms": u_wall}
+                continue
+            log("sweep Q=%d" % q)
+            fw, fk = time_impl(ssd, torch, g, w, q, "fused", max(5, args.steps // 2), 2)
+            uw, uk = time_impl(ssd, torch, g, w, q, "unfused", max(5, args.steps // 2), 2)
+            sweep[str(q)] = {"fused_ms": fw, "unfused_ms": uw, "fused_kernel_ms": fk}
+        out["chunk_sweep"] = sweep
+    del g
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

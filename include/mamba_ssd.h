@@ -68,7 +68,7 @@ typedef struct {
     int headdim;      /* P in {16, 32, 64, 128} */
     int dstate;       /* N in {32, 64, 128} (also 16 when in_dtype is SSD_F32) */
     int ngroups;      /* G >= 1, H % G == 0 */
-    int chunk_size;   /* Q in {64, 128, 192, 256} */
+    int chunk_size;   /* Q in {64, 128, 256} */
     int in_dtype;     /* ssd_dtype_t */
     int state_dtype;  /* ssd_dtype_t */
     int dt_softplus;  /* 1: dt = softplus(dt_raw + dt_bias); 0: dt = dt_raw + dt_bias */
@@ -107,6 +107,21 @@ ssd_status_t ssd_prefill(const ssd_params_t* p,
                          void* y, void* final_state,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ssd_prefill plus timing: records the caller's HIP events `kernel_begin` and
+ * `kernel_end` (hipEvent_t passed as void*, both required, created by the caller) on
+ * `stream` immediately before and after the SSD compute kernels -- the single fused
+ * kernel for SSD_IMPL_FUSED; the five step kernels (with the state-passing boundary
+ * copies between them) for SSD_IMPL_UNFUSED -- so their elapsed time excludes the
+ * fused form's boundary copies.  Same arguments and errors as ssd_prefill otherwise. */
+ssd_status_t ssd_prefill_timed(const ssd_params_t* p,
+                               const void* x, const void* dt, const float* A,
+                               const void* B, const void* C,
+                               const float* D, const float* dt_bias,
+                               const void* initial_state,
+                               void* y, void* final_state,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               void* kernel_begin, void* kernel_end);
+
 /* Synchronises `stream`, then reads the device status word the last fused
  * ssd_prefill on `workspace` left: SSD_OK, or SSD_ERR_SYNC_TIMEOUT when one of its
  * waits gave up (its outputs are then invalid).  SSD_ERR_HIP if a HIP call fails. */
@@ -124,10 +139,11 @@ const char* ssd_status_string(ssd_status_t s);
  *                                    with j > i are never written nor read      bmm
  *   s       fp32 [B][nc][H][P][N]    chunk-end state from a zero start
  *                                    (unfused only; 0 bytes when fused)          chunk_state
- *   states  state_dtype [B][K][H][P][N]  state entering chunk c lives in slot c % K;
- *                                    K = nc + 1 unfused, a small ring (K = 2) fused;
- *                                    slot 0 holds the initial state and slot nc % K
- *                                    the final state                            state_passing
+ *   states  state_dtype, K slots     state entering chunk c lives in slot c % K; slot 0
+ *                                    holds the initial state, slot nc % K the final one
+ *           unfused: [B][K = nc+1][H][P][N]                                      state_passing
+ *           fused:   a two-slot ring (K = 2) in an internal lane-major order
+ *                    (the fused kernel's own layout, not for callers)
  *   sync    uint32 words: per-chain chunk flags, cumsum / bmm completion flags,
  *           the work ticket and the abort word (fused only)
  *   status  uint32 device status word

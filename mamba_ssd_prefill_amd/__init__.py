@@ -24,7 +24,8 @@ IMPL_CODES = {"unfused": 0, "fused": 1}
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_INVALID_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
                 4: "SSD_ERR_MISALIGNED", 5: "SSD_ERR_WORKSPACE_TOO_SMALL", 6: "SSD_ERR_HIP",
                 7: "SSD_ERR_SYNC_TIMEOUT", 8: "SSD_ERR_INVALID_ARGUMENT"}
-EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill", "ssd_check_device_status",
+EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill", "ssd_prefill_timed",
+                    "ssd_check_device_status",
                     "ssd_status_string", "ssd_workspace_layout", "ssd_step_chunk_cumsum", "ssd_step_bmm",
                     "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan"]
 
@@ -80,6 +81,8 @@ def load_library():
     lib.ssd_validate.restype = ctypes.c_int
     lib.ssd_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_prefill.restype = ctypes.c_int
+    lib.ssd_prefill_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.ssd_prefill_timed.restype = ctypes.c_int
     lib.ssd_check_device_status.argtypes = [P, vp, vp]
     lib.ssd_check_device_status.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
@@ -180,11 +183,13 @@ def _check_tensors(x, dt, A, B, C, D, dt_bias, h0):
 
 
 def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_size=128, state_dtype=None,
-                impl="fused", dt_softplus=True, workspace=None, y=None, final_state=None):
+                impl="fused", dt_softplus=True, workspace=None, y=None, final_state=None, kernel_events=None):
     """Run one SSD prefill on the GPU; returns (y[B,L,H,P], final_state[B,H,P,N]).
 
     ``state_dtype`` defaults to initial_state's dtype, else float32.  ``workspace``
-    (uint8 device tensor), ``y`` and ``final_state`` may be passed to avoid allocation."""
+    (uint8 device tensor), ``y`` and ``final_state`` may be passed to avoid allocation.
+    ``kernel_events`` = (begin, end) torch.cuda.Event(enable_timing=True) pair, recorded
+    by the library around the SSD compute kernel(s) (ssd_prefill_timed)."""
     import torch
     _check_tensors(x, dt, A, B, C, D, dt_bias, initial_state)
     if state_dtype is None:
@@ -201,10 +206,17 @@ def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_
         final_state = torch.empty((Bt, H, P, N), dtype=state_dtype, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(prm, x.device)
-    rc = load_library().ssd_prefill(ctypes.byref(prm), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                    _ptr(dt_bias), _ptr(initial_state), _ptr(y), _ptr(final_state),
-                                    _ptr(workspace), workspace.numel(), _stream(x.device))
-    _check(rc, "ssd_prefill")
+    args = (ctypes.byref(prm), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+            _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(x.device))
+    if kernel_events is None:
+        _check(load_library().ssd_prefill(*args), "ssd_prefill")
+    else:
+        ev0, ev1 = kernel_events
+        for ev in (ev0, ev1):
+            if ev.cuda_event == 0:  # torch creates the HIP event lazily on first record
+                ev.record()
+        _check(load_library().ssd_prefill_timed(*args, ctypes.c_void_p(ev0.cuda_event), ctypes.c_void_p(ev1.cuda_event)),
+               "ssd_prefill_timed")
     return y, final_state
 
 

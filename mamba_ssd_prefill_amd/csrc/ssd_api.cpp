@@ -51,7 +51,7 @@ ssd_status_t validate(const ssd_params_t* p) {
     const int P = p->headdim, N = p->dstate, Q = p->chunk_size;
     if (P != 16 && P != 32 && P != 64 && P != 128) return SSD_ERR_UNSUPPORTED;
     if (N != 32 && N != 64 && N != 128 && !(N == 16 && p->in_dtype == SSD_F32)) return SSD_ERR_UNSUPPORTED;
-    if (Q != 64 && Q != 128 && Q != 192 && Q != 256) return SSD_ERR_UNSUPPORTED;
+    if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
     // every grid and ticket count must fit a signed 32-bit index
     const int64_t nc = ((int64_t)p->seqlen + Q - 1) / Q;
     const int64_t hpg = p->nheads / p->ngroups;
@@ -299,10 +299,10 @@ SSD_EXPORT ssd_status_t ssd_step_chunk_scan(const ssd_params_t* p, const void* x
 
 // ---- the whole prefill ----------------------------------------------------------------------
 
-SSD_EXPORT ssd_status_t ssd_prefill(const ssd_params_t* p, const void* x, const void* dt, const float* A,
-                                   const void* B, const void* C, const float* D, const float* dt_bias,
-                                   const void* initial_state, void* y, void* final_state, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt, const float* A, const void* B,
+                            const void* C, const float* D, const float* dt_bias, const void* initial_state, void* y,
+                            void* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                            hipEvent_t ev_begin, hipEvent_t ev_end) {
     Layout l;
     ssd_status_t s = check_ws(p, workspace, workspace_bytes, &l);
     if (s != SSD_OK) return s;
@@ -322,21 +322,49 @@ SSD_EXPORT ssd_status_t ssd_prefill(const ssd_params_t* p, const void* x, const 
     a.dt_bias = dt_bias;
     a.y = y;
     hipError_t e;
+    auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, st) : hipSuccess; };
     if (p->impl == SSD_IMPL_FUSED) {
-        // initial state into slot 0 and every sync word (flags, counters, status) reset
-        e = boundary_in(p, l, a, initial_state, a.flags, l.nsync, l.nflags, st);
+        // initial state into the ring's slot 0 and every sync word (flags, counters, status) reset
+        const int es = (int)elem_size(p->state_dtype), K = l.w.state_slots;
+        e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, p->dstate, K, 0, es,
+                                  a.flags, l.nsync, l.nflags, (uint32_t)(l.w.nchunks + 1), st);
+        if (e == hipSuccess) e = mark(ev_begin);
         if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED, p, a, st);
-        if (e == hipSuccess) e = boundary_out(p, l, a, final_state, st);
+        if (e == hipSuccess) e = mark(ev_end);
+        // final state out of the last chunk's slot
+        if (e == hipSuccess)
+            e = ssd::launch_ring_copy(a.states, final_state, 0, p->batch, p->nheads, p->headdim, p->dstate, K,
+                                      l.w.nchunks % K, es, nullptr, 0, 0, 1, st);
         return hip_status(e);
     }
-    e = dispatch(ssd::STEP_CUMSUM, p, a, st);
+    e = mark(ev_begin);
+    if (e == hipSuccess) e = dispatch(ssd::STEP_CUMSUM, p, a, st);
     if (e == hipSuccess) e = dispatch(ssd::STEP_BMM, p, a, st);
     if (e == hipSuccess) e = dispatch(ssd::STEP_CHUNK_STATE, p, a, st);
     if (e == hipSuccess) e = boundary_in(p, l, a, initial_state, a.status, 1, 0, st);
     if (e == hipSuccess) e = ssd::launch_state_passing(a, p->headdim * p->dstate, st);
     if (e == hipSuccess) e = boundary_out(p, l, a, final_state, st);
     if (e == hipSuccess) e = dispatch(ssd::STEP_CHUNK_SCAN, p, a, st);
+    if (e == hipSuccess) e = mark(ev_end);
     return hip_status(e);
+}
+
+SSD_EXPORT ssd_status_t ssd_prefill(const ssd_params_t* p, const void* x, const void* dt, const float* A,
+                                   const void* B, const void* C, const float* D, const float* dt_bias,
+                                   const void* initial_state, void* y, void* final_state, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    return prefill(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes, stream,
+                   nullptr, nullptr);
+}
+
+SSD_EXPORT ssd_status_t ssd_prefill_timed(const ssd_params_t* p, const void* x, const void* dt, const float* A,
+                                         const void* B, const void* C, const float* D, const float* dt_bias,
+                                         const void* initial_state, void* y, void* final_state, void* workspace,
+                                         size_t workspace_bytes, void* stream, void* kernel_begin,
+                                         void* kernel_end) {
+    if (!kernel_begin || !kernel_end) return SSD_ERR_NULL_POINTER;
+    return prefill(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes, stream,
+                   (hipEvent_t)kernel_begin, (hipEvent_t)kernel_end);
 }
 
 SSD_EXPORT ssd_status_t ssd_check_device_status(const ssd_params_t* p, const void* workspace, void* stream) {

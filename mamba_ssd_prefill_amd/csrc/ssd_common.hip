@@ -13,13 +13,13 @@ __global__ __launch_bounds__(256) void k_state_passing(SsdArgs a, int PN) {
     if (e >= PN) return;
     const int h = blockIdx.y, b = blockIdx.z;
     const int H = a.nheads, nc = a.nchunks, Q = a.chunk, K = a.slots;
-    f32x4 S = load_state4(a.states, a.state_dtype, ((size_t)b * K * H + h) * PN + e);
+    f32x4 S = load_state4<false>(a.states, a.state_dtype, ((size_t)b * K * H + h) * PN + e);
 #pragma unroll 4
     for (int c = 0; c < nc; ++c) {
         const float dec = __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
         const f32x4 sl = *(const f32x4*)(a.s + (((size_t)b * nc + c) * H + h) * PN + e);
         S = dec * S + sl;
-        store_state4(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);
+        store_state4<false>(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);
     }
 }
 
@@ -43,6 +43,55 @@ __global__ __launch_bounds__(256) void k_boundary(const char* src, size_t src_bs
     }
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsync; i += stride)
         sync[i] = (i < nflags && (i % flag_period) == 0) ? 1u : 0u;
+}
+
+// Boundary copies of the fused form, between the callers' [B][H][P][N] states and the ring
+// layout (see ring_chain): to_ring = 1 copies src (or zeros) into slot `slot`, to_ring = 0
+// copies slot `slot` out to dst.  One thread per 4 consecutive n of one (b, h, p).  Also
+// resets sync words like k_boundary.
+__global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, int to_ring, int B, int H, int P,
+                                                    int N, int K, int slot, int es, uint32_t* sync, size_t nsync,
+                                                    size_t nflags, uint32_t flag_period) {
+    const int PW = P < 32 ? P : 32, WPH = P / PW, MBP = PW / 16, NB = N / 16;
+    const size_t total = (size_t)B * H * P * (N / 4);
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int n = (int)(i % (N / 4)) * 4;
+        const size_t r = i / (N / 4);
+        const int p = (int)(r % P);
+        const int h = (int)((r / P) % H);
+        const int b = (int)(r / ((size_t)P * H));
+        const int ph = p / PW, pw = p % PW, pb = pw / 16, r16 = pw % 16;
+        const int nb = n / 16, q = (n % 16) / 4;
+        const size_t ring = ring_chain(b, slot, h, ph, K, H, WPH, NB * MBP) + ((size_t)(nb * MBP + pb) * 64 + 16 * q + r16) * 4;
+        const size_t user = (((size_t)b * H + h) * P + p) * N + n;
+        const size_t from = to_ring ? user : ring, to = to_ring ? ring : user;
+        if (es == 4) {
+            uint4 v = {0u, 0u, 0u, 0u};
+            if (src) v = *(const uint4*)(src + from * 4);
+            *(uint4*)(dst + to * 4) = v;
+        } else {
+            uint2 v = {0u, 0u};
+            if (src) v = *(const uint2*)(src + from * 2);
+            *(uint2*)(dst + to * 2) = v;
+        }
+    }
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsync; i += stride)
+        sync[i] = (i < nflags && (i % flag_period) == 0) ? 1u : 0u;
+}
+
+hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int N, int K, int slot,
+                            int es, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
+                            hipStream_t st) {
+    const size_t work = (size_t)B * H * P * (N / 4);
+    const size_t big = work > nsync ? work : nsync;
+    size_t grid = (big + 255) / 256;
+    if (grid < 1) grid = 1;
+    if (grid > 8192) grid = 8192;
+    const char* s = (const char*)src;
+    char* d = (char*)dst;
+    void* args[] = {&s, &d, &to_ring, &B, &H, &P, &N, &K, &slot, &es, &sync, &nsync, &nflags, &flag_period};
+    return hipLaunchKernel((const void*)&k_ring_copy, dim3((unsigned)grid), dim3(256), args, 0, st);
 }
 
 hipError_t launch_state_passing(SsdArgs& a, int PN, hipStream_t st) {

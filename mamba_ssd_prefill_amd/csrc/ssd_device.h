@@ -120,27 +120,6 @@ __device__ inline float softplus_f(float z) {
 
 template <typename T> __device__ inline float f32of(T v) { return (float)v; }
 
-__device__ inline f32x4 load_state4(const void* base, int dtype, size_t off) {
-    if (dtype == DT_F32) return *(const f32x4*)((const float*)base + off);
-    if (dtype == DT_F16) {
-        f16x4 v = *(const f16x4*)((const _Float16*)base + off);
-        return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-    }
-    bf16x4 v = *(const bf16x4*)((const __bf16*)base + off);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-
-__device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) {
-    if (dtype == DT_F32) {
-        *(f32x4*)((float*)base + off) = v;
-    } else if (dtype == DT_F16) {
-        *(f16x4*)((_Float16*)base + off) =
-            f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-    } else {
-        *(bf16x4*)((__bf16*)base + off) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-    }
-}
-
 template <typename T> __device__ inline typename TT<T>::v4 cvt4(f32x4 v) {
     typename TT<T>::v4 o;
     o[0] = (T)v[0];
@@ -157,48 +136,179 @@ template <typename T> __device__ inline typename TT<T>::frag load_frag(const T* 
         return *p;
 }
 
+// ---- data shared between workgroups of one launch ------------------------------------------
+// The fused kernel hands dt/acs, CB and inter-chunk states from one workgroup to another,
+// possibly on another XCD, whose L2 is not coherent with the writer's.  Those accesses
+// use device-scope ("sc1") loads and stores, which bypass non-coherent cache copies, and
+// ordering comes from waiting for the stores to complete before raising a flag.  This
+// avoids agent-scope acquire/release fences, which on gfx950 write back or invalidate
+// the whole L2 of the XCD (buffer_wbl2 / buffer_inv sc1) and would evict every other
+// workgroup's cached operands.  With COH = false (the unfused kernels, where kernel
+// boundaries order everything) the same helpers are plain vector accesses.
+template <bool COH> __device__ inline float ld_f32(const float* p) {
+    if constexpr (COH)
+        return __builtin_bit_cast(float, __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT));
+    else
+        return *p;
+}
+template <bool COH> __device__ inline void st_f32(float* p, float v) {
+    if constexpr (COH)
+        __hip_atomic_store((uint32_t*)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+template <bool COH> __device__ inline uint64_t ld_u64(const void* p) {
+    if constexpr (COH)
+        return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        return *(const uint64_t*)p;
+}
+template <bool COH> __device__ inline void st_u64(void* p, uint64_t v) {
+    if constexpr (COH)
+        __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *(uint64_t*)p = v;
+}
+template <bool COH> __device__ inline f32x4 ld_f32x4(const float* p) {
+    if constexpr (COH) {
+        const f32x2 lo = __builtin_bit_cast(f32x2, ld_u64<true>(p));
+        const f32x2 hi = __builtin_bit_cast(f32x2, ld_u64<true>(p + 2));
+        return f32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+        return *(const f32x4*)p;
+    }
+}
+template <bool COH> __device__ inline void st_f32x4(float* p, f32x4 v) {
+    if constexpr (COH) {
+        st_u64<true>(p, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}));
+        st_u64<true>(p + 2, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}));
+    } else {
+        *(f32x4*)p = v;
+    }
+}
+
+// 4 consecutive state elements in the state dtype, widened to / rounded from fp32.
+template <bool COH> __device__ inline f32x4 load_state4(const void* base, int dtype, size_t off) {
+    if (dtype == DT_F32) return ld_f32x4<COH>((const float*)base + off);
+    const uint64_t bits = ld_u64<COH>((const uint16_t*)base + off);
+    if (dtype == DT_F16) {
+        const f16x4 v = __builtin_bit_cast(f16x4, bits);
+        return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+    const bf16x4 v = __builtin_bit_cast(bf16x4, bits);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+template <bool COH> __device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) {
+    if (dtype == DT_F32) {
+        st_f32x4<COH>((float*)base + off, v);
+    } else if (dtype == DT_F16) {
+        st_u64<COH>((uint16_t*)base + off,
+                    __builtin_bit_cast(uint64_t, f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]}));
+    } else {
+        st_u64<COH>((uint16_t*)base + off,
+                    __builtin_bit_cast(uint64_t, bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]}));
+    }
+}
+
 // ---- cross-workgroup waits -------------------------------------------------------------
 // Poll a flag word until it is non-zero.  Bounded: after spin_limit polls (or once any
 // wait has given up) it raises the abort word and the status word and returns false, so
 // every workgroup still runs to completion.  All lanes of the calling wave(s) poll the
-// same address; the acquire fence after a successful poll orders the reads that follow.
+// same address.  Data published before the flag is then read with COH = true accesses.
 __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a) {
     uint32_t spins = 0;
+    bool ok = true;
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
         ++spins;
         if ((spins & 31u) == 0u) {
-            if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
+            if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                ok = false;
+                break;
+            }
             if (spins > a.spin_limit) {
                 __hip_atomic_store(a.abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(a.status, 7u /* SSD_ERR_SYNC_TIMEOUT */, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-                return false;
+                ok = false;
+                break;
             }
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return true;
+    // keeps the compiler from hoisting the reads of published data above the poll
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return ok;
 }
 
-// Every lane: make its own prior global writes visible at agent scope, then set *f.
+// s_waitcnt vmcnt(0): every global load and store this wave issued has completed.
+__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Every lane: its device-scope stores have completed, then set *f.
 __device__ inline void publish_flag_wave(uint32_t* f) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    wait_vm_all();
     __hip_atomic_store(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Whole workgroup: all threads release their writes, then thread 0 sets *f.
+// Whole workgroup: every wave's device-scope stores have completed, then thread 0 sets *f.
 __device__ inline void publish_flag_block(uint32_t* f) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    wait_vm_all();
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_store(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- the fused form's inter-chunk state ring -----------------------------------------------
+// Slot layout: for every (b, slot, h, p-slice ph) the owning wave's accumulator tiles follow
+// each other, lane after lane: element e of tile t held by lane l sits at
+// ring_chain(b, slot, h, ph) + (t * 64 + l) * 4 + e, where tile t = nb * MBP + pb covers
+// S[p = ph*PW + pb*16 + (l & 15)][n = nb*16 + 4*(l >> 4) + e].  Each lane therefore moves one
+// contiguous 16-byte (fp32) or 8-byte (16-bit) piece and a wave moves 1 KB / 512 B at once.
+// The boundary copies convert between this layout and the callers' [P][N] layout.
+__device__ inline size_t ring_chain(int b, int slot, int h, int ph, int K, int H, int WPH, int tiles) {
+    return ((((size_t)b * K + slot) * H + h) * WPH + ph) * (size_t)tiles * 256;
+}
+
+// Device-coherent (sc1) load / store of one lane's 4 ring elements at element offset `off`
+// inside the chain starting at element `chain`.
+__device__ inline f32x4 ring_load(const void* states, int dtype, size_t chain, int tiles, uint32_t off) {
+    const int es = dtype == DT_F32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((char*)const_cast<void*>(states) + chain * es, 0, tiles * 256 * es,
+                                          0x00020000);
+    if (dtype == DT_F32) return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 4, 0, 16));
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off * 2, 0, 16);
+    if (dtype == DT_F16) {
+        const f16x4 v = __builtin_bit_cast(f16x4, w);
+        return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+    const bf16x4 v = __builtin_bit_cast(bf16x4, w);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+__device__ inline void ring_store(void* states, int dtype, size_t chain, int tiles, uint32_t off, f32x4 v) {
+    const int es = dtype == DT_F32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((char*)states + chain * es, 0, tiles * 256 * es, 0x00020000);
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    if (dtype == DT_F32) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off * 4, 0, 16);
+    } else if (dtype == DT_F16) {
+        const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off * 2, 0, 16);
+    } else {
+        const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off * 2, 0, 16);
+    }
 }
 
 // ---- step 1: chunk_cumsum ([KF] item 4; [HW] segsum section: decay in log space) ------
 // For one (b, c): dt = softplus(dt_raw + dt_bias) (0 past L) and the inclusive in-chunk
 // running sum of dt * A, both fp32.  One wave per head; each lane owns Q/64 consecutive
 // tokens, then a wave-wide exclusive scan of the lane totals.
-template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c) {
+template <typename T, bool COH> __device__ void cumsum_tile(const SsdArgs& a, int b, int c) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Q = a.chunk, L = a.seqlen, H = a.nheads, nc = a.nchunks;
     const int V = Q >> 6;  // 1..4
@@ -232,8 +342,8 @@ template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (k < V) {
-                a.dtf[base + k] = d[k];
-                a.acs[base + k] = excl + run[k];
+                st_f32<COH>(a.dtf + base + k, d[k]);
+                st_f32<COH>(a.acs + base + k, excl + run[k]);
             }
     }
 }
@@ -243,7 +353,7 @@ template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c
 // columns i) so each lane stores 4 consecutive j of one row i.  Only blocks with
 // i-block >= j-block are formed: the scan step reads j <= i only.  Fragments come
 // straight from global memory (rows are n-contiguous).
-template <typename T, int N> __device__ void bmm_tile(const SsdArgs& a, int b, int c, int g) {
+template <typename T, int N, bool COH> __device__ void bmm_tile(const SsdArgs& a, int b, int c, int g) {
     constexpr int KPL = TT<T>::KPL, KI = 4 * KPL;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
@@ -269,7 +379,7 @@ template <typename T, int N> __device__ void bmm_tile(const SsdArgs& a, int b, i
                                        : vzero<frag>();
                 acc = TT<T>::mma(af[ks], bf, acc);
             }
-            *(f32x4*)(cbase + (size_t)(ib * 16 + r16) * Q + jb * 16 + 4 * q) = acc;
+            st_f32x4<COH>(cbase + (size_t)(ib * 16 + r16) * Q + jb * 16 + 4 * q, acc);
         }
     }
 }
@@ -352,6 +462,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
     typedef typename TT<T>::frag frag;
     typedef typename TT<T>::v4 v4;
 
+    constexpr bool COH = MODE == MODE_FUSED;  // data handed over inside one launch
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int hs = wave / WPH, ph = wave % WPH;
@@ -372,8 +483,8 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
         const int hh = e / Q, i = e - hh * Q;
         const bool ok = (tig * HPT + hh) < hpg;
         const size_t off = (((size_t)b * nc + c) * H + head0 + hh) * Q + i;
-        sDt[hh * QMAX + i] = ok ? a.dtf[off] : 0.f;
-        sAcs[hh * QMAX + i] = ok ? a.acs[off] : 0.f;
+        sDt[hh * QMAX + i] = ok ? ld_f32<COH>(a.dtf + off) : 0.f;
+        sAcs[hh * QMAX + i] = ok ? ld_f32<COH>(a.acs + off) : 0.f;
     }
     __syncthreads();
     for (int e = tid; e < HPT * Q; e += 256) {
@@ -438,17 +549,16 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                 uint32_t* fl = a.flags + chain * (nc + 1);
                 wait_flag(fl + c, a);
                 const int K = a.slots;
-                const int slot = c % K, nslot = (c + 1) % K;
+                const size_t rin = ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP);
+                const size_t rout = ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP);
                 const float dec = __expf(acs_last);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) {
-                        const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
-                        const size_t in = ((((size_t)b * K + slot) * H + h) * P + p) * N + n;
-                        const size_t out = ((((size_t)b * K + nslot) * H + h) * P + p) * N + n;
-                        sc[nb][pb] = load_state4(a.states, a.state_dtype, in);
-                        store_state4(a.states, a.state_dtype, out, dec * sc[nb][pb] + acc[nb][pb]);
+                        const uint32_t off = ((nb * MBP + pb) * 64 + lane) * 4;
+                        sc[nb][pb] = ring_load(a.states, a.state_dtype, rin, NB * MBP, off);
+                        ring_store(a.states, a.state_dtype, rout, NB * MBP, off, dec * sc[nb][pb] + acc[nb][pb]);
                     }
                 publish_flag_wave(fl + c + 1);
             }
@@ -461,8 +571,8 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
 #pragma unroll
                 for (int pb = 0; pb < MBP; ++pb) {
                     const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
-                    sc[nb][pb] = load_state4(a.states, a.state_dtype,
-                                             ((((size_t)b * K + slot) * H + h) * P + p) * N + n);
+                    sc[nb][pb] = load_state4<false>(a.states, a.state_dtype,
+                                                    ((((size_t)b * K + slot) * H + h) * P + p) * N + n);
                 }
         }
     }
@@ -539,7 +649,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                 for (int it = tid; it < W * (W / 4); it += 256) {
                     const int jq = it % (W / 4), ii = it / (W / 4);
                     const int i = i0 + ii, j = j0 + 4 * jq;
-                    const f32x4 cbv = *(const f32x4*)(cbase + (size_t)i * Q + j);
+                    const f32x4 cbv = ld_f32x4<COH>(cbase + (size_t)i * Q + j);
 #pragma unroll
                     for (int hh = 0; hh < HPT; ++hh) {
                         const float ai = sAcs[hh * QMAX + i];

@@ -1,22 +1,15 @@
-// ssd_kernels_bf16.hip -- kernel instantiations for bf16 inputs.
-#include "ssd_kernels.h"
+// ssd_kernels_bf16.hip -- bf16 inputs: dispatch on the chunk size.
+#include "ssd_launch.h"
 
 namespace ssd {
 
 hipError_t launch_step_bf16(int step, int P, int N, SsdArgs& a, hipStream_t st) {
-    if (P == 16 && N == 32) return launch_step_t<__bf16, 16, 32>(step, a, st);
-    if (P == 16 && N == 64) return launch_step_t<__bf16, 16, 64>(step, a, st);
-    if (P == 16 && N == 128) return launch_step_t<__bf16, 16, 128>(step, a, st);
-    if (P == 32 && N == 32) return launch_step_t<__bf16, 32, 32>(step, a, st);
-    if (P == 32 && N == 64) return launch_step_t<__bf16, 32, 64>(step, a, st);
-    if (P == 32 && N == 128) return launch_step_t<__bf16, 32, 128>(step, a, st);
-    if (P == 64 && N == 32) return launch_step_t<__bf16, 64, 32>(step, a, st);
-    if (P == 64 && N == 64) return launch_step_t<__bf16, 64, 64>(step, a, st);
-    if (P == 64 && N == 128) return launch_step_t<__bf16, 64, 128>(step, a, st);
-    if (P == 128 && N == 32) return launch_step_t<__bf16, 128, 32>(step, a, st);
-    if (P == 128 && N == 64) return launch_step_t<__bf16, 128, 64>(step, a, st);
-    if (P == 128 && N == 128) return launch_step_t<__bf16, 128, 128>(step, a, st);
-    return hipErrorNotSupported;
+    switch (a.chunk) {
+    case 64: return launch_step_bf16_q64(step, P, N, a, st);
+    case 128: return launch_step_bf16_q128(step, P, N, a, st);
+    case 256: return launch_step_bf16_q256(step, P, N, a, st);
+    default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace ssd

@@ -53,9 +53,19 @@ inline int heads_per_tile(int P) { return 4 / waves_per_head(P); }
 hipError_t launch_step_f32(int step, int P, int N, SsdArgs& a, hipStream_t st);
 hipError_t launch_step_f16(int step, int P, int N, SsdArgs& a, hipStream_t st);
 hipError_t launch_step_bf16(int step, int P, int N, SsdArgs& a, hipStream_t st);
+// 16-bit inputs, one translation unit per (dtype, chunk size)
+hipError_t launch_step_f16_q64(int step, int P, int N, SsdArgs& a, hipStream_t st);
+hipError_t launch_step_f16_q128(int step, int P, int N, SsdArgs& a, hipStream_t st);
+hipError_t launch_step_f16_q256(int step, int P, int N, SsdArgs& a, hipStream_t st);
+hipError_t launch_step_bf16_q64(int step, int P, int N, SsdArgs& a, hipStream_t st);
+hipError_t launch_step_bf16_q128(int step, int P, int N, SsdArgs& a, hipStream_t st);
+hipError_t launch_step_bf16_q256(int step, int P, int N, SsdArgs& a, hipStream_t st);
 
 // Non-templated kernels (ssd_common.hip).
 hipError_t launch_state_passing(SsdArgs& a, int PN, hipStream_t st);
+hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int N, int K, int slot,
+                            int es, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
+                            hipStream_t st);
 hipError_t launch_boundary(const void* src, size_t src_bs, void* dst, size_t dst_bs, size_t bytes_per_b,
                            int batch, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
                            hipStream_t st);

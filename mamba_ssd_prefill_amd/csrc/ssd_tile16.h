@@ -1,0 +1,469 @@
+// ssd_tile16.h -- chunk tile for 16-bit inputs (bf16 / fp16) on gfx950.
+//
+// Same arithmetic as chunk_tile in ssd_device.h (page keys are listed there), organised
+// around three gfx950 features:
+//   * buffer_load_dwordx4 ... lds: x, B and C chunks are copied from HBM straight into LDS
+//     (no register round trip), each lane moving one 16-byte piece; the buffer resource's
+//     record count makes tokens past the end of the sequence read as zeros;
+//   * ds_read_b64_tr_b16: LDS tiles stay in their HBM row layout ([token][column]) and the
+//     token-major MFMA operands (x and B with k = token) are read transposed;
+//   * rows are stored with their 16-byte pieces XOR-permuted (swizzled) so the transposed
+//     reads of 16 rows do not pile onto the same LDS banks.
+// The x operand of the chunk-state product is kept in registers and reused (unscaled)
+// by the diagonal-block product of chunk_scan; L = CB * decay * dt is formed directly in
+// registers from CB; y is produced 16 rows at a time.
+#pragma once
+
+#include "ssd_device.h"
+
+namespace ssd {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+#define SSD_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int P, int N, int Q> struct Geo16 {
+    static constexpr int PW = P < 32 ? P : 32;  // p columns per wave
+    static constexpr int WPH = P / PW;          // waves per head
+    static constexpr int HPT = 4 / WPH;         // heads per tile
+    static constexpr int MBP = PW / 16;
+    static constexpr int NB = N / 16;
+    static constexpr int KS = Q / 32;  // 32-token k-steps
+    static constexpr int QB = Q / 16;  // 16-token row blocks
+    static constexpr int SZ_X = HPT * Q * P * 2;
+    static constexpr int SZ_BC = Q * N * 2;
+    static constexpr int SZ_V = 3 * HPT * Q * 4;  // dt, acs, chunk-state weights
+    // CB (fp32) staged in LDS as 32-row bands holding only the columns the diagonal block
+    // reads: band r (rows 32r .. 32r+31) keeps columns [0, 32(r+1)) in rows of 8(r+1)+1
+    // 16-byte pieces (the odd pitch spreads 16 consecutive rows over all bank groups), each
+    // band padded to whole 1 KB copy instructions.  Only for Q <= 128 (it would not fit at 256).
+    static constexpr bool CB_LDS = Q <= 128;
+    static constexpr int band_pieces(int r) { return ((32 * (8 * r + 9) + 63) / 64) * 64; }
+    static constexpr int cb_pieces() {
+        int t = 0;
+        for (int r = 0; r < Q / 32; ++r) t += band_pieces(r);
+        return t;
+    }
+    static constexpr int SZ_CB = CB_LDS ? cb_pieces() * 16 : 0;
+    static constexpr int SZ_R1 = SZ_X > SZ_CB ? SZ_X : SZ_CB;  // x, later CB
+    static constexpr int SMEM = SZ_R1 + SZ_BC + SZ_V;
+    static_assert(Q % 32 == 0 && Q <= 256, "Q must be a multiple of 32, at most 256");
+    static_assert(N % 32 == 0, "N % 32 == 0");
+};
+
+// Swizzle of the 16-byte piece index inside a row of CH pieces.  A transposed operand read
+// touches rows k0 + 8q + m (q, m = 0..3, k0 a multiple of 32; the second read adds 4); the
+// swizzle sends those 16 rows to distinct 16-byte bank groups of a 256-byte bank line.
+template <int CH> __device__ inline int swz(int row) {
+    if constexpr (CH >= 16) return ((row & 3) | ((row >> 1) & 12)) & (CH - 1);
+    else if constexpr (CH == 8) return ((row >> 1) & 1) | ((row >> 2) & 6);  // 2 rows per bank line
+    else if constexpr (CH == 4) return (row >> 3) & 3;                        // 4 rows per bank line
+    else return (row >> 3) & 1;
+}
+
+// Tiles read row-wise (C in chunk_scan: 16 consecutive rows per read) use the low row bits.
+template <int CH> __device__ inline int swz_row(int row) { return row & (CH - 1); }
+
+enum : int { SWZ_TR = 0, SWZ_ROW = 1 };
+
+// Element offset of (row, col) in a swizzled [rows][COLS] 16-bit LDS tile.
+template <int COLS, int KIND = SWZ_TR> __device__ inline int sw_off(int row, int col) {
+    constexpr int CH = COLS / 8;
+    const int sz = KIND == SWZ_TR ? swz<CH>(row) : swz_row<CH>(row);
+    return row * COLS + (((col >> 3) ^ sz) << 3) + (col & 7);
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// rows [0, rows) of a row-major slice (row r at byte r * rs) -> swizzled LDS tile [rows][COLS];
+// the four waves split the 1 KB copy instructions.
+template <int COLS, int KIND = SWZ_TR>
+__device__ inline void dma_rows(void* lds_tile, __amdgpu_buffer_rsrc_t rs_src, int rows, uint32_t rs) {
+    constexpr int CH = COLS / 8;
+    constexpr int RPI = 64 / CH;  // rows per 1 KB instruction
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ninst = rows / RPI;
+    for (int k = wave; k < ninst; k += 4) {
+        const int row = k * RPI + lane / CH;
+        const int c = (lane % CH) ^ (KIND == SWZ_TR ? swz<CH>(row) : swz_row<CH>(row));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_src, SSD_LDS(void, (char*)lds_tile + k * 1024), 16,
+                                                 row * rs + c * 16, 0, 0, 0);
+    }
+}
+
+// Token-major MFMA operands from a swizzled [tokens][COLS] tile via transposed reads.  Lane l
+// of 16-lane group q points at row k0 + 8q + m (m = (l & 15) >> 2) and columns col0 + 4 (l & 3)
+// .. +3; the read hands lane l column col0 + (l & 15) of rows k0 + 8q .. +3, and a second read
+// 4 rows down completes the 8 tokens of the MFMA k slots.  The swizzle of those rows does not
+// depend on k0 (a multiple of 32) nor on the +4, so the lane offset for k0 = 0 is computed once
+// per column block and each k step is a constant offset.
+template <int COLS> __device__ inline int tr_lane_off(int col0) {
+    const int lane = threadIdx.x & 63;
+    const int q = lane >> 4, m = (lane & 15) >> 2, jj = lane & 3;
+    return sw_off<COLS>(8 * q + m, col0 + 4 * jj);
+}
+
+template <typename T, int COLS> __device__ inline typename TT<T>::frag tr_frag_at(const T* tile, int lane_off, int k0) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SSD_LDS(s16x4, tile + lane_off + k0 * COLS));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SSD_LDS(s16x4, tile + lane_off + (k0 + 4) * COLS));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename TT<T>::frag, w);
+}
+
+// 8 fp32 values -> one 16-bit MFMA fragment.
+template <typename T> __device__ inline typename TT<T>::frag pack8(f32x4 lo, f32x4 hi) {
+    return __builtin_shufflevector(cvt4<T>(lo), cvt4<T>(hi), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Copy the CB rows/columns the diagonal block reads (bands of the lower triangle, see
+// Geo16) from HBM into LDS.  aux = 16 makes the copy device-coherent (CB written by another
+// workgroup of the same launch).
+template <int Q, int AUX> __device__ inline void dma_cb_bands(float* lds, const float* cb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(cb, (uint32_t)(Q * Q * 4));
+    int base = 0;  // pieces
+#pragma unroll
+    for (int band = 0; band < Q / 32; ++band) {
+        const int pitch = 8 * band + 9;  // pieces per row (8(band+1) data + 1 pad)
+        const int used = 32 * pitch;
+        const int ninst = (used + 63) / 64;
+        for (int k = wave; k < ninst; k += 4) {
+            const int f = k * 64 + lane;  // piece index inside the band
+            const int row = f / pitch, pc = f - row * pitch;
+            const bool ok = f < used && pc < 8 * (band + 1);
+            const uint32_t voff = ok ? (uint32_t)(((32 * band + row) * Q + 4 * pc) * 4) : 0x40000000u;  // past num_records: reads as zeros
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SSD_LDS(void, lds + (base + k * 64) * 4), 16, voff, 0, 0, AUX);
+        }
+        base += ((used + 63) / 64) * 64;
+    }
+}
+
+// Offset (in floats) of CB[i][j] in the banded LDS copy.
+template <int Q> __device__ inline int cb_off(int i, int j) {
+    const int band = i >> 5;
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < Q / 32; ++r)
+        if (r < band) base += ((32 * (8 * r + 9) + 63) / 64) * 64;
+    return (base + (i & 31) * (8 * band + 9)) * 4 + j;
+}
+
+template <typename T, int P, int N, int Q, int MODE>
+__device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, char* smem) {
+    typedef Geo16<T, P, N, Q> G_;
+    constexpr int PW = G_::PW, WPH = G_::WPH, HPT = G_::HPT, MBP = G_::MBP, NB = G_::NB, KS = G_::KS,
+                  QB = G_::QB;
+    constexpr bool COH = MODE == MODE_FUSED;
+    constexpr int CB_AUX = COH ? 16 : 0;  // sc1 (device-coherent) reads of CB inside one launch
+    constexpr bool CB_LDS = G_::CB_LDS;
+    typedef typename TT<T>::frag frag;
+    typedef typename TT<T>::v4 v4;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int hs = wave / WPH, ph = wave % WPH;
+    const int L = a.seqlen, H = a.nheads, Gn = a.ngroups, nc = a.nchunks, hpg = a.hpg;
+    const int head0 = g * hpg + tig * HPT;
+    const int h = head0 + hs;
+    const bool hvalid = (tig * HPT + hs) < hpg;
+    const int tok0 = c * Q;
+    const int valid = L - tok0 < Q ? L - tok0 : Q;  // tokens of this chunk inside the sequence
+
+    T* sX = (T*)smem;                                     // R1: [HPT][Q][P] x, later CB bands
+    float* sCB = (float*)smem;
+    T* sBC = (T*)(smem + G_::SZ_R1);                      // R2: [Q][N] B, later C
+    // per-token vectors, [HPT][Q] each: sA2 = acs * log2(e); sW = chunk-state weights
+    // exp(acs[Q-1] - acs_j) dt_j, later replaced by sF; sDt = dt, later replaced by sE (see below)
+    float* sA2 = (float*)(smem + G_::SZ_R1 + G_::SZ_BC);
+    float* sW = sA2 + HPT * Q;
+    float* sDt = sW + HPT * Q;
+    float* sF = sW;
+    float* sE = sDt;
+
+    const float* cbp = a.cb + (((size_t)b * nc + c) * Gn + g) * (size_t)Q * Q;
+    const uint32_t xrs = (uint32_t)H * P * 2, bcrs = (uint32_t)Gn * N * 2;
+    const uint32_t bc_bytes = (uint32_t)(valid - 1) * bcrs + N * 2;
+    const size_t bc_off = (((size_t)b * L + tok0) * Gn + g) * N;
+
+    // ---- round 1: x of every head of the tile, and B (or C), into LDS ----------------------
+    for (int hh = 0; hh < HPT; ++hh) {
+        const bool ok = (tig * HPT + hh) < hpg;
+        const T* xb = (const T*)a.x + (((size_t)b * L + tok0) * H + head0 + (ok ? hh : 0)) * P;
+        const uint32_t bytes = ok ? (uint32_t)(valid - 1) * xrs + P * 2 : 0u;
+        dma_rows<P>(sX + hh * Q * P, make_rsrc(xb, bytes), Q, xrs);
+    }
+    if constexpr (MODE != MODE_SCAN)
+        dma_rows<N, SWZ_TR>(sBC, make_rsrc((const T*)a.B + bc_off, bc_bytes), Q, bcrs);
+    else
+        dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
+    for (int e = tid; e < HPT * Q; e += 256) {
+        const int hh = e / Q, i = e - hh * Q;
+        const bool ok = (tig * HPT + hh) < hpg;
+        const size_t off = (((size_t)b * nc + c) * H + head0 + hh) * Q + i;
+        sDt[e] = ok ? ld_f32<COH>(a.dtf + off) : 0.f;
+        sA2[e] = ok ? ld_f32<COH>(a.acs + off) * LOG2E : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < HPT * Q; e += 256) {
+        const int hh = e / Q;
+        sW[e] = __builtin_amdgcn_exp2f(sA2[hh * Q + Q - 1] - sA2[e]) * sDt[e];
+    }
+    wait_vm_all();
+    __syncthreads();
+
+    const float* a2_h = sA2 + hs * Q;
+
+    // x operand, token-major: xf[kk][pb] holds x[kk*32 + 8q .. +7][ph*PW + pb*16 + r16]
+    frag xf[KS][MBP];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int pb = 0; pb < MBP; ++pb) xf[kk][pb] = tr_frag_at<T, P>(sX + hs * Q * P, tr_lane_off<P>(ph * PW + pb * 16), kk * 32);
+
+    // S_c in accumulator layout, rounded to T: tile (nb, pb), lane -> S[p = ph*PW + pb*16 + r16][n = nb*16 + 4q + r]
+    v4 scb[NB][MBP];
+    if constexpr (MODE != MODE_SCAN) {
+        // ---- chunk_state: s^T[n][p] = sum_j B[j][n] (x[j][p] w_j) ----
+        f32x4 acc[NB][MBP];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb) acc[nb][pb] = vzero<f32x4>();
+        int boff[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) boff[nb] = tr_lane_off<N>(nb * 16);
+        if (hvalid) {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const f32x4 w0 = *(const f32x4*)(sW + hs * Q + kk * 32 + 8 * q);
+                const f32x4 w1 = *(const f32x4*)(sW + hs * Q + kk * 32 + 8 * q + 4);
+                frag xw[MBP];
+#pragma unroll
+                for (int pb = 0; pb < MBP; ++pb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xw[pb][e] = (T)((float)xf[kk][pb][e] * w0[e]);
+                        xw[pb][e + 4] = (T)((float)xf[kk][pb][e + 4] * w1[e]);
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const frag af = tr_frag_at<T, N>(sBC, boff[nb], kk * 32);
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) acc[nb][pb] = TT<T>::mma(af, xw[pb], acc[nb][pb]);
+                }
+            }
+        }
+        if constexpr (MODE == MODE_STATE) {
+            if (hvalid) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) {
+                        const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
+                        *(f32x4*)(a.s + ((((size_t)b * nc + c) * H + h) * P + p) * N + n) = acc[nb][pb];
+                    }
+            }
+            return;
+        } else {
+            // ---- round 2 (overlaps the hop): C and the CB bands into LDS, x for D x into registers
+            __syncthreads();  // every wave is done reading x and B from LDS
+            dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
+            if constexpr (CB_LDS) dma_cb_bands<Q, CB_AUX>(sCB, cbp);
+            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c
+            if (hvalid) {
+                const size_t chain = ((size_t)b * H + h) * WPH + ph;
+                uint32_t* fl = a.flags + chain * (nc + 1);
+                wait_flag(fl + c, a);
+                const int K = a.slots;
+                const size_t rin = ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP);
+                const size_t rout = ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP);
+                const float dec = __builtin_amdgcn_exp2f(a2_h[Q - 1]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) {
+                        const uint32_t off = ((nb * MBP + pb) * 64 + lane) * 4;
+                        const f32x4 sv = ring_load(a.states, a.state_dtype, rin, NB * MBP, off);
+                        ring_store(a.states, a.state_dtype, rout, NB * MBP, off, dec * sv + acc[nb][pb]);
+                        scb[nb][pb] = cvt4<T>(sv);
+                    }
+                publish_flag_wave(fl + c + 1);
+            }
+            wait_vm_all();
+            __syncthreads();  // C and CB are in LDS
+        }
+    } else {
+        __syncthreads();
+        // ---- round 2: the CB bands replace x in LDS; S_c and x for D x into registers ----
+        __syncthreads();  // every wave holds its x operand in registers
+        if constexpr (CB_LDS) dma_cb_bands<Q, 0>(sCB, cbp);
+        if (hvalid) {
+            const int K = a.slots, slot = c % K;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int pb = 0; pb < MBP; ++pb) {
+                    const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
+                    scb[nb][pb] = cvt4<T>(load_state4<false>(a.states, a.state_dtype,
+                                                             ((((size_t)b * K + slot) * H + h) * P + p) * N + n));
+                }
+        }
+        wait_vm_all();
+        __syncthreads();
+    }
+
+    if constexpr (MODE != MODE_STATE) {
+        // ---- chunk_scan, 16 rows of y at a time ----
+        // Per-token factors for the diagonal block, replacing sW and sDt in place (each element
+        // is rewritten by the thread that reads it):
+        //   sF[j] = exp(acs_r - acs_j) dt_j, r = the last token of j's 32-token block (<= dt_j);
+        //   sE[j] = acs_j log2(e) - log2(dt_j)  (+inf when dt_j = 0).
+        // Off the diagonal (all of a 32-column block left of the 16 rows) L[i][j] is split as
+        // exp(acs_i - acs_r) * exp(acs_r - acs_j) dt_j: both factors are at most 1 because acs does
+        // not increase along the chunk, so nothing overflows, and a factor only underflows when
+        // the exact product is below e^-87.  The column factor scales x once per tile; the row
+        // factor is one exp per lane per block.  On the diagonal, each element takes its own
+        // exp2(acs_i log2(e) - sE[j]) = exp(acs_i - acs_j) dt_j.
+        for (int e = tid; e < HPT * Q; e += 256) {
+            const int hh = e / Q, j = e - hh * Q;
+            const float dt = sDt[e];
+            const float ar = sA2[hh * Q + (j | 31)];
+            sF[e] = __builtin_amdgcn_exp2f(ar - sA2[e]) * dt;
+            sE[e] = sA2[e] - __log2f(dt);
+        }
+        __syncthreads();
+        if (!hvalid) return;
+        // S_c as the A operand of C . S^T; k slots of step ks: n = 32ks + 4q + {0..3} and
+        // 32ks + 16 + 4q + {0..3} (the accumulator layout), matched by the C reads below.
+        frag sop[N / 32][MBP];
+#pragma unroll
+        for (int ks = 0; ks < N / 32; ++ks)
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb)
+                sop[ks][pb] = __builtin_shufflevector(scb[2 * ks][pb], scb[2 * ks + 1][pb], 0, 1, 2, 3, 4, 5, 6, 7);
+        // x scaled by the column factor, for the blocks left of the diagonal
+        frag xs[KS][MBP];
+        const float* f_h = sF + hs * Q;
+        const float* e_h = sE + hs * Q;
+#pragma unroll
+        for (int kk = 0; kk + 1 < KS; ++kk) {
+            const f32x4 f0 = *(const f32x4*)(f_h + kk * 32 + 8 * q);
+            const f32x4 f1 = *(const f32x4*)(f_h + kk * 32 + 8 * q + 4);
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb) {
+                f32x4 lo, hi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo[e] = (float)xf[kk][pb][e] * f0[e];
+                    hi[e] = (float)xf[kk][pb][e + 4] * f1[e];
+                }
+                xs[kk][pb] = pack8<T>(lo, hi);
+            }
+        }
+        const float Dh = a.D ? a.D[h] : 0.f;
+        const __amdgpu_buffer_rsrc_t cbr = make_rsrc(cbp, (uint32_t)(Q * Q * 4));
+        // x for the D x term in the y layout (x[ib*16 + r16][ph*PW + pb*16 + 4q .. +3]), read from
+        // HBM/L2 two row blocks ahead of its use; rows past the sequence read as zeros
+        const __amdgpu_buffer_rsrc_t xr =
+            make_rsrc((const T*)a.x + (((size_t)b * L + tok0) * H + h) * P, (uint32_t)(valid - 1) * xrs + P * 2);
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        auto xd_load = [&](int ib, int pb) -> v4 {
+            const uint32_t off = (uint32_t)(ib * 16 + r16) * xrs + (uint32_t)(ph * PW + pb * 16 + 4 * q) * 2;
+            return __builtin_bit_cast(v4, __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0));
+        };
+        v4 xd0[MBP], xd1[MBP];
+#pragma unroll
+        for (int pb = 0; pb < MBP; ++pb) {
+            xd0[pb] = xd_load(0, pb);
+            xd1[pb] = xd_load(1, pb);
+        }
+        T* yg = (T*)a.y;
+        // this lane's C-row read offsets for k step ks (row r16 of a 16-row block; the row
+        // swizzle of C repeats every 16 rows, so block ib adds ib * 16 * N)
+        int clo[N / 32], chi[N / 32];
+#pragma unroll
+        for (int ks = 0; ks < N / 32; ++ks) {
+            clo[ks] = sw_off<N, SWZ_ROW>(r16, ks * 32 + 4 * q);
+            chi[ks] = sw_off<N, SWZ_ROW>(r16, ks * 32 + 16 + 4 * q);
+        }
+#pragma unroll
+        for (int ib = 0; ib < QB; ++ib) {
+            const int i = ib * 16 + r16;  // this lane's output row (column of y^T)
+            f32x4 accY[MBP];
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb) accY[pb] = vzero<f32x4>();
+#pragma unroll
+            for (int ks = 0; ks < N / 32; ++ks) {
+                const v4 lo = *(const v4*)(sBC + clo[ks] + ib * 16 * N);
+                const v4 hi = *(const v4*)(sBC + chi[ks] + ib * 16 * N);
+                const frag cf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int pb = 0; pb < MBP; ++pb) accY[pb] = TT<T>::mma(sop[ks][pb], cf, accY[pb]);
+            }
+            const float ai2 = a2_h[i];
+            const float ei = __builtin_amdgcn_exp2f(ai2);
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb) accY[pb] *= ei;
+            const int kd = ib >> 1;  // the diagonal 32-column block of these 16 rows
+#pragma unroll
+            for (int kk = 0; kk <= kd; ++kk) {
+                const int j0 = kk * 32 + 8 * q;
+                f32x4 c0, c1;
+                if constexpr (CB_LDS) {
+                    c0 = *(const f32x4*)(sCB + cb_off<Q>(i, j0));
+                    c1 = *(const f32x4*)(sCB + cb_off<Q>(i, j0 + 4));
+                } else {
+                    c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0) * 4, 0, CB_AUX));
+                    c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0 + 4) * 4, 0, CB_AUX));
+                }
+                if (kk < kd) {
+                    const float gi = __builtin_amdgcn_exp2f(ai2 - a2_h[kk * 32 + 31]);
+                    const frag lf = pack8<T>(c0 * gi, c1 * gi);
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) accY[pb] = TT<T>::mma(xs[kk][pb], lf, accY[pb]);
+                } else {
+                    const f32x4 e0 = *(const f32x4*)(e_h + j0), e1 = *(const f32x4*)(e_h + j0 + 4);
+                    f32x4 l0, l1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v0 = c0[e] * __builtin_amdgcn_exp2f(ai2 - e0[e]);
+                        const float v1 = c1[e] * __builtin_amdgcn_exp2f(ai2 - e1[e]);
+                        l0[e] = j0 + e <= i ? v0 : 0.f;
+                        l1[e] = j0 + 4 + e <= i ? v1 : 0.f;
+                    }
+                    const frag lf = pack8<T>(l0, l1);
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) accY[pb] = TT<T>::mma(xf[kk][pb], lf, accY[pb]);
+                }
+            }
+            // y = acc + D x, 4 consecutive p per lane
+            v4 xcur[MBP];
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb) {
+                xcur[pb] = xd0[pb];
+                xd0[pb] = xd1[pb];
+                if (ib + 2 < QB) xd1[pb] = xd_load(ib + 2, pb);
+            }
+            if (i < valid) {
+#pragma unroll
+                for (int pb = 0; pb < MBP; ++pb) {
+                    const int p = ph * PW + pb * 16 + 4 * q;
+                    f32x4 yv = accY[pb];
+                    yv[0] += Dh * (float)xcur[pb][0];
+                    yv[1] += Dh * (float)xcur[pb][1];
+                    yv[2] += Dh * (float)xcur[pb][2];
+                    yv[3] += Dh * (float)xcur[pb][3];
+                    *(v4*)(yg + (((size_t)b * L + tok0 + i) * H + h) * P + p) = cvt4<T>(yv);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace ssd

@@ -66,7 +66,7 @@ def test_status_strings(lib):
     (dict(headdim=48), UNSUP), (dict(headdim=256), UNSUP), (dict(dstate=16), UNSUP),
     (dict(dstate=256), UNSUP), (dict(chunk_size=32), UNSUP), (dict(chunk_size=100), UNSUP),
     (dict(chunk_size=512), UNSUP),
-    (dict(dstate=16, in_dtype="f32"), OK), (dict(chunk_size=192), OK), (dict(headdim=128), OK),
+    (dict(dstate=16, in_dtype="f32"), OK), (dict(chunk_size=192), UNSUP), (dict(headdim=128), OK),
     (dict(in_dtype=3), BADARG), (dict(state_dtype=-1), BADARG), (dict(impl=2), BADARG),
     (dict(dt_softplus=True, impl="unfused"), OK),
 ])

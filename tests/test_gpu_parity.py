@@ -42,7 +42,7 @@ CASES = [
     ("f16", "f32", False, 2, 640, 6, 64, 128, 1, 128),
     ("f16", "f16", True, 1, 1100, 8, 64, 128, 1, 128),
     ("bf16", "f32", True, 1, 900, 4, 64, 128, 1, 256),
-    ("bf16", "f32", True, 1, 900, 4, 64, 128, 1, 192),
+    ("f16", "f32", True, 2, 700, 4, 64, 64, 2, 256),
     ("f32", "f32", True, 1, 300, 4, 64, 128, 1, 128),
     ("bf16", "f32", True, 2, 333, 8, 32, 64, 4, 64),
     ("bf16", "f32", True, 1, 400, 6, 16, 32, 3, 128),
