@@ -258,6 +258,17 @@ __device__ inline void publish_flag_block(uint32_t* f) {
     if (threadIdx.x == 0) __hip_atomic_store(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Buffer resource for [base, base + bytes); every caller passes wave-uniform values, which are
+// made scalar explicitly so the descriptor lives in SGPRs (a descriptor the compiler cannot
+// prove uniform is re-built per lane in a loop around every access).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* p = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 // ---- the fused form's inter-chunk state ring -----------------------------------------------
 // Slot layout: for every (b, slot, h, p-slice ph) the owning wave's accumulator tiles follow
 // each other, lane after lane: element e of tile t held by lane l sits at
@@ -270,12 +281,13 @@ __device__ inline size_t ring_chain(int b, int slot, int h, int ph, int K, int H
 }
 
 // Device-coherent (sc1) load / store of one lane's 4 ring elements at element offset `off`
-// inside the chain starting at element `chain`.
-__device__ inline f32x4 ring_load(const void* states, int dtype, size_t chain, int tiles, uint32_t off) {
+// of the chain whose descriptor is `r` (ring_rsrc).
+__device__ inline __amdgpu_buffer_rsrc_t ring_rsrc(const void* states, int dtype, size_t chain, int tiles) {
     const int es = dtype == DT_F32 ? 4 : 2;
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((char*)const_cast<void*>(states) + chain * es, 0, tiles * 256 * es,
-                                          0x00020000);
+    return make_rsrc((const char*)states + chain * es, tiles * 256 * es);
+}
+
+__device__ inline f32x4 ring_load(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t off) {
     if (dtype == DT_F32) return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 4, 0, 16));
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off * 2, 0, 16);
@@ -287,10 +299,7 @@ __device__ inline f32x4 ring_load(const void* states, int dtype, size_t chain, i
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
-__device__ inline void ring_store(void* states, int dtype, size_t chain, int tiles, uint32_t off, f32x4 v) {
-    const int es = dtype == DT_F32 ? 4 : 2;
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((char*)states + chain * es, 0, tiles * 256 * es, 0x00020000);
+__device__ inline void ring_store(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t off, f32x4 v) {
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     if (dtype == DT_F32) {
@@ -309,7 +318,7 @@ __device__ inline void ring_store(void* states, int dtype, size_t chain, int til
 // running sum of dt * A, both fp32.  One wave per head; each lane owns Q/64 consecutive
 // tokens, then a wave-wide exclusive scan of the lane totals.
 template <typename T, bool COH> __device__ void cumsum_tile(const SsdArgs& a, int b, int c) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int Q = a.chunk, L = a.seqlen, H = a.nheads, nc = a.nchunks;
     const int V = Q >> 6;  // 1..4
     const T* dtr = (const T*)a.dt;
@@ -355,7 +364,7 @@ template <typename T, bool COH> __device__ void cumsum_tile(const SsdArgs& a, in
 // straight from global memory (rows are n-contiguous).
 template <typename T, int N, bool COH> __device__ void bmm_tile(const SsdArgs& a, int b, int c, int g) {
     constexpr int KPL = TT<T>::KPL, KI = 4 * KPL;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = lane >> 4, r16 = lane & 15;
     const int Q = a.chunk, L = a.seqlen, G = a.ngroups, nc = a.nchunks;
     const int QB = Q >> 4;
@@ -463,7 +472,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
     typedef typename TT<T>::v4 v4;
 
     constexpr bool COH = MODE == MODE_FUSED;  // data handed over inside one launch
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, r16 = lane & 15;
     const int hs = wave / WPH, ph = wave % WPH;
     const int Q = a.chunk, L = a.seqlen, H = a.nheads, Gn = a.ngroups, nc = a.nchunks, hpg = a.hpg;
@@ -549,16 +558,18 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                 uint32_t* fl = a.flags + chain * (nc + 1);
                 wait_flag(fl + c, a);
                 const int K = a.slots;
-                const size_t rin = ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP);
-                const size_t rout = ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP);
+                const __amdgpu_buffer_rsrc_t rin =
+                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
+                const __amdgpu_buffer_rsrc_t rout =
+                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const float dec = __expf(acs_last);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) {
                         const uint32_t off = ((nb * MBP + pb) * 64 + lane) * 4;
-                        sc[nb][pb] = ring_load(a.states, a.state_dtype, rin, NB * MBP, off);
-                        ring_store(a.states, a.state_dtype, rout, NB * MBP, off, dec * sc[nb][pb] + acc[nb][pb]);
+                        sc[nb][pb] = ring_load(rin, a.state_dtype, off);
+                        ring_store(rout, a.state_dtype, off, dec * sc[nb][pb] + acc[nb][pb]);
                     }
                 publish_flag_wave(fl + c + 1);
             }

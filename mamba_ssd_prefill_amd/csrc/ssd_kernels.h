@@ -45,7 +45,7 @@ template <typename T, int P, int N> __global__ __launch_bounds__(256) void k_fus
     __shared__ uint32_t s_ticket;
     if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
     __syncthreads();
-    const uint32_t t = s_ticket;
+    const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);  // uniform: keeps tile math scalar
     const uint32_t Bn = a.batch, nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
     const uint32_t t_cs = Bn * nc, t_bmm = Bn * nc * Gn;
     if (t >= t_cs + t_bmm + Bn * nc * Gn * tpg) return;  // only if the ticket word was not reset
@@ -91,7 +91,7 @@ template <typename T, int P, int N, int Q> __global__ __launch_bounds__(256, 2) 
     __shared__ uint32_t s_ticket;
     if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
     __syncthreads();
-    const uint32_t t = s_ticket;
+    const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);  // uniform: keeps tile math scalar
     const uint32_t Bn = a.batch, nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
     const uint32_t t_cs = Bn * nc, t_bmm = Bn * nc * Gn;
     if (t >= t_cs + t_bmm + Bn * nc * Gn * tpg) return;  // only if the ticket word was not reset

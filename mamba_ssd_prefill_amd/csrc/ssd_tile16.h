@@ -75,17 +75,13 @@ template <int COLS, int KIND = SWZ_TR> __device__ inline int sw_off(int row, int
     return row * COLS + (((col >> 3) ^ sz) << 3) + (col & 7);
 }
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
 // rows [0, rows) of a row-major slice (row r at byte r * rs) -> swizzled LDS tile [rows][COLS];
 // the four waves split the 1 KB copy instructions.
 template <int COLS, int KIND = SWZ_TR>
 __device__ inline void dma_rows(void* lds_tile, __amdgpu_buffer_rsrc_t rs_src, int rows, uint32_t rs) {
     constexpr int CH = COLS / 8;
     constexpr int RPI = 64 / CH;  // rows per 1 KB instruction
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ninst = rows / RPI;
     for (int k = wave; k < ninst; k += 4) {
         const int row = k * RPI + lane / CH;
@@ -124,7 +120,7 @@ template <typename T> __device__ inline typename TT<T>::frag pack8(f32x4 lo, f32
 // Geo16) from HBM into LDS.  aux = 16 makes the copy device-coherent (CB written by another
 // workgroup of the same launch).
 template <int Q, int AUX> __device__ inline void dma_cb_bands(float* lds, const float* cb) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(cb, (uint32_t)(Q * Q * 4));
     int base = 0;  // pieces
 #pragma unroll
@@ -164,7 +160,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     typedef typename TT<T>::frag frag;
     typedef typename TT<T>::v4 v4;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, r16 = lane & 15;
     const int hs = wave / WPH, ph = wave % WPH;
     const int L = a.seqlen, H = a.nheads, Gn = a.ngroups, nc = a.nchunks, hpg = a.hpg;
@@ -271,30 +267,34 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             }
             return;
         } else {
-            // ---- round 2 (overlaps the hop): C and the CB bands into LDS, x for D x into registers
-            __syncthreads();  // every wave is done reading x and B from LDS
-            dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
-            if constexpr (CB_LDS) dma_cb_bands<Q, CB_AUX>(sCB, cbp);
-            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c
+            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c.  It comes before the round-2
+            // copies so that its flag waits only for the state stores: the hop is the serial
+            // chain between chunks.
             if (hvalid) {
                 const size_t chain = ((size_t)b * H + h) * WPH + ph;
                 uint32_t* fl = a.flags + chain * (nc + 1);
                 wait_flag(fl + c, a);
                 const int K = a.slots;
-                const size_t rin = ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP);
-                const size_t rout = ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP);
+                const __amdgpu_buffer_rsrc_t rin =
+                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
+                const __amdgpu_buffer_rsrc_t rout =
+                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const float dec = __builtin_amdgcn_exp2f(a2_h[Q - 1]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) {
                         const uint32_t off = ((nb * MBP + pb) * 64 + lane) * 4;
-                        const f32x4 sv = ring_load(a.states, a.state_dtype, rin, NB * MBP, off);
-                        ring_store(a.states, a.state_dtype, rout, NB * MBP, off, dec * sv + acc[nb][pb]);
+                        const f32x4 sv = ring_load(rin, a.state_dtype, off);
+                        ring_store(rout, a.state_dtype, off, dec * sv + acc[nb][pb]);
                         scb[nb][pb] = cvt4<T>(sv);
                     }
                 publish_flag_wave(fl + c + 1);
             }
+            // ---- round 2: C and the CB bands into LDS (x and B are no longer read)
+            __syncthreads();
+            dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
+            if constexpr (CB_LDS) dma_cb_bands<Q, CB_AUX>(sCB, cbp);
             wait_vm_all();
             __syncthreads();  // C and CB are in LDS
         }
