@@ -56,7 +56,8 @@ typedef enum {
     SSD_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < ssd_prefill_workspace_size() */
     SSD_ERR_HIP = 6,                 /* a HIP runtime call or kernel launch failed */
     SSD_ERR_SYNC_TIMEOUT = 7,        /* fused kernel: a cross-workgroup wait hit its spin limit (results invalid) */
-    SSD_ERR_INVALID_ARGUMENT = 8     /* an enum field is out of range, or struct_size is too small */
+    SSD_ERR_INVALID_ARGUMENT = 8,    /* an enum field is out of range, or struct_size is too small */
+    SSD_ERR_SCHEDULE = 9             /* fused kernel: a work partition found no workgroup on its XCD (results invalid) */
 } ssd_status_t;
 
 /* Problem description.  Set struct_size = sizeof(ssd_params_t). */
@@ -123,8 +124,9 @@ ssd_status_t ssd_prefill_timed(const ssd_params_t* p,
                                void* kernel_begin, void* kernel_end);
 
 /* Synchronises `stream`, then reads the device status word the last fused
- * ssd_prefill on `workspace` left: SSD_OK, or SSD_ERR_SYNC_TIMEOUT when one of its
- * waits gave up (its outputs are then invalid).  SSD_ERR_HIP if a HIP call fails. */
+ * ssd_prefill on `workspace` left: SSD_OK, SSD_ERR_SYNC_TIMEOUT when one of its waits
+ * gave up, or SSD_ERR_SCHEDULE when one of its work partitions was never served (in
+ * both cases its outputs are invalid).  SSD_ERR_HIP if a HIP call fails. */
 ssd_status_t ssd_check_device_status(const ssd_params_t* p, const void* workspace, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
@@ -137,16 +139,20 @@ const char* ssd_status_string(ssd_status_t s);
  *   acs     fp32 [B][nc][H][Q]       inclusive in-chunk sum of dt * A            chunk_cumsum
  *   cb      fp32 [B][nc][G][Q][Q]    CB[i][j] = C_i . B_j for j <= i; entries
  *                                    with j > i are never written nor read      bmm
+ *           fused: [B*G + 7][nc][Q][Q], one [nc] run per (work partition, (b, g) pair)
  *   s       fp32 [B][nc][H][P][N]    chunk-end state from a zero start
  *                                    (unfused only; 0 bytes when fused)          chunk_state
  *   states  state_dtype, K slots     state entering chunk c lives in slot c % K; slot 0
  *                                    holds the initial state, slot nc % K the final one
  *           unfused: [B][K = nc+1][H][P][N]                                      state_passing
- *           fused:   a two-slot ring (K = 2) in an internal lane-major order
- *                    (the fused kernel's own layout, not for callers)
- *   sync    uint32 words: per-chain chunk flags, cumsum / bmm completion flags,
- *           the work ticket and the abort word (fused only)
+ *           fused:   one slot (K = 1) per chain, updated in place chunk after chunk, in
+ *                    an internal lane-major order (the fused kernel's own layout)
+ *   sync    uint32 words: per-chain chunk flags, cumsum / bmm completion flags, one
+ *           work counter and one owner word per partition, the exit counter and the
+ *           abort word (fused only)
  *   status  uint32 device status word
+ * The fused form splits its work into one partition per XCD of the device (at most 8);
+ * the sizes above are bounds that hold for any such split.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
     size_t total_bytes;

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/mamba_ssd.h"
 #include "ssd_launch.h"
 
@@ -12,7 +14,7 @@
 
 namespace {
 
-constexpr int kRingSlots = 2;        // fused form: states ring depth
+constexpr int kRingSlots = 1;        // fused form: one state slot per chain, updated in place
 constexpr size_t kAlign = 256;       // workspace region alignment
 constexpr uint32_t kDefaultSpin = 1u << 22;
 
@@ -32,10 +34,15 @@ uint32_t spin_limit() {
 
 struct Layout {
     ssd_workspace_layout_t w;
-    size_t nflags, nsync;  // sync words: [flags | cs_done | bmm_done | ticket | abort | status]
-    size_t flags_w, cs_w, bmm_w, ticket_w, abort_w, status_w;
+    // sync words: [flags | cs_done | bmm_done | tickets | owners | exit | abort | status]
+    size_t nflags, nsync;
+    size_t flags_w, cs_w, bmm_w, ticket_w, owner_w, exit_w, abort_w, status_w;
     int tpg, wph;
 };
+
+// Upper bound of the fused form's (b, g) pair slots: the B*G pairs, plus one more for every
+// partition boundary that splits a pair (each side keeps its own cumsum / bmm copy).
+size_t pair_slots_max(const ssd_params_t* p) { return (size_t)p->batch * p->ngroups + ssd::kMaxXcc - 1; }
 
 ssd_status_t validate(const ssd_params_t* p) {
     if (!p) return SSD_ERR_NULL_POINTER;
@@ -56,7 +63,8 @@ ssd_status_t validate(const ssd_params_t* p) {
     const int64_t nc = ((int64_t)p->seqlen + Q - 1) / Q;
     const int64_t hpg = p->nheads / p->ngroups;
     const int64_t tpg = (hpg + ssd::heads_per_tile(P) - 1) / ssd::heads_per_tile(P);
-    const int64_t tickets = (int64_t)p->batch * nc * (1 + p->ngroups + (int64_t)p->ngroups * tpg);
+    const int64_t pairs = (int64_t)p->batch * p->ngroups;
+    const int64_t tickets = nc * (2 * (pairs + ssd::kMaxXcc) + pairs * tpg);
     if (tickets >= (int64_t)1 << 31) return SSD_ERR_INVALID_SHAPE;
     if ((int64_t)p->batch * p->seqlen * p->nheads >= (int64_t)1 << 40) return SSD_ERR_INVALID_SHAPE;
     return SSD_OK;
@@ -76,15 +84,18 @@ Layout layout(const ssd_params_t* p) {
     w.state_slots = (int)K;
     w.dt_bytes = B * nc * H * Q * 4;
     w.acs_bytes = w.dt_bytes;
-    w.cb_bytes = B * nc * G * Q * Q * 4;
+    const size_t PS = fused ? pair_slots_max(p) : 0;
+    w.cb_bytes = (fused ? PS : B * G) * nc * Q * Q * 4;
     w.s_bytes = fused ? 0 : B * nc * H * P * N * 4;
     w.states_bytes = B * K * H * P * N * elem_size(p->state_dtype);
     l.nflags = fused ? B * H * (size_t)l.wph * (nc + 1) : 0;
     l.flags_w = 0;
     l.cs_w = l.nflags;
-    l.bmm_w = l.cs_w + (fused ? B * nc : 0);
-    l.ticket_w = l.bmm_w + (fused ? B * nc * G : 0);
-    l.abort_w = l.ticket_w + 1;
+    l.bmm_w = l.cs_w + PS * nc;
+    l.ticket_w = l.bmm_w + PS * nc;
+    l.owner_w = l.ticket_w + (fused ? (size_t)ssd::kMaxXcc * ssd::kTicketStride : 0);
+    l.exit_w = l.owner_w + (fused ? ssd::kMaxXcc : 0);
+    l.abort_w = l.exit_w + (fused ? 1 : 0);
     l.status_w = l.abort_w + 1;
     l.nsync = l.status_w + 1;
     w.sync_bytes = l.nsync * 4;
@@ -135,6 +146,8 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.cs_done = sync + l.cs_w;
     a.bmm_done = sync + l.bmm_w;
     a.ticket = sync + l.ticket_w;
+    a.owner = sync + l.owner_w;
+    a.exit_count = sync + l.exit_w;
     a.abort_word = sync + l.abort_w;
     a.status = sync + l.status_w;
     a.batch = p->batch;
@@ -150,6 +163,60 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.softplus = p->dt_softplus;
     a.spin_limit = spin_limit();
     return a;
+}
+
+// Per-device facts the fused launch needs: its XCD count (the number of work partitions,
+// at most kMaxXcc) and compute-unit count.
+struct DevInfo {
+    int nparts, cus;
+};
+
+hipError_t device_info(DevInfo* out) {
+    static std::mutex mu;
+    static DevInfo cache[64];
+    static bool have[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < 64 && have[dev]) {
+        *out = cache[dev];
+        return hipSuccess;
+    }
+    int xcc = 1, cus = 1;
+    e = hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    DevInfo d;
+    d.nparts = xcc < 1 ? 1 : (xcc > ssd::kMaxXcc ? ssd::kMaxXcc : xcc);
+    d.cus = cus < 1 ? 1 : cus;
+    if (dev >= 0 && dev < 64) {
+        cache[dev] = d;
+        have[dev] = true;
+    }
+    *out = d;
+    return hipSuccess;
+}
+
+// Fused form: split the U = B*G*tpg chains into nparts contiguous, near-equal ranges and give
+// each partition's (b, g) pairs consecutive cb / flag slots.
+void set_partitions(const ssd_params_t* p, const Layout& l, const DevInfo& d, ssd::SsdArgs& a) {
+    const int64_t U = (int64_t)p->batch * p->ngroups * l.tpg;
+    const int64_t nc = l.w.nchunks;
+    a.nparts = d.nparts;
+    a.cu_count = d.cus;
+    int pb = 0, maxw = 0;
+    for (int x = 0; x <= d.nparts; ++x) {
+        a.part_u0[x] = (int)(U * x / d.nparts);
+        a.part_pb[x] = pb;
+        if (x == d.nparts) break;
+        const int u0 = (int)(U * x / d.nparts), u1 = (int)(U * (x + 1) / d.nparts);
+        const int np = u1 > u0 ? (u1 - 1) / l.tpg - u0 / l.tpg + 1 : 0;
+        pb += np;
+        const int64_t work = nc * (2 * np + (u1 - u0));
+        if (work > maxw) maxw = (int)work;
+    }
+    a.part_max_work = maxw;
 }
 
 ssd_status_t check_ws(const ssd_params_t* p, void* ws, size_t ws_bytes, Layout* l) {
@@ -209,6 +276,7 @@ SSD_EXPORT const char* ssd_status_string(ssd_status_t s) {
     case SSD_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case SSD_ERR_SYNC_TIMEOUT: return "a cross-workgroup wait hit its spin limit; outputs are invalid";
     case SSD_ERR_INVALID_ARGUMENT: return "an enum field is out of range or struct_size is too small";
+    case SSD_ERR_SCHEDULE: return "fused kernel: a work partition was not served by any workgroup; outputs are invalid";
     default: return "unknown status";
     }
 }
@@ -324,6 +392,10 @@ static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt
     hipError_t e;
     auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, st) : hipSuccess; };
     if (p->impl == SSD_IMPL_FUSED) {
+        DevInfo d;
+        e = device_info(&d);
+        if (e != hipSuccess) return hip_status(e);
+        set_partitions(p, l, d, a);
         // initial state into the ring's slot 0 and every sync word (flags, counters, status) reset
         const int es = (int)elem_size(p->state_dtype), K = l.w.state_slots;
         e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, p->dstate, K, 0, es,

@@ -13,13 +13,13 @@ __global__ __launch_bounds__(256) void k_state_passing(SsdArgs a, int PN) {
     if (e >= PN) return;
     const int h = blockIdx.y, b = blockIdx.z;
     const int H = a.nheads, nc = a.nchunks, Q = a.chunk, K = a.slots;
-    f32x4 S = load_state4<false>(a.states, a.state_dtype, ((size_t)b * K * H + h) * PN + e);
+    f32x4 S = load_state4(a.states, a.state_dtype, ((size_t)b * K * H + h) * PN + e);
 #pragma unroll 4
     for (int c = 0; c < nc; ++c) {
         const float dec = __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
         const f32x4 sl = *(const f32x4*)(a.s + (((size_t)b * nc + c) * H + h) * PN + e);
         S = dec * S + sl;
-        store_state4<false>(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);
+        store_state4(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);
     }
 }
 

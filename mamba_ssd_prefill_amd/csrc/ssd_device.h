@@ -113,6 +113,16 @@ template <typename T, int P, int N> struct Geo {
 };
 
 // ---- scalar helpers ------------------------------------------------------------------
+// threadIdx.x through an opaque move.  Tile code that the fused kernel runs inside its work
+// loop derives its lane offsets from this, so the compiler computes them where they are used
+// on each trip instead of hoisting them out of the loop and keeping them all live.
+__device__ inline int tid_here() {
+    int t;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+    return t;
+}
+
+
 __device__ inline float softplus_f(float z) {
     // log(1 + e^z) without overflow
     return z > 0.f ? z + log1pf(__expf(-z)) : log1pf(__expf(z));
@@ -136,62 +146,44 @@ template <typename T> __device__ inline typename TT<T>::frag load_frag(const T* 
         return *p;
 }
 
+// Buffer resource for [base, base + bytes); every caller passes wave-uniform values, which are
+// made scalar explicitly so the descriptor lives in SGPRs (a descriptor the compiler cannot
+// prove uniform is re-built per lane in a loop around every access).  Reads past `bytes`
+// return zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* p = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 // ---- data shared between workgroups of one launch ------------------------------------------
-// The fused kernel hands dt/acs, CB and inter-chunk states from one workgroup to another,
-// possibly on another XCD, whose L2 is not coherent with the writer's.  Those accesses
-// use device-scope ("sc1") loads and stores, which bypass non-coherent cache copies, and
-// ordering comes from waiting for the stores to complete before raising a flag.  This
-// avoids agent-scope acquire/release fences, which on gfx950 write back or invalidate
-// the whole L2 of the XCD (buffer_wbl2 / buffer_inv sc1) and would evict every other
-// workgroup's cached operands.  With COH = false (the unfused kernels, where kernel
-// boundaries order everything) the same helpers are plain vector accesses.
-template <bool COH> __device__ inline float ld_f32(const float* p) {
-    if constexpr (COH)
-        return __builtin_bit_cast(float, __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT));
-    else
-        return *p;
+// The fused kernel keeps every producer -> consumer hand-off (dt/acs, CB, the inter-chunk
+// states and the flags that order them) inside one XCD: a chain's chunk tiles and the
+// cumsum / bmm tiles they read belong to one work partition, served only by workgroups
+// running on one XCD (see fused_loop).  On gfx950 (measured on MI355X):
+//   * plain stores go through the CU's L1 into the XCD's L2, which is write-back: another
+//     XCD does not see them until the kernel ends, a workgroup on the same XCD does;
+//   * loads with sc1 set miss the CU's L1 and are served by the L2 (about 200 cycles when
+//     the line is there); sc0 alone, and plain loads, may return a stale L1 copy, and
+//     buffer_inv sc0 does not prevent that outside thread-group-split dispatches;
+// so a producer stores plainly, waits for its stores (s_waitcnt vmcnt(0)) and raises a flag;
+// the consumer polls the flag and reads the data with sc1 loads.  No cache-wide fence is
+// needed: an agent-scope acquire / release would invalidate / write back the whole L2.
+constexpr int AUX_L2 = 16;  // sc1
+
+template <int AUX> __device__ inline float bload_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, AUX));
 }
-template <bool COH> __device__ inline void st_f32(float* p, float v) {
-    if constexpr (COH)
-        __hip_atomic_store((uint32_t*)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-        *p = v;
-}
-template <bool COH> __device__ inline uint64_t ld_u64(const void* p) {
-    if constexpr (COH)
-        return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-        return *(const uint64_t*)p;
-}
-template <bool COH> __device__ inline void st_u64(void* p, uint64_t v) {
-    if constexpr (COH)
-        __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-        *(uint64_t*)p = v;
-}
-template <bool COH> __device__ inline f32x4 ld_f32x4(const float* p) {
-    if constexpr (COH) {
-        const f32x2 lo = __builtin_bit_cast(f32x2, ld_u64<true>(p));
-        const f32x2 hi = __builtin_bit_cast(f32x2, ld_u64<true>(p + 2));
-        return f32x4{lo[0], lo[1], hi[0], hi[1]};
-    } else {
-        return *(const f32x4*)p;
-    }
-}
-template <bool COH> __device__ inline void st_f32x4(float* p, f32x4 v) {
-    if constexpr (COH) {
-        st_u64<true>(p, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}));
-        st_u64<true>(p + 2, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}));
-    } else {
-        *(f32x4*)p = v;
-    }
+template <int AUX> __device__ inline f32x4 bload_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, AUX));
 }
 
 // 4 consecutive state elements in the state dtype, widened to / rounded from fp32.
-template <bool COH> __device__ inline f32x4 load_state4(const void* base, int dtype, size_t off) {
-    if (dtype == DT_F32) return ld_f32x4<COH>((const float*)base + off);
-    const uint64_t bits = ld_u64<COH>((const uint16_t*)base + off);
+__device__ inline f32x4 load_state4(const void* base, int dtype, size_t off) {
+    if (dtype == DT_F32) return *((const f32x4*)((const float*)base + off));
+    const uint64_t bits = *(const uint64_t*)((const uint16_t*)base + off);
     if (dtype == DT_F16) {
         const f16x4 v = __builtin_bit_cast(f16x4, bits);
         return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
@@ -200,27 +192,26 @@ template <bool COH> __device__ inline f32x4 load_state4(const void* base, int dt
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
-template <bool COH> __device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) {
+__device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) {
     if (dtype == DT_F32) {
-        st_f32x4<COH>((float*)base + off, v);
+        *(f32x4*)((float*)base + off) = v;
     } else if (dtype == DT_F16) {
-        st_u64<COH>((uint16_t*)base + off,
-                    __builtin_bit_cast(uint64_t, f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]}));
+        *(f16x4*)((uint16_t*)base + off) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
     } else {
-        st_u64<COH>((uint16_t*)base + off,
-                    __builtin_bit_cast(uint64_t, bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]}));
+        *(bf16x4*)((uint16_t*)base + off) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     }
 }
 
 // ---- cross-workgroup waits -------------------------------------------------------------
-// Poll a flag word until it is non-zero.  Bounded: after spin_limit polls (or once any
-// wait has given up) it raises the abort word and the status word and returns false, so
-// every workgroup still runs to completion.  All lanes of the calling wave(s) poll the
-// same address.  Data published before the flag is then read with COH = true accesses.
+// Poll a flag word (sc1 loads, from the L2) until it is non-zero.  Bounded: after spin_limit polls (or
+// once any wait has given up) it raises the abort word and the status word -- device-scope
+// accesses, since every partition must see them -- and returns false, so every workgroup
+// still runs to completion.  All lanes of the calling wave poll the same address.
 __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(f, 4);
     uint32_t spins = 0;
     bool ok = true;
-    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    while (__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, AUX_L2) == 0u) {
         ++spins;
         if ((spins & 31u) == 0u) {
             if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
@@ -245,28 +236,19 @@ __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a) {
 // s_waitcnt vmcnt(0): every global load and store this wave issued has completed.
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Every lane: its device-scope stores have completed, then set *f.
+__device__ inline void raise_flag(uint32_t* f) { __builtin_amdgcn_raw_buffer_store_b32(1u, make_rsrc(f, 4), 0, 0, 0); }
+
+// Every lane: its stores have reached the L2, then set *f.
 __device__ inline void publish_flag_wave(uint32_t* f) {
     wait_vm_all();
-    __hip_atomic_store(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    raise_flag(f);
 }
 
-// Whole workgroup: every wave's device-scope stores have completed, then thread 0 sets *f.
+// Whole workgroup: every wave's stores have reached the L2, then thread 0 sets *f.
 __device__ inline void publish_flag_block(uint32_t* f) {
     wait_vm_all();
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Buffer resource for [base, base + bytes); every caller passes wave-uniform values, which are
-// made scalar explicitly so the descriptor lives in SGPRs (a descriptor the compiler cannot
-// prove uniform is re-built per lane in a loop around every access).
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    void* p = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(p, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+    if (threadIdx.x == 0) raise_flag(f);
 }
 
 // ---- the fused form's inter-chunk state ring -----------------------------------------------
@@ -280,17 +262,17 @@ __device__ inline size_t ring_chain(int b, int slot, int h, int ph, int K, int H
     return ((((size_t)b * K + slot) * H + h) * WPH + ph) * (size_t)tiles * 256;
 }
 
-// Device-coherent (sc1) load / store of one lane's 4 ring elements at element offset `off`
-// of the chain whose descriptor is `r` (ring_rsrc).
+// Load (sc1: from the XCD's L2) / plain store of one lane's 4 ring elements at element offset
+// `off` of the chain whose descriptor is `r` (ring_rsrc).
 __device__ inline __amdgpu_buffer_rsrc_t ring_rsrc(const void* states, int dtype, size_t chain, int tiles) {
     const int es = dtype == DT_F32 ? 4 : 2;
     return make_rsrc((const char*)states + chain * es, tiles * 256 * es);
 }
 
 __device__ inline f32x4 ring_load(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t off) {
-    if (dtype == DT_F32) return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 4, 0, 16));
+    if (dtype == DT_F32) return bload_f32x4<AUX_L2>(r, off * 4);
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off * 2, 0, 16);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off * 2, 0, AUX_L2);
     if (dtype == DT_F16) {
         const f16x4 v = __builtin_bit_cast(f16x4, w);
         return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
@@ -303,26 +285,27 @@ __device__ inline void ring_store(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t 
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     if (dtype == DT_F32) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off * 4, 0, 16);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off * 4, 0, 0);
     } else if (dtype == DT_F16) {
         const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off * 2, 0, 16);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off * 2, 0, 0);
     } else {
         const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off * 2, 0, 16);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off * 2, 0, 0);
     }
 }
 
 // ---- step 1: chunk_cumsum ([KF] item 4; [HW] segsum section: decay in log space) ------
-// For one (b, c): dt = softplus(dt_raw + dt_bias) (0 past L) and the inclusive in-chunk
-// running sum of dt * A, both fp32.  One wave per head; each lane owns Q/64 consecutive
-// tokens, then a wave-wide exclusive scan of the lane totals.
-template <typename T, bool COH> __device__ void cumsum_tile(const SsdArgs& a, int b, int c) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// For one (b, c) and heads [h0, h1): dt = softplus(dt_raw + dt_bias) (0 past L) and the
+// inclusive in-chunk running sum of dt * A, both fp32, into dtf / acs [B][nc][H][Q].  One
+// wave per head; each lane owns Q/64 consecutive tokens, then a wave-wide exclusive scan of
+// the lane totals.
+template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c, int h0, int h1) {
+    const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int Q = a.chunk, L = a.seqlen, H = a.nheads, nc = a.nchunks;
     const int V = Q >> 6;  // 1..4
     const T* dtr = (const T*)a.dt;
-    for (int h = wave; h < H; h += 4) {
+    for (int h = h0 + wave; h < h1; h += 4) {
         const float bias = a.dt_bias ? a.dt_bias[h] : 0.f;
         const float Ah = a.A[h];
         float d[4], run[4];
@@ -351,27 +334,26 @@ template <typename T, bool COH> __device__ void cumsum_tile(const SsdArgs& a, in
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (k < V) {
-                st_f32<COH>(a.dtf + base + k, d[k]);
-                st_f32<COH>(a.acs + base + k, excl + run[k]);
+                a.dtf[base + k] = d[k];
+                a.acs[base + k] = excl + run[k];
             }
     }
 }
 
 // ---- step 2: bmm ([KF] item 7) ---------------------------------------------------------
-// CB[i][j] = sum_n C_i[n] B_j[n] for one (b, c, g), computed as CB^T blocks (rows j,
-// columns i) so each lane stores 4 consecutive j of one row i.  Only blocks with
-// i-block >= j-block are formed: the scan step reads j <= i only.  Fragments come
-// straight from global memory (rows are n-contiguous).
-template <typename T, int N, bool COH> __device__ void bmm_tile(const SsdArgs& a, int b, int c, int g) {
+// CB[i][j] = sum_n C_i[n] B_j[n] for one (b, c, g) into cbase[Q][Q], computed as CB^T blocks
+// (rows j, columns i) so each lane stores 4 consecutive j of one row i.  Only blocks with
+// i-block >= j-block are formed: the scan step reads j <= i only.  Fragments come straight
+// from global memory (rows are n-contiguous).
+template <typename T, int N> __device__ void bmm_tile(const SsdArgs& a, int b, int c, int g, float* cbase) {
     constexpr int KPL = TT<T>::KPL, KI = 4 * KPL;
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, r16 = lane & 15;
-    const int Q = a.chunk, L = a.seqlen, G = a.ngroups, nc = a.nchunks;
+    const int Q = a.chunk, L = a.seqlen, G = a.ngroups;
     const int QB = Q >> 4;
     const T* Bp = (const T*)a.B;
     const T* Cp = (const T*)a.C;
     typedef typename TT<T>::frag frag;
-    float* cbase = a.cb + (((size_t)b * nc + c) * G + g) * (size_t)Q * Q;
     for (int jb = wave; jb < QB; jb += 4) {
         const int tj = c * Q + jb * 16 + r16;
         frag af[N / KI];
@@ -388,7 +370,7 @@ template <typename T, int N, bool COH> __device__ void bmm_tile(const SsdArgs& a
                                        : vzero<frag>();
                 acc = TT<T>::mma(af[ks], bf, acc);
             }
-            st_f32x4<COH>(cbase + (size_t)(ib * 16 + r16) * Q + jb * 16 + 4 * q, acc);
+            *(f32x4*)(cbase + (size_t)(ib * 16 + r16) * Q + jb * 16 + 4 * q) = acc;
         }
     }
 }
@@ -463,7 +445,7 @@ enum : int { MODE_STATE = 0, MODE_SCAN = 1, MODE_FUSED = 2 };
 //             [KF] "高效内核融合技术揭秘"): wait for S_c, write S_{c+1} = exp(acs[Q-1]) S_c
 //             + s_c to the next ring slot and release it, then chunk_scan with S_c.
 template <typename T, int P, int N, int MODE>
-__device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char* smem) {
+__device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbase) {
     typedef Geo<T, P, N> G_;
     constexpr int W = G_::W, PW = G_::PW, WPH = G_::WPH, HPT = G_::HPT, MBP = G_::MBP;
     constexpr int NB = G_::NB, WB = G_::WB, KPL = G_::KPL, KI = G_::KI, LDW = G_::LDW, LDN = G_::LDN;
@@ -471,8 +453,8 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
     typedef typename TT<T>::frag frag;
     typedef typename TT<T>::v4 v4;
 
-    constexpr bool COH = MODE == MODE_FUSED;  // data handed over inside one launch
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int AUX = MODE == MODE_FUSED ? AUX_L2 : 0;  // data handed over inside one launch
+    const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, r16 = lane & 15;
     const int hs = wave / WPH, ph = wave % WPH;
     const int Q = a.chunk, L = a.seqlen, H = a.nheads, Gn = a.ngroups, nc = a.nchunks, hpg = a.hpg;
@@ -488,12 +470,17 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
     float* sAcs = sDt + HPT * QMAX;             // [HPT][QMAX]
     float* sW = sAcs + HPT * QMAX;              // [HPT][QMAX] chunk-state weights
 
-    for (int e = tid; e < HPT * Q; e += 256) {
-        const int hh = e / Q, i = e - hh * Q;
-        const bool ok = (tig * HPT + hh) < hpg;
-        const size_t off = (((size_t)b * nc + c) * H + head0 + hh) * Q + i;
-        sDt[hh * QMAX + i] = ok ? ld_f32<COH>(a.dtf + off) : 0.f;
-        sAcs[hh * QMAX + i] = ok ? ld_f32<COH>(a.acs + off) : 0.f;
+    {
+        // heads of the tile past the group read as zeros
+        const int nvh = hpg - tig * HPT < HPT ? hpg - tig * HPT : HPT;
+        const size_t off = (((size_t)b * nc + c) * H + head0) * Q;
+        const __amdgpu_buffer_rsrc_t rdt = make_rsrc(a.dtf + off, (uint32_t)(nvh * Q * 4));
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.acs + off, (uint32_t)(nvh * Q * 4));
+        for (int e = tid; e < HPT * Q; e += 256) {
+            const int hh = e / Q, i = e - hh * Q;
+            sDt[hh * QMAX + i] = bload_f32<AUX>(rdt, (uint32_t)e * 4);
+            sAcs[hh * QMAX + i] = bload_f32<AUX>(ra, (uint32_t)e * 4);
+        }
     }
     __syncthreads();
     for (int e = tid; e < HPT * Q; e += 256) {
@@ -582,8 +569,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
 #pragma unroll
                 for (int pb = 0; pb < MBP; ++pb) {
                     const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
-                    sc[nb][pb] = load_state4<false>(a.states, a.state_dtype,
-                                                    ((((size_t)b * K + slot) * H + h) * P + p) * N + n);
+                    sc[nb][pb] = load_state4(a.states, a.state_dtype, ((((size_t)b * K + slot) * H + h) * P + p) * N + n);
                 }
         }
     }
@@ -594,7 +580,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
         T* sL = (T*)(smem + G_::SZ_C);
         T* sXT = (T*)(smem + G_::SZ_C + G_::SZ_L);
         const float Dh = (a.D && hvalid) ? a.D[h] : 0.f;
-        const float* cbase = a.cb + (((size_t)b * nc + c) * Gn + g) * (size_t)Q * Q;
+        const __amdgpu_buffer_rsrc_t rcb = make_rsrc(cbase, (uint32_t)(Q * Q * 4));
         for (int i0 = 0; i0 < Q; i0 += W) {
             __syncthreads();
             stage_rows<T, N, W, LDN>(sC, Cg + ((size_t)b * L * Gn + g) * N, (size_t)Gn * N, tok0 + i0, L);
@@ -660,7 +646,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                 for (int it = tid; it < W * (W / 4); it += 256) {
                     const int jq = it % (W / 4), ii = it / (W / 4);
                     const int i = i0 + ii, j = j0 + 4 * jq;
-                    const f32x4 cbv = ld_f32x4<COH>(cbase + (size_t)i * Q + j);
+                    const f32x4 cbv = bload_f32x4<AUX>(rcb, (uint32_t)(i * Q + j) * 4);
 #pragma unroll
                     for (int hh = 0; hh < HPT; ++hh) {
                         const float ai = sAcs[hh * QMAX + i];

@@ -11,14 +11,18 @@ namespace ssd {
 // ---- unfused form: one kernel per step -------------------------------------------------
 template <typename T> __global__ __launch_bounds__(256) void k_chunk_cumsum(SsdArgs a) {
     const int c = blockIdx.x % a.nchunks, b = blockIdx.x / a.nchunks;
-    cumsum_tile<T, false>(a, b, c);
+    cumsum_tile<T>(a, b, c, 0, a.nheads);
+}
+
+__device__ inline float* cb_global(const SsdArgs& a, int b, int c, int g) {
+    return a.cb + (((size_t)b * a.nchunks + c) * a.ngroups + g) * (size_t)a.chunk * a.chunk;
 }
 
 template <typename T, int N> __global__ __launch_bounds__(256) void k_bmm(SsdArgs a) {
     const int g = blockIdx.x % a.ngroups;
     const int c = (blockIdx.x / a.ngroups) % a.nchunks;
     const int b = blockIdx.x / (a.ngroups * a.nchunks);
-    bmm_tile<T, N, false>(a, b, c, g);
+    bmm_tile<T, N>(a, b, c, g, cb_global(a, b, c, g));
 }
 
 // blockIdx.x -> (b, c, g, tile-in-group)
@@ -31,49 +35,9 @@ template <typename T, int P, int N, int MODE> __global__ __launch_bounds__(256) 
     r /= a.ngroups;
     const int c = r % a.nchunks;
     const int b = r / a.nchunks;
-    chunk_tile<T, P, N, MODE>(a, b, c, g, tig, smem);
+    chunk_tile<T, P, N, MODE>(a, b, c, g, tig, smem, cb_global(a, b, c, g));
 }
 
-// ---- fused form: a single launch ([KF] "高效内核融合技术揭秘") ------------------------------
-// Each workgroup takes one ticket.  Tickets [0, T_cs) are cumsum tiles (b, c) in chunk
-// order, [T_cs, T_cs + T_bmm) are bmm tiles (b, c, g) in chunk order, the rest are chunk
-// tiles (c, b, g, tile-in-group) in chunk-major order.  A chunk tile waits only on work
-// with smaller tickets (its cumsum and bmm tiles and the previous chunk's tile of its
-// chains), all of which were claimed by running workgroups, so the waits always end.
-template <typename T, int P, int N> __global__ __launch_bounds__(256) void k_fused(SsdArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[Geo<T, P, N>::SMEM];
-    __shared__ uint32_t s_ticket;
-    if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
-    __syncthreads();
-    const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);  // uniform: keeps tile math scalar
-    const uint32_t Bn = a.batch, nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
-    const uint32_t t_cs = Bn * nc, t_bmm = Bn * nc * Gn;
-    if (t >= t_cs + t_bmm + Bn * nc * Gn * tpg) return;  // only if the ticket word was not reset
-    if (t < t_cs) {
-        const int c = t / Bn, b = t % Bn;
-        cumsum_tile<T, true>(a, b, c);
-        publish_flag_block(a.cs_done + (size_t)b * nc + c);
-    } else if (t < t_cs + t_bmm) {
-        const uint32_t u = t - t_cs;
-        const int c = u / (Bn * Gn), b = (u / Gn) % Bn, g = u % Gn;
-        bmm_tile<T, N, true>(a, b, c, g);
-        publish_flag_block(a.bmm_done + ((size_t)b * nc + c) * Gn + g);
-    } else {
-        const uint32_t u = t - t_cs - t_bmm;
-        const uint32_t per_chunk = Bn * Gn * tpg;
-        const int c = u / per_chunk;
-        const uint32_t rem = u % per_chunk;
-        const int b = rem / (Gn * tpg), g = (rem / tpg) % Gn, tig = rem % tpg;
-        if (threadIdx.x == 0) {
-            wait_flag(a.cs_done + (size_t)b * nc + c, a);
-            wait_flag(a.bmm_done + ((size_t)b * nc + c) * Gn + g, a);
-        }
-        __syncthreads();
-        chunk_tile<T, P, N, MODE_FUSED>(a, b, c, g, tig, smem);
-    }
-}
-
-// ---- 16-bit inputs: chunk tiles with the chunk size fixed at compile time ------------------
 template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds__(256) void k_chunk16(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
     int r = blockIdx.x;
@@ -83,46 +47,150 @@ template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds_
     r /= a.ngroups;
     const int c = r % a.nchunks;
     const int b = r / a.nchunks;
-    chunk_tile16<T, P, N, Q, MODE>(a, b, c, g, tig, smem);
+    chunk_tile16<T, P, N, Q, MODE>(a, b, c, g, tig, smem, cb_global(a, b, c, g));
+}
+
+// ---- fused form: a single launch ([KF] "高效内核融合技术揭秘") ------------------------------
+// The chains u = (b, g, tile-in-group) are split into contiguous partitions, one per XCD.
+// Partition x owns the chunk tiles (u, c) of its chains and its own copy of the cumsum and
+// bmm work those tiles read: cumsum tiles (pair, c) over the heads of its chains in pair
+// (b, g), and bmm tiles (pair, c) into its own CB slots.  Its queue, in claim order:
+//   [0, np*nc)             cumsum tiles, chunk-major
+//   [np*nc, 2*np*nc)       bmm tiles, chunk-major
+//   [2*np*nc, +nu*nc)      chunk tiles (c, u), chunk-major
+// Workgroups are persistent: each reads the id of the XCD it runs on, takes tickets from that
+// partition's queue until it is empty, then leaves.  So every hand-off of a partition stays in
+// one L2 (see the coherence notes in ssd_device.h).  A chunk tile waits only on work with
+// smaller tickets of its own queue (its cumsum and bmm tiles and the previous chunk's tile of
+// its chains), claimed by workgroups that are running, so every wait ends.
+struct FusedPart {
+    int u0, nu, p0, np, pb;
+    uint32_t n_cs, n_total;
+};
+
+__device__ inline FusedPart fused_part(const SsdArgs& a, int x) {
+    FusedPart f;
+    f.u0 = a.part_u0[x];
+    f.nu = a.part_u0[x + 1] - f.u0;
+    f.p0 = f.u0 / a.tpg;
+    f.np = f.nu > 0 ? (f.u0 + f.nu - 1) / a.tpg - f.p0 + 1 : 0;
+    f.pb = a.part_pb[x];
+    f.n_cs = (uint32_t)f.np * a.nchunks;
+    f.n_total = 2 * f.n_cs + (uint32_t)f.nu * a.nchunks;
+    return f;
+}
+
+// hardware id of the XCD this wave runs on (HW_REG_XCC_ID, bits [3:0])
+__device__ inline uint32_t xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20); }
+
+// The argument block seen through an offset the compiler cannot fold: reading it again on
+// every trip of the work loop costs a few scalar loads, while letting the compiler hoist the
+// tile code's many argument loads out of the loop keeps them live across the whole tile and
+// spills registers.
+__device__ inline const SsdArgs& fresh_args(const SsdArgs& a) {
+    int zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    return *(const SsdArgs*)((const char*)&a + zero);
+}
+
+// chunk(args, b, c, g, tig, cb) runs one chunk tile after its cumsum and bmm tiles are done.
+template <int HPT, typename T, int N, typename ChunkFn>
+__device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
+    __shared__ uint32_t s_word;
+    const uint32_t raw = xcc_id();
+    const int x = (int)(raw % (uint32_t)a0.nparts);
+    const SsdArgs& a = a0;
+    // The first workgroup to reach partition x records its XCD; a workgroup from another XCD
+    // whose id maps to the same partition leaves it alone (its hand-offs would cross L2s).
+    if (threadIdx.x == 0) {
+        const uint32_t prev = atomicCAS(a.owner + x, 0u, raw + 1);
+        s_word = (prev == 0u || prev == raw + 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool mine = __builtin_amdgcn_readfirstlane(s_word) != 0u;
+    while (mine) {
+        __syncthreads();  // the previous tile is done with LDS and s_word
+        const SsdArgs& a = fresh_args(a0);
+        if (threadIdx.x == 0) s_word = atomicAdd(a.ticket + x * kTicketStride, 1u);
+        __syncthreads();
+        const uint32_t t = __builtin_amdgcn_readfirstlane(s_word);
+        const FusedPart f = fused_part(a, x);
+        const int nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg, hpg = a.hpg, Q = a.chunk;
+        if (t >= f.n_total) break;
+        if (t < 2 * f.n_cs) {
+            const uint32_t v = t < f.n_cs ? t : t - f.n_cs;
+            const int c = v / f.np, lp = v % f.np;
+            const int pair = f.p0 + lp, b = pair / Gn, g = pair % Gn;
+            const size_t slot = (size_t)(f.pb + lp) * nc + c;
+            if (t < f.n_cs) {
+                // heads of this pair that belong to the partition's chains
+                const int lo = (f.u0 > pair * tpg ? f.u0 - pair * tpg : 0) * HPT;
+                const int hi_u = f.u0 + f.nu < (pair + 1) * tpg ? f.u0 + f.nu - pair * tpg : tpg;
+                const int hi = hi_u * HPT < hpg ? hi_u * HPT : hpg;
+                cumsum_tile<T>(a, b, c, g * hpg + lo, g * hpg + hi);
+                publish_flag_block(a.cs_done + slot);
+            } else {
+                bmm_tile<T, N>(a, b, c, g, a.cb + slot * Q * Q);
+                publish_flag_block(a.bmm_done + slot);
+            }
+        } else {
+            const uint32_t v = t - 2 * f.n_cs;
+            const int c = v / f.nu;
+            const int u = f.u0 + (int)(v % f.nu);
+            const int pair = u / tpg, tig = u % tpg, b = pair / Gn, g = pair % Gn;
+            const size_t slot = (size_t)(f.pb + pair - f.p0) * nc + c;
+            if (threadIdx.x == 0) {
+                wait_flag(a.cs_done + slot, a);
+                wait_flag(a.bmm_done + slot, a);
+            }
+            __syncthreads();
+            chunk(a, b, c, g, tig, a.cb + slot * Q * Q);
+        }
+    }
+    // The last workgroup to leave checks that every partition's queue was emptied (a
+    // partition no workgroup served would leave its outputs unwritten).
+    __syncthreads();
+    if (threadIdx.x == 0 && atomicAdd(a.exit_count, 1u) == gridDim.x - 1) {
+        for (int y = 0; y < a.nparts; ++y) {
+            const uint32_t claimed = __hip_atomic_load(a.ticket + y * kTicketStride, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (claimed < fused_part(a, y).n_total)
+                __hip_atomic_store(a.status, 9u /* SSD_ERR_SCHEDULE */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <typename T, int P, int N> __global__ __launch_bounds__(256) void k_fused(SsdArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[Geo<T, P, N>::SMEM];
+    fused_loop<Geo<T, P, N>::HPT, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig, const float* cbp) {
+        chunk_tile<T, P, N, MODE_FUSED>(ai, b, c, g, tig, smem, cbp);
+    });
 }
 
 template <typename T, int P, int N, int Q> __global__ __launch_bounds__(256, 2) void k_fused16(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
-    __shared__ uint32_t s_ticket;
-    if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
-    __syncthreads();
-    const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);  // uniform: keeps tile math scalar
-    const uint32_t Bn = a.batch, nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
-    const uint32_t t_cs = Bn * nc, t_bmm = Bn * nc * Gn;
-    if (t >= t_cs + t_bmm + Bn * nc * Gn * tpg) return;  // only if the ticket word was not reset
-    if (t < t_cs) {
-        const int c = t / Bn, b = t % Bn;
-        cumsum_tile<T, true>(a, b, c);
-        publish_flag_block(a.cs_done + (size_t)b * nc + c);
-    } else if (t < t_cs + t_bmm) {
-        const uint32_t u = t - t_cs;
-        const int c = u / (Bn * Gn), b = (u / Gn) % Bn, g = u % Gn;
-        bmm_tile<T, N, true>(a, b, c, g);
-        publish_flag_block(a.bmm_done + ((size_t)b * nc + c) * Gn + g);
-    } else {
-        const uint32_t u = t - t_cs - t_bmm;
-        const uint32_t per_chunk = Bn * Gn * tpg;
-        const int c = u / per_chunk;
-        const uint32_t rem = u % per_chunk;
-        const int b = rem / (Gn * tpg), g = (rem / tpg) % Gn, tig = rem % tpg;
-        if (threadIdx.x == 0) {
-            wait_flag(a.cs_done + (size_t)b * nc + c, a);
-            wait_flag(a.bmm_done + ((size_t)b * nc + c) * Gn + g, a);
-        }
-        __syncthreads();
-        chunk_tile16<T, P, N, Q, MODE_FUSED>(a, b, c, g, tig, smem);
-    }
+    fused_loop<Geo16<T, P, N, Q>::HPT, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig, const float* cbp) {
+        chunk_tile16<T, P, N, Q, MODE_FUSED>(ai, b, c, g, tig, smem, cbp);
+    });
 }
 
 // ---- host launchers ----------------------------------------------------------------------
 inline hipError_t launch(const void* fn, unsigned grid, void* arg0, hipStream_t st) {
     void* args[] = {arg0};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st);
+}
+
+// Persistent fused launch: as many workgroups per partition as fit on its XCD at once (and no
+// more than its queue holds).  Workgroups are dealt to XCDs round robin, so partition x's
+// share arrives on one XCD; fused_loop does not rely on that for correctness.
+inline hipError_t launch_fused(const void* fn, SsdArgs& a, hipStream_t st) {
+    int occ = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 256, 0);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    const int per_xcd = (a.cu_count / a.nparts > 0 ? a.cu_count / a.nparts : 1) * occ;
+    const int wgs = per_xcd < a.part_max_work ? per_xcd : a.part_max_work;
+    return launch(fn, (unsigned)(a.nparts * (wgs > 0 ? wgs : 1)), &a, st);
 }
 
 template <typename T, int P, int N> hipError_t launch_step_t(int step, SsdArgs& a, hipStream_t st) {
@@ -140,7 +208,7 @@ template <typename T, int P, int N> hipError_t launch_step_t(int step, SsdArgs& 
     case STEP_CHUNK_SCAN:
         return launch((const void*)&k_chunk<T, P, N, MODE_SCAN>, Bn * nc * Gn * tpg, &a, st);
     case STEP_FUSED:
-        return launch((const void*)&k_fused<T, P, N>, Bn * nc + Bn * nc * Gn + Bn * nc * Gn * tpg, &a, st);
+        return launch_fused((const void*)&k_fused<T, P, N>, a, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -161,7 +229,7 @@ template <typename T, int P, int N, int Q> hipError_t launch_step16(int step, Ss
     case STEP_CHUNK_SCAN:
         return launch((const void*)&k_chunk16<T, P, N, Q, MODE_SCAN>, Bn * nc * Gn * tpg, &a, st);
     case STEP_FUSED:
-        return launch((const void*)&k_fused16<T, P, N, Q>, Bn * nc + Bn * nc * Gn + Bn * nc * Gn * tpg, &a, st);
+        return launch_fused((const void*)&k_fused16<T, P, N, Q>, a, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -8,6 +8,9 @@
 
 namespace ssd {
 
+// Largest number of XCDs (L2 domains) the fused form partitions its work over.
+constexpr int kMaxXcc = 8;
+
 // Kernel argument block (passed by value).  Layouts are described in mamba_ssd.h.
 struct SsdArgs {
     const void* x;
@@ -20,19 +23,32 @@ struct SsdArgs {
     void* y;
     float* dtf;          // [B][nc][H][Q]
     float* acs;          // [B][nc][H][Q]
-    float* cb;           // [B][nc][G][Q][Q]
+    float* cb;           // unfused: [B][nc][G][Q][Q]; fused: [pair slot][nc][Q][Q]
     float* s;            // [B][nc][H][P][N] (unfused form)
-    void* states;        // [B][K][H][P][N] in the state dtype
+    void* states;        // unfused: [B][K][H][P][N]; fused: one ring slot per chain
     uint32_t* flags;     // [B][H][WPH][nc + 1]
-    uint32_t* cs_done;   // [B][nc]
-    uint32_t* bmm_done;  // [B][nc][G]
-    uint32_t* ticket;
+    uint32_t* cs_done;   // fused: [pair slot][nc]
+    uint32_t* bmm_done;  // fused: [pair slot][nc]
+    uint32_t* ticket;    // fused: one work counter per partition, kTicketStride words apart
+    uint32_t* owner;     // fused: [kMaxXcc] hardware XCC id (+1) that serves each partition
+    uint32_t* exit_count;
     uint32_t* abort_word;
     uint32_t* status;
     int batch, seqlen, nheads, ngroups, chunk, nchunks, hpg, tpg, slots;
     int state_dtype, softplus;
     uint32_t spin_limit;
+    // fused form: the chains (b, g, tile-in-group), numbered u = (b * G + g) * tpg + tig, are
+    // split into nparts contiguous ranges [part_u0[x], part_u0[x + 1]); partition x runs on
+    // the XCD whose id is x modulo nparts.  Its (b, g) pairs use cb / flag slots starting at
+    // part_pb[x].
+    int nparts;
+    int part_u0[kMaxXcc + 1];
+    int part_pb[kMaxXcc + 1];
+    int part_max_work;  // host only: the longest partition queue
+    int cu_count;       // host only: compute units of the device
 };
+
+constexpr int kTicketStride = 32;  // one 128-byte line per partition counter
 
 enum : int {
     STEP_CUMSUM = 0,

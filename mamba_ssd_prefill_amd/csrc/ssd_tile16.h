@@ -81,7 +81,7 @@ template <int COLS, int KIND = SWZ_TR>
 __device__ inline void dma_rows(void* lds_tile, __amdgpu_buffer_rsrc_t rs_src, int rows, uint32_t rs) {
     constexpr int CH = COLS / 8;
     constexpr int RPI = 64 / CH;  // rows per 1 KB instruction
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ninst = rows / RPI;
     for (int k = wave; k < ninst; k += 4) {
         const int row = k * RPI + lane / CH;
@@ -98,7 +98,7 @@ __device__ inline void dma_rows(void* lds_tile, __amdgpu_buffer_rsrc_t rs_src, i
 // depend on k0 (a multiple of 32) nor on the +4, so the lane offset for k0 = 0 is computed once
 // per column block and each k step is a constant offset.
 template <int COLS> __device__ inline int tr_lane_off(int col0) {
-    const int lane = threadIdx.x & 63;
+    const int lane = tid_here() & 63;
     const int q = lane >> 4, m = (lane & 15) >> 2, jj = lane & 3;
     return sw_off<COLS>(8 * q + m, col0 + 4 * jj);
 }
@@ -117,10 +117,10 @@ template <typename T> __device__ inline typename TT<T>::frag pack8(f32x4 lo, f32
 }
 
 // Copy the CB rows/columns the diagonal block reads (bands of the lower triangle, see
-// Geo16) from HBM into LDS.  aux = 16 makes the copy device-coherent (CB written by another
-// workgroup of the same launch).
+// Geo16) from HBM into LDS.  AUX = AUX_L2 when CB was written by another workgroup of the
+// same launch (on the same XCD).
 template <int Q, int AUX> __device__ inline void dma_cb_bands(float* lds, const float* cb) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(cb, (uint32_t)(Q * Q * 4));
     int base = 0;  // pieces
 #pragma unroll
@@ -150,17 +150,17 @@ template <int Q> __device__ inline int cb_off(int i, int j) {
 }
 
 template <typename T, int P, int N, int Q, int MODE>
-__device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, char* smem) {
+__device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbp) {
     typedef Geo16<T, P, N, Q> G_;
     constexpr int PW = G_::PW, WPH = G_::WPH, HPT = G_::HPT, MBP = G_::MBP, NB = G_::NB, KS = G_::KS,
                   QB = G_::QB;
-    constexpr bool COH = MODE == MODE_FUSED;
-    constexpr int CB_AUX = COH ? 16 : 0;  // sc1 (device-coherent) reads of CB inside one launch
+    constexpr int AUX = MODE == MODE_FUSED ? AUX_L2 : 0;  // dt/acs and CB written inside one launch
+    constexpr int CB_AUX = AUX;
     constexpr bool CB_LDS = G_::CB_LDS;
     typedef typename TT<T>::frag frag;
     typedef typename TT<T>::v4 v4;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, r16 = lane & 15;
     const int hs = wave / WPH, ph = wave % WPH;
     const int L = a.seqlen, H = a.nheads, Gn = a.ngroups, nc = a.nchunks, hpg = a.hpg;
@@ -181,7 +181,6 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     float* sF = sW;
     float* sE = sDt;
 
-    const float* cbp = a.cb + (((size_t)b * nc + c) * Gn + g) * (size_t)Q * Q;
     const uint32_t xrs = (uint32_t)H * P * 2, bcrs = (uint32_t)Gn * N * 2;
     const uint32_t bc_bytes = (uint32_t)(valid - 1) * bcrs + N * 2;
     const size_t bc_off = (((size_t)b * L + tok0) * Gn + g) * N;
@@ -197,12 +196,16 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         dma_rows<N, SWZ_TR>(sBC, make_rsrc((const T*)a.B + bc_off, bc_bytes), Q, bcrs);
     else
         dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
-    for (int e = tid; e < HPT * Q; e += 256) {
-        const int hh = e / Q, i = e - hh * Q;
-        const bool ok = (tig * HPT + hh) < hpg;
-        const size_t off = (((size_t)b * nc + c) * H + head0 + hh) * Q + i;
-        sDt[e] = ok ? ld_f32<COH>(a.dtf + off) : 0.f;
-        sA2[e] = ok ? ld_f32<COH>(a.acs + off) * LOG2E : 0.f;
+    {
+        // heads of the tile past the group read as zeros
+        const int nvh = hpg - tig * HPT < HPT ? hpg - tig * HPT : HPT;
+        const size_t off = (((size_t)b * nc + c) * H + head0) * Q;
+        const __amdgpu_buffer_rsrc_t rdt = make_rsrc(a.dtf + off, (uint32_t)(nvh * Q * 4));
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.acs + off, (uint32_t)(nvh * Q * 4));
+        for (int e = tid; e < HPT * Q; e += 256) {
+            sDt[e] = bload_f32<AUX>(rdt, (uint32_t)e * 4);
+            sA2[e] = bload_f32<AUX>(ra, (uint32_t)e * 4) * LOG2E;
+        }
     }
     __syncthreads();
     for (int e = tid; e < HPT * Q; e += 256) {
@@ -310,8 +313,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
 #pragma unroll
                 for (int pb = 0; pb < MBP; ++pb) {
                     const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
-                    scb[nb][pb] = cvt4<T>(load_state4<false>(a.states, a.state_dtype,
-                                                             ((((size_t)b * K + slot) * H + h) * P + p) * N + n));
+                    scb[nb][pb] = cvt4<T>(load_state4(a.states, a.state_dtype, ((((size_t)b * K + slot) * H + h) * P + p) * N + n));
                 }
         }
         wait_vm_all();
@@ -372,7 +374,6 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         // HBM/L2 two row blocks ahead of its use; rows past the sequence read as zeros
         const __amdgpu_buffer_rsrc_t xr =
             make_rsrc((const T*)a.x + (((size_t)b * L + tok0) * H + h) * P, (uint32_t)(valid - 1) * xrs + P * 2);
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         auto xd_load = [&](int ib, int pb) -> v4 {
             const uint32_t off = (uint32_t)(ib * 16 + r16) * xrs + (uint32_t)(ph * PW + pb * 16 + 4 * q) * 2;
             return __builtin_bit_cast(v4, __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0));

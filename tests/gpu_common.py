@@ -23,12 +23,25 @@ def say(*a):
     sys.stdout.flush()
 
 
+_STATE_CODE = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
 def run_gpu(inp, chunk_size, impl, state_dtype=None, dev="cuda:0"):
+    """One ssd_prefill on the GPU; also requires the device status word to read SSD_OK."""
     g = inp.to(dev)
+    if state_dtype is None:
+        state_dtype = g.h0.dtype if g.h0 is not None else torch.float32
+    Bt, L, H, P = g.x.shape
+    G, N = g.B.shape[2], g.B.shape[3]
+    prm = ssd.make_params(Bt, L, H, P, N, G, chunk_size, DT_NAME[g.x.dtype], _STATE_CODE[state_dtype],
+                          inp.dt_softplus, impl)
+    ws = ssd.alloc_workspace(prm, g.x.device)
     y, fin = ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=chunk_size,
                              impl=impl, dt_softplus=inp.dt_softplus,
-                             state_dtype=state_dtype)
+                             state_dtype=state_dtype, workspace=ws)
     torch.cuda.synchronize()
+    status = ssd.check_device_status(prm, ws)
+    assert status == 0, "device status %d after %s Q=%d" % (status, impl, chunk_size)
     return y, fin
 
 

@@ -16,7 +16,7 @@ import mamba_ssd_prefill_amd as ssd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mamba_ssd.h")
 
-OK, NULLP, SHAPE, UNSUP, MISAL, WS_SMALL, HIP, TIMEOUT, BADARG = range(9)
+OK, NULLP, SHAPE, UNSUP, MISAL, WS_SMALL, HIP, TIMEOUT, BADARG, SCHEDULE = range(10)
 
 
 def header_functions():
@@ -53,7 +53,7 @@ def test_abi_struct_sizes_match_header():
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.ssd_status_string(code)
         assert s and len(s) > 3
     assert lib.ssd_status_string(1234) == b"unknown status"
@@ -97,12 +97,15 @@ def test_workspace_layout_arithmetic(lib, impl, state):
     Bt, L, H, P, N, G, Q = 2, 300, 8, 64, 128, 2, 128
     nc = -(-L // Q)
     es = 4 if state == "f32" else 2
+    fused = impl == "fused"
     assert lay.nchunks == nc
-    K = 2 if impl == "fused" else nc + 1
+    K = 1 if fused else nc + 1
     assert lay.state_slots == K
     assert lay.dt_bytes == Bt * nc * H * Q * 4 == lay.acs_bytes
-    assert lay.cb_bytes == Bt * nc * G * Q * Q * 4
-    assert lay.s_bytes == (0 if impl == "fused" else Bt * nc * H * P * N * 4)
+    # fused: one CB run per (partition, (b, g) pair); at most B*G + 7 with up to 8 partitions
+    pair_slots = Bt * G + 7
+    assert lay.cb_bytes == (pair_slots if fused else Bt * G) * nc * Q * Q * 4
+    assert lay.s_bytes == (0 if fused else Bt * nc * H * P * N * 4)
     assert lay.states_bytes == Bt * K * H * P * N * es
     regions = sorted([(lay.dt_offset, lay.dt_bytes), (lay.acs_offset, lay.acs_bytes), (lay.cb_offset, lay.cb_bytes),
                       (lay.s_offset, lay.s_bytes), (lay.states_offset, lay.states_bytes),
@@ -112,9 +115,12 @@ def test_workspace_layout_arithmetic(lib, impl, state):
     assert lay.sync_offset <= lay.status_offset < lay.sync_offset + lay.sync_bytes
     assert lay.total_bytes >= lay.sync_offset + lay.sync_bytes
     assert ssd.workspace_size(p) == lay.total_bytes
-    if impl == "fused":
-        # flags [B][H][P/32][nc+1] + cs_done [B][nc] + bmm_done [B][nc][G] + ticket + abort + status
-        assert lay.sync_bytes == 4 * (Bt * H * 2 * (nc + 1) + Bt * nc + Bt * nc * G + 3)
+    if fused:
+        # flags [B][H][P/32][nc+1], cs_done and bmm_done [pair slots][nc], 8 partition counters
+        # 32 words apart, 8 owner words, exit counter, abort, status
+        assert lay.sync_bytes == 4 * (Bt * H * 2 * (nc + 1) + 2 * pair_slots * nc + 8 * 32 + 8 + 3)
+    else:
+        assert lay.sync_bytes == 8  # abort and status words
 
 
 def test_workspace_size_zero_for_invalid(lib):
