@@ -15,7 +15,7 @@
  * "Mamba-2炸裂升级！…", section "Mamba-2核心操作与融合的必要性"): chunk_cumsum, bmm,
  * chunk_state, state_passing, chunk_scan, either as five kernels (SSD_IMPL_UNFUSED)
  * or as one kernel whose workgroups claim cumsum and bmm work first and then
- * chunk_state -> state_passing -> chunk_scan work, ordered by per-chunk flags
+ * chunk_state -> state_passing -> chunk_scan work, ordered by flags and counters
  * (SSD_IMPL_FUSED; same write-up, section "高效内核融合技术揭秘").
  *
  * Conventions for every entry point:
@@ -147,7 +147,8 @@ const char* ssd_status_string(ssd_status_t s);
  *           unfused: [B][K = nc+1][H][P][N]                                      state_passing
  *           fused:   one slot (K = 1) per chain, updated in place chunk after chunk, in
  *                    an internal lane-major order (the fused kernel's own layout)
- *   sync    uint32 words: per-chain chunk flags, cumsum / bmm completion flags, one
+ *   sync    uint32 words: per-chain progress counters (one 128-byte line each),
+ *           cumsum / bmm completion flags, one
  *           work counter and one owner word per partition, the exit counter and the
  *           abort word (fused only)
  *   status  uint32 device status word

@@ -32,6 +32,17 @@ uint32_t spin_limit() {
     return v;
 }
 
+// MAMBA_SSD_CHAIN_GROUP: chains per claim group of the fused kernel (unset or 0: automatic).
+int chain_group_env() {
+    static const int v = [] {
+        const char* e = getenv("MAMBA_SSD_CHAIN_GROUP");
+        if (!e || !*e) return 0;
+        const long x = strtol(e, nullptr, 10);
+        return x > 0 && x < (1L << 30) ? (int)x : 0;
+    }();
+    return v;
+}
+
 struct Layout {
     ssd_workspace_layout_t w;
     // sync words: [flags | cs_done | bmm_done | tickets | owners | exit | abort | status]
@@ -88,7 +99,7 @@ Layout layout(const ssd_params_t* p) {
     w.cb_bytes = (fused ? PS : B * G) * nc * Q * Q * 4;
     w.s_bytes = fused ? 0 : B * nc * H * P * N * 4;
     w.states_bytes = B * K * H * P * N * elem_size(p->state_dtype);
-    l.nflags = fused ? B * H * (size_t)l.wph * (nc + 1) : 0;
+    l.nflags = fused ? B * H * (size_t)l.wph * ssd::kChainCounterStride : 0;
     l.flags_w = 0;
     l.cs_w = l.nflags;
     l.bmm_w = l.cs_w + PS * nc;
@@ -205,6 +216,7 @@ void set_partitions(const ssd_params_t* p, const Layout& l, const DevInfo& d, ss
     const int64_t nc = l.w.nchunks;
     a.nparts = d.nparts;
     a.cu_count = d.cus;
+    a.chain_group = chain_group_env();
     int pb = 0, maxw = 0;
     for (int x = 0; x <= d.nparts; ++x) {
         a.part_u0[x] = (int)(U * x / d.nparts);
@@ -396,10 +408,11 @@ static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt
         e = device_info(&d);
         if (e != hipSuccess) return hip_status(e);
         set_partitions(p, l, d, a);
-        // initial state into the ring's slot 0 and every sync word (flags, counters, status) reset
+        // initial state into the ring's slot 0; every sync word reset (chain counters to 1: the
+        // state entering chunk 0 is ready)
         const int es = (int)elem_size(p->state_dtype), K = l.w.state_slots;
         e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, p->dstate, K, 0, es,
-                                  a.flags, l.nsync, l.nflags, (uint32_t)(l.w.nchunks + 1), st);
+                                  a.flags, l.nsync, l.nflags, (uint32_t)ssd::kChainCounterStride, st);
         if (e == hipSuccess) e = mark(ev_begin);
         if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED, p, a, st);
         if (e == hipSuccess) e = mark(ev_end);

@@ -203,15 +203,15 @@ __device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) 
 }
 
 // ---- cross-workgroup waits -------------------------------------------------------------
-// Poll a flag word (sc1 loads, from the L2) until it is non-zero.  Bounded: after spin_limit polls (or
+// Poll a flag word (sc1 loads, from the L2) until it reaches `target`.  Bounded: after spin_limit polls (or
 // once any wait has given up) it raises the abort word and the status word -- device-scope
 // accesses, since every partition must see them -- and returns false, so every workgroup
 // still runs to completion.  All lanes of the calling wave poll the same address.
-__device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a) {
+__device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a, uint32_t target = 1u) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(f, 4);
     uint32_t spins = 0;
     bool ok = true;
-    while (__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, AUX_L2) == 0u) {
+    while (__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, AUX_L2) < target) {
         ++spins;
         if ((spins & 31u) == 0u) {
             if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
@@ -236,12 +236,22 @@ __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a) {
 // s_waitcnt vmcnt(0): every global load and store this wave issued has completed.
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-__device__ inline void raise_flag(uint32_t* f) { __builtin_amdgcn_raw_buffer_store_b32(1u, make_rsrc(f, 4), 0, 0, 0); }
+__device__ inline void raise_flag(uint32_t* f, uint32_t v = 1u) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, make_rsrc(f, 4), 0, 0, 0);
+}
 
-// Every lane: its stores have reached the L2, then set *f.
-__device__ inline void publish_flag_wave(uint32_t* f) {
+// Every lane: its stores have reached the L2, then set *f = v.
+__device__ inline void publish_flag_wave(uint32_t* f, uint32_t v = 1u) {
     wait_vm_all();
-    raise_flag(f);
+    raise_flag(f, v);
+}
+
+// Per-chain progress counter of the fused form: one word per (b, h, p-slice) chain, alone in
+// its 128-byte line, so the line stays resident in the L2 (a flag word that shares a line
+// with cold data, or a first store that allocates a partial line, makes the next sc1 read
+// go to memory).  Value v: the states entering chunks 0 .. v-1 are published.
+__device__ inline uint32_t* chain_counter(const SsdArgs& a, int b, int h, int ph, int WPH) {
+    return a.flags + (((size_t)b * a.nheads + h) * WPH + ph) * kChainCounterStride;
 }
 
 // Whole workgroup: every wave's stores have reached the L2, then thread 0 sets *f.
@@ -541,9 +551,8 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
         } else {
             // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c
             if (hvalid) {
-                const size_t chain = ((size_t)b * H + h) * WPH + ph;
-                uint32_t* fl = a.flags + chain * (nc + 1);
-                wait_flag(fl + c, a);
+                uint32_t* fl = chain_counter(a, b, h, ph, WPH);
+                wait_flag(fl, a, (uint32_t)c + 1);
                 const int K = a.slots;
                 const __amdgpu_buffer_rsrc_t rin =
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
@@ -558,7 +567,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                         sc[nb][pb] = ring_load(rin, a.state_dtype, off);
                         ring_store(rout, a.state_dtype, off, dec * sc[nb][pb] + acc[nb][pb]);
                     }
-                publish_flag_wave(fl + c + 1);
+                publish_flag_wave(fl, (uint32_t)c + 2);
             }
         }
     } else {

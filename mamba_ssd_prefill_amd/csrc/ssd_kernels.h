@@ -57,7 +57,9 @@ template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds_
 // (b, g), and bmm tiles (pair, c) into its own CB slots.  Its queue, in claim order:
 //   [0, np*nc)             cumsum tiles, chunk-major
 //   [np*nc, 2*np*nc)       bmm tiles, chunk-major
-//   [2*np*nc, +nu*nc)      chunk tiles (c, u), chunk-major
+//   [2*np*nc, +nu*nc)      chunk tiles: the chains in groups of chain_group, one group after
+//                          the other, chunk-major inside a group (so only one group's state
+//                          slots need to stay in the L2 at a time)
 // Workgroups are persistent: each reads the id of the XCD it runs on, takes tickets from that
 // partition's queue until it is empty, then leaves.  So every hand-off of a partition stays in
 // one L2 (see the coherence notes in ssd_device.h).  A chunk tile waits only on work with
@@ -135,8 +137,14 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
             }
         } else {
             const uint32_t v = t - 2 * f.n_cs;
-            const int c = v / f.nu;
-            const int u = f.u0 + (int)(v % f.nu);
+            const int cg = a.chain_group < f.nu ? a.chain_group : f.nu;
+            const uint32_t per_group = (uint32_t)cg * nc;
+            const int grp = v / per_group;
+            const uint32_t w = v - grp * per_group;
+            const int gu0 = grp * cg;
+            const int gsz = f.nu - gu0 < cg ? f.nu - gu0 : cg;
+            const int c = w / gsz;
+            const int u = f.u0 + gu0 + (int)(w % gsz);
             const int pair = u / tpg, tig = u % tpg, b = pair / Gn, g = pair % Gn;
             const size_t slot = (size_t)(f.pb + pair - f.p0) * nc + c;
             if (threadIdx.x == 0) {
@@ -190,6 +198,9 @@ inline hipError_t launch_fused(const void* fn, SsdArgs& a, hipStream_t st) {
     if (occ < 1) occ = 1;
     const int per_xcd = (a.cu_count / a.nparts > 0 ? a.cu_count / a.nparts : 1) * occ;
     const int wgs = per_xcd < a.part_max_work ? per_xcd : a.part_max_work;
+    // default: all of a partition's chains in one group (measured fastest: smaller groups keep
+    // fewer state slots live but serialise on the chunk-to-chunk hand-off)
+    if (a.chain_group <= 0) a.chain_group = 1 << 30;
     return launch(fn, (unsigned)(a.nparts * (wgs > 0 ? wgs : 1)), &a, st);
 }
 

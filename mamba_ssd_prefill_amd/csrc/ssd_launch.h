@@ -26,7 +26,7 @@ struct SsdArgs {
     float* cb;           // unfused: [B][nc][G][Q][Q]; fused: [pair slot][nc][Q][Q]
     float* s;            // [B][nc][H][P][N] (unfused form)
     void* states;        // unfused: [B][K][H][P][N]; fused: one ring slot per chain
-    uint32_t* flags;     // [B][H][WPH][nc + 1]
+    uint32_t* flags;     // fused: per-chain progress counters [B][H][WPH], 32 words apart
     uint32_t* cs_done;   // fused: [pair slot][nc]
     uint32_t* bmm_done;  // fused: [pair slot][nc]
     uint32_t* ticket;    // fused: one work counter per partition, kTicketStride words apart
@@ -44,11 +44,13 @@ struct SsdArgs {
     int nparts;
     int part_u0[kMaxXcc + 1];
     int part_pb[kMaxXcc + 1];
+    int chain_group;    // chains whose chunk tiles are claimed together (0: set at launch)
     int part_max_work;  // host only: the longest partition queue
     int cu_count;       // host only: compute units of the device
 };
 
-constexpr int kTicketStride = 32;  // one 128-byte line per partition counter
+constexpr int kTicketStride = 32;        // one 128-byte line per partition counter
+constexpr int kChainCounterStride = 32;  // one 128-byte line per chain progress counter
 
 enum : int {
     STEP_CUMSUM = 0,

@@ -77,7 +77,7 @@ template <int COLS, int KIND = SWZ_TR> __device__ inline int sw_off(int row, int
 
 // rows [0, rows) of a row-major slice (row r at byte r * rs) -> swizzled LDS tile [rows][COLS];
 // the four waves split the 1 KB copy instructions.
-template <int COLS, int KIND = SWZ_TR>
+template <int COLS, int KIND = SWZ_TR, int AUX = 0>
 __device__ inline void dma_rows(void* lds_tile, __amdgpu_buffer_rsrc_t rs_src, int rows, uint32_t rs) {
     constexpr int CH = COLS / 8;
     constexpr int RPI = 64 / CH;  // rows per 1 KB instruction
@@ -87,7 +87,7 @@ __device__ inline void dma_rows(void* lds_tile, __amdgpu_buffer_rsrc_t rs_src, i
         const int row = k * RPI + lane / CH;
         const int c = (lane % CH) ^ (KIND == SWZ_TR ? swz<CH>(row) : swz_row<CH>(row));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_src, SSD_LDS(void, (char*)lds_tile + k * 1024), 16,
-                                                 row * rs + c * 16, 0, 0, 0);
+                                                 row * rs + c * 16, 0, 0, AUX);
     }
 }
 
@@ -217,6 +217,22 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
 
     const float* a2_h = sA2 + hs * Q;
 
+    // Touch this wave's state-slot lines (one lane per 128-byte line, sc1 so nothing stale
+    // stays in the L1) so they are resident in the L2 when the state hop reads them after its
+    // wait: under load they are otherwise evicted between chunks and the hop -- the serial
+    // chain from chunk to chunk -- would pay a memory round trip.  The values read here are
+    // not used (the state may not be written yet).
+    uint32_t pf0 = 0, pf1 = 0;
+    if constexpr (MODE == MODE_FUSED) {
+        if (hvalid) {
+            const int K = a.slots;
+            const __amdgpu_buffer_rsrc_t rpf =
+                ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
+            pf0 = __builtin_amdgcn_raw_buffer_load_b32(rpf, (uint32_t)lane * 128, 0, AUX_L2);
+            pf1 = __builtin_amdgcn_raw_buffer_load_b32(rpf, 8192 + (uint32_t)lane * 128, 0, AUX_L2);
+        }
+    }
+
     // x operand, token-major: xf[kk][pb] holds x[kk*32 + 8q .. +7][ph*PW + pb*16 + r16]
     frag xf[KS][MBP];
 #pragma unroll
@@ -270,13 +286,16 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             }
             return;
         } else {
-            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c.  It comes before the round-2
-            // copies so that its flag waits only for the state stores: the hop is the serial
-            // chain between chunks.
+            // ---- round 2: C and the CB bands into LDS (x and B are no longer read).  The copies
+            // are in flight while the hop below waits for and updates the state.
+            __syncthreads();
+            dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
+            if constexpr (CB_LDS) dma_cb_bands<Q, CB_AUX>(sCB, cbp);
+            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c, in place in the chain's slot
             if (hvalid) {
-                const size_t chain = ((size_t)b * H + h) * WPH + ph;
-                uint32_t* fl = a.flags + chain * (nc + 1);
-                wait_flag(fl + c, a);
+                uint32_t* fl = chain_counter(a, b, h, ph, WPH);
+                wait_flag(fl, a, (uint32_t)c + 1);
+                asm volatile("" ::"v"(pf0), "v"(pf1));  // the touch loads are complete (long ago)
                 const int K = a.slots;
                 const __amdgpu_buffer_rsrc_t rin =
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
@@ -292,12 +311,8 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                         ring_store(rout, a.state_dtype, off, dec * sv + acc[nb][pb]);
                         scb[nb][pb] = cvt4<T>(sv);
                     }
-                publish_flag_wave(fl + c + 1);
+                publish_flag_wave(fl, (uint32_t)c + 2);  // its wait covers the copies too
             }
-            // ---- round 2: C and the CB bands into LDS (x and B are no longer read)
-            __syncthreads();
-            dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
-            if constexpr (CB_LDS) dma_cb_bands<Q, CB_AUX>(sCB, cbp);
             wait_vm_all();
             __syncthreads();  // C and CB are in LDS
         }
@@ -384,7 +399,10 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             xd0[pb] = xd_load(0, pb);
             xd1[pb] = xd_load(1, pb);
         }
-        T* yg = (T*)a.y;
+        // y: written once and never read here, so non-temporal (nt) stores keep it from
+        // pushing the state slots and CB out of the L2
+        const __amdgpu_buffer_rsrc_t yr =
+            make_rsrc((T*)a.y + (((size_t)b * L + tok0) * H + h) * P, (uint32_t)(valid - 1) * xrs + P * 2);
         // this lane's C-row read offsets for k step ks (row r16 of a 16-row block; the row
         // swizzle of C repeats every 16 rows, so block ib adds ib * 16 * N)
         int clo[N / 32], chi[N / 32];
@@ -460,7 +478,9 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     yv[1] += Dh * (float)xcur[pb][1];
                     yv[2] += Dh * (float)xcur[pb][2];
                     yv[3] += Dh * (float)xcur[pb][3];
-                    *(v4*)(yg + (((size_t)b * L + tok0 + i) * H + h) * P + p) = cvt4<T>(yv);
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4<T>(yv)), yr,
+                                                          (uint32_t)i * xrs + (uint32_t)p * 2, 0, 2);
                 }
             }
         }

@@ -116,9 +116,9 @@ def test_workspace_layout_arithmetic(lib, impl, state):
     assert lay.total_bytes >= lay.sync_offset + lay.sync_bytes
     assert ssd.workspace_size(p) == lay.total_bytes
     if fused:
-        # flags [B][H][P/32][nc+1], cs_done and bmm_done [pair slots][nc], 8 partition counters
-        # 32 words apart, 8 owner words, exit counter, abort, status
-        assert lay.sync_bytes == 4 * (Bt * H * 2 * (nc + 1) + 2 * pair_slots * nc + 8 * 32 + 8 + 3)
+        # chain counters [B][H][P/32] 32 words apart, cs_done and bmm_done [pair slots][nc],
+        # 8 partition tickets 32 words apart, 8 owner words, exit counter, abort, status
+        assert lay.sync_bytes == 4 * (Bt * H * 2 * 32 + 2 * pair_slots * nc + 8 * 32 + 8 + 3)
     else:
         assert lay.sync_bytes == 8  # abort and status words
 
