@@ -4,6 +4,7 @@
 
 Each translation unit is compiled in its own hipcc process (in parallel), then linked.
 """
+import hashlib
 import os
 import subprocess
 import sys
@@ -56,6 +57,17 @@ def build(force=True, verbose=False):
     subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     os.replace(tmp, LIB)
     return LIB
+
+
+def source_hash():
+    """Short hash of every kernel source file (csrc/ and the C header): a profile taken on
+    other sources is stale."""
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
 
 
 def _newest_input(src):
