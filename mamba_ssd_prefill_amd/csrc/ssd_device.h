@@ -236,6 +236,16 @@ __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a, uint32_t t
 // s_waitcnt vmcnt(0): every global load and store this wave issued has completed.
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier for LDS hand-offs only: this wave's LDS accesses have completed
+// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() (whose workgroup fence waits for
+// every outstanding global access too) it leaves global loads in flight, so a read issued
+// early keeps overlapping whatever follows.  Also a compiler barrier for memory accesses.
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ inline void raise_flag(uint32_t* f, uint32_t v = 1u) {
     __builtin_amdgcn_raw_buffer_store_b32(v, make_rsrc(f, 4), 0, 0, 0);
 }

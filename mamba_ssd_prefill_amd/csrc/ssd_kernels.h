@@ -111,10 +111,10 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     __syncthreads();
     const bool mine = __builtin_amdgcn_readfirstlane(s_word) != 0u;
     while (mine) {
-        __syncthreads();  // the previous tile is done with LDS and s_word
+        lds_barrier();  // the previous tile is done with LDS and s_word (its stores may still fly)
         const SsdArgs& a = fresh_args(a0);
         if (threadIdx.x == 0) s_word = atomicAdd(a.ticket + x * kTicketStride, 1u);
-        __syncthreads();
+        lds_barrier();
         const uint32_t t = __builtin_amdgcn_readfirstlane(s_word);
         const FusedPart f = fused_part(a, x);
         const int nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg, hpg = a.hpg, Q = a.chunk;
@@ -151,7 +151,7 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                 wait_flag(a.cs_done + slot, a);
                 wait_flag(a.bmm_done + slot, a);
             }
-            __syncthreads();
+            lds_barrier();  // every wave starts after the flags were seen
             chunk(a, b, c, g, tig, a.cb + slot * Q * Q);
         }
     }

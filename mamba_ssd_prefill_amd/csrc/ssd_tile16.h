@@ -47,7 +47,15 @@ template <typename T, int P, int N, int Q> struct Geo16 {
         return t;
     }
     static constexpr int SZ_CB = CB_LDS ? cb_pieces() * 16 : 0;
-    static constexpr int SZ_R1 = SZ_X > SZ_CB ? SZ_X : SZ_CB;  // x, later CB
+    static constexpr int SZ_R1 = SZ_X > SZ_CB ? SZ_X : SZ_CB;  // x, later CB (and L)
+    // L_h[i][j] = CB[i][j] exp(acs_i - acs_j) dt_j (j <= i, else 0) of every head of the tile,
+    // in T, staged as 32-row bands of the lower triangle: band r keeps columns [0, 32(r+1)) in
+    // rows of 4(r+1)+1 16-byte pieces (odd pitch: 16 consecutive rows hit distinct bank groups).
+    // Built once per tile over the CB bands when it fits in their space.
+    static constexpr int lband_pitch(int r) { return 4 * (r + 1) + 1; }
+    static constexpr int lband_base(int r) { return 32 * r * (2 * r + 3); }  // pieces before band r
+    static constexpr int SZ_LH = lband_base(KS) * 16;                          // bytes per head
+    static constexpr bool L_LDS = CB_LDS && HPT * SZ_LH <= SZ_R1;
     static constexpr int SMEM = SZ_R1 + SZ_BC + SZ_V;
     static_assert(Q % 32 == 0 && Q <= 256, "Q must be a multiple of 32, at most 256");
     static_assert(N % 32 == 0, "N % 32 == 0");
@@ -149,6 +157,141 @@ template <int Q> __device__ inline int cb_off(int i, int j) {
     return (base + (i & 31) * (8 * band + 9)) * 4 + j;
 }
 
+// Piece offset (16-byte units) of L_h[i][8 jp .. 8 jp + 7] inside one head's bands.
+template <typename G_> __device__ inline int lband_off(int i, int jp) {
+    const int r = i >> 5;
+    return G_::lband_base(r) + (i & 31) * G_::lband_pitch(r) + jp;
+}
+
+// The L bands of every valid head of the tile, built once per tile from CB.  Items are
+// (row i, 8-column piece jp) of the lower 32-row bands, of three kinds:
+//   factored: j's 16-token block ends before row i (all of a 32-block left of the diagonal,
+//             and the lower-left 16x16 of a diagonal 32-block): L = CB * exp(acs_i - acs_m) *
+//             sF[j], with m = the last token of j's 16-block and sF[j] = exp(acs_m - acs_j) dt_j.
+//             Both factors are at most 1 (acs does not increase along the chunk), so nothing
+//             overflows; a factor underflows only when the exact product is below e^-87.
+//   diagonal: i and j in the same 16-token block: L = CB * exp2(acs_i log2 e - sE[j]) with
+//             sE[j] = acs_j log2 e - log2 dt_j, masked to j <= i;
+//   zero:     the upper-right 16x16 of a diagonal 32-block.
+// load() reads this thread's CB pieces from HBM/L2 into registers (issued early, so the reads
+// overlap other work); store() writes the L pieces of every valid head into LDS.
+template <typename T, typename G_, int AUX> struct LBuild {
+    static constexpr int KS = G_::KS, Q = KS * 32, HPT = G_::HPT;
+    static constexpr int NF = 64 * KS * (KS - 1) + 32 * KS;  // factored items, all bands
+    static constexpr int ND = 64 * KS, NZ = 32 * KS;         // diagonal, zero items
+    static constexpr int FI = (NF + 255) / 256, DI = (ND + 255) / 256;
+    typedef typename TT<T>::frag frag;
+    f32x4 cf[FI][2], cd[DI][2];
+    int fi[FI], fj[FI];
+
+    // factored item k -> (i, jp): band b holds rows 0..31 x pieces [0, 4b), then rows 16..31 x
+    // pieces {4b, 4b + 1}
+    __device__ static inline void f_item(int k, int& i, int& jp) {
+        int b = 0, base = 0;
+#pragma unroll
+        for (int bb = 1; bb < KS; ++bb) {
+            const int fb = 64 * bb * (bb - 1) + 32 * bb;
+            if (k >= fb) {
+                b = bb;
+                base = fb;
+            }
+        }
+        const int kl = k - base;
+        if (kl < 128 * b) {
+            // row = kl / (4b) for b in 1..3 (kl < 384): multiply by 2^16 / b, rounded up
+            const int mul = b == 1 ? 65536 : (b == 2 ? 32768 : 21846);
+            const int row = ((kl >> 2) * mul) >> 16;
+            jp = kl - row * 4 * b;
+            i = 32 * b + row;
+        } else {
+            const int kz = kl - 128 * b;
+            i = 32 * b + 16 + (kz >> 1);
+            jp = 4 * b + (kz & 1);
+        }
+    }
+    __device__ static inline void d_item(int k, int& i, int& jp) {
+        const int b = k >> 6, kl = k & 63;
+        i = 32 * b + (kl < 32 ? kl >> 1 : 16 + ((kl - 32) >> 1));
+        jp = 4 * b + (kl < 32 ? 0 : 2) + (kl & 1);
+    }
+
+    __device__ inline void load(const float* cbp, int tid) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(cbp, (uint32_t)(Q * Q * 4));
+#pragma unroll
+        for (int it = 0; it < FI; ++it) {
+            const int k = tid + it * 256;
+            int i = 0, jp = 0;
+            if (k < NF) f_item(k, i, jp);
+            fi[it] = i;
+            fj[it] = jp;
+            const uint32_t off = k < NF ? (uint32_t)(i * Q + 8 * jp) * 4 : 0x40000000u;  // past the end: zeros
+            cf[it][0] = bload_f32x4<AUX>(r, off);
+            cf[it][1] = bload_f32x4<AUX>(r, off + 16);
+        }
+#pragma unroll
+        for (int it = 0; it < DI; ++it) {
+            const int k = tid + it * 256;
+            int i = 0, jp = 0;
+            if (k < ND) d_item(k, i, jp);
+            const uint32_t off = k < ND ? (uint32_t)(i * Q + 8 * jp) * 4 : 0x40000000u;
+            cd[it][0] = bload_f32x4<AUX>(r, off);
+            cd[it][1] = bload_f32x4<AUX>(r, off + 16);
+        }
+    }
+
+    __device__ inline void store(T* sL, const float* sA2, const float* sF, const float* sE, int nvh, int tid) {
+#pragma unroll
+        for (int it = 0; it < FI; ++it) {
+            const int k = tid + it * 256;
+            if (k < NF) {
+                const int i = fi[it], jp = fj[it], j0 = 8 * jp;
+                const int o = lband_off<G_>(i, jp) * 8;
+#pragma unroll
+                for (int hh = 0; hh < HPT; ++hh) {
+                    if (hh < nvh) {
+                        const float g = __builtin_amdgcn_exp2f(sA2[hh * Q + i] - sA2[hh * Q + (j0 | 15)]);
+                        const f32x4 f0 = *(const f32x4*)(sF + hh * Q + j0) * g;
+                        const f32x4 f1 = *(const f32x4*)(sF + hh * Q + j0 + 4) * g;
+                        *(frag*)(sL + (size_t)hh * (G_::SZ_LH / sizeof(T)) + o) = pack8<T>(cf[it][0] * f0, cf[it][1] * f1);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < DI; ++it) {
+            const int k = tid + it * 256;
+            if (k < ND) {
+                int i, jp;
+                d_item(k, i, jp);
+                const int j0 = 8 * jp;
+                const int o = lband_off<G_>(i, jp) * 8;
+#pragma unroll
+                for (int hh = 0; hh < HPT; ++hh) {
+                    if (hh < nvh) {
+                        const float ai = sA2[hh * Q + i];
+                        const f32x4 e0 = *(const f32x4*)(sE + hh * Q + j0);
+                        const f32x4 e1 = *(const f32x4*)(sE + hh * Q + j0 + 4);
+                        f32x4 l0, l1;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            l0[e] = j0 + e <= i ? cd[it][0][e] * __builtin_amdgcn_exp2f(ai - e0[e]) : 0.f;
+                            l1[e] = j0 + 4 + e <= i ? cd[it][1][e] * __builtin_amdgcn_exp2f(ai - e1[e]) : 0.f;
+                        }
+                        *(frag*)(sL + (size_t)hh * (G_::SZ_LH / sizeof(T)) + o) = pack8<T>(l0, l1);
+                    }
+                }
+            }
+        }
+        for (int k = tid; k < NZ; k += 256) {
+            const int bb = k >> 5, kl = k & 31;
+            const int o = lband_off<G_>(32 * bb + (kl >> 1), 4 * bb + 2 + (kl & 1)) * 8;
+#pragma unroll
+            for (int hh = 0; hh < HPT; ++hh)
+                if (hh < nvh) *(frag*)(sL + (size_t)hh * (G_::SZ_LH / sizeof(T)) + o) = vzero<frag>();
+        }
+    }
+};
+
 template <typename T, int P, int N, int Q, int MODE>
 __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbp) {
     typedef Geo16<T, P, N, Q> G_;
@@ -207,7 +350,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             sA2[e] = bload_f32<AUX>(ra, (uint32_t)e * 4) * LOG2E;
         }
     }
-    __syncthreads();
+    lds_barrier();  // dt, acs in LDS (the x / B copies may still be in flight)
     for (int e = tid; e < HPT * Q; e += 256) {
         const int hh = e / Q;
         sW[e] = __builtin_amdgcn_exp2f(sA2[hh * Q + Q - 1] - sA2[e]) * sDt[e];
@@ -242,6 +385,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
 
     // S_c in accumulator layout, rounded to T: tile (nb, pb), lane -> S[p = ph*PW + pb*16 + r16][n = nb*16 + 4q + r]
     v4 scb[NB][MBP];
+    LBuild<T, G_, AUX> lb;  // the L bands' CB pieces, read early (Q <= 128 with room for L)
     if constexpr (MODE != MODE_SCAN) {
         // ---- chunk_state: s^T[n][p] = sum_j B[j][n] (x[j][p] w_j) ----
         f32x4 acc[NB][MBP];
@@ -286,11 +430,15 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             }
             return;
         } else {
-            // ---- round 2: C and the CB bands into LDS (x and B are no longer read).  The copies
-            // are in flight while the hop below waits for and updates the state.
-            __syncthreads();
+            // ---- round 2: C into LDS (B is no longer read) and CB -- into registers for the L
+            // bands, else into LDS.  The reads are in flight while the hop below waits for and
+            // updates the state.
+            lds_barrier();  // every wave is done reading x and B
             dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
-            if constexpr (CB_LDS) dma_cb_bands<Q, CB_AUX>(sCB, cbp);
+            if constexpr (G_::L_LDS)
+                lb.load(cbp, tid);
+            else if constexpr (CB_LDS)
+                dma_cb_bands<Q, CB_AUX>(sCB, cbp);
             // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c, in place in the chain's slot
             if (hvalid) {
                 uint32_t* fl = chain_counter(a, b, h, ph, WPH);
@@ -314,13 +462,16 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 publish_flag_wave(fl, (uint32_t)c + 2);  // its wait covers the copies too
             }
             wait_vm_all();
-            __syncthreads();  // C and CB are in LDS
+            __syncthreads();  // C (and CB) are in LDS
         }
     } else {
         __syncthreads();
-        // ---- round 2: the CB bands replace x in LDS; S_c and x for D x into registers ----
+        // ---- round 2: CB (into registers for the L bands, else into LDS over x); S_c into registers
         __syncthreads();  // every wave holds its x operand in registers
-        if constexpr (CB_LDS) dma_cb_bands<Q, 0>(sCB, cbp);
+        if constexpr (G_::L_LDS)
+            lb.load(cbp, tid);
+        else if constexpr (CB_LDS)
+            dma_cb_bands<Q, 0>(sCB, cbp);
         if (hvalid) {
             const int K = a.slots, slot = c % K;
 #pragma unroll
@@ -347,14 +498,43 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         // the exact product is below e^-87.  The column factor scales x once per tile; the row
         // factor is one exp per lane per block.  On the diagonal, each element takes its own
         // exp2(acs_i log2(e) - sE[j]) = exp(acs_i - acs_j) dt_j.
+        // (With the L bands, the column factors end at 16-token blocks instead: see LBuild.)
+        //
+        // x for the D x term in the y layout (x[ib*16 + r16][ph*PW + pb*16 + 4q .. +3]).  While the
+        // x tile is still in LDS (it is, unless the CB bands were copied over it) it comes from
+        // there: with the L bands, which replace it next, every row block is read now; without
+        // CB in LDS, at its use.  Otherwise it is read again from HBM/L2, two blocks ahead.
+        constexpr bool XD_LDS = G_::L_LDS || !CB_LDS;
+        constexpr int XDA = G_::L_LDS ? QB : (XD_LDS ? 1 : 2);
+        const __amdgpu_buffer_rsrc_t xr =
+            make_rsrc((const T*)a.x + (((size_t)b * L + tok0) * H + h) * P, (uint32_t)(valid - 1) * xrs + P * 2);
+        const T* sX_h = sX + hs * Q * P;
+        auto xd_load = [&](int ib, int pb) -> v4 {
+            if constexpr (XD_LDS)
+                return *(const v4*)(sX_h + sw_off<P>(ib * 16 + r16, ph * PW + pb * 16 + 4 * q));
+            const uint32_t off = (uint32_t)(ib * 16 + r16) * xrs + (uint32_t)(ph * PW + pb * 16 + 4 * q) * 2;
+            return __builtin_bit_cast(v4, __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0));
+        };
+        v4 xd[XDA][MBP];
+        if (hvalid) {
+#pragma unroll
+            for (int ib = 0; ib < (XD_LDS && !G_::L_LDS ? 0 : XDA); ++ib)
+#pragma unroll
+                for (int pb = 0; pb < MBP; ++pb) xd[ib][pb] = xd_load(ib, pb);
+        }
         for (int e = tid; e < HPT * Q; e += 256) {
             const int hh = e / Q, j = e - hh * Q;
             const float dt = sDt[e];
-            const float ar = sA2[hh * Q + (j | 31)];
+            const float ar = sA2[hh * Q + (G_::L_LDS ? (j | 15) : (j | 31))];
             sF[e] = __builtin_amdgcn_exp2f(ar - sA2[e]) * dt;
             sE[e] = sA2[e] - __log2f(dt);
         }
-        __syncthreads();
+        lds_barrier();
+        if constexpr (G_::L_LDS) {
+            const int nvh = hpg - tig * HPT < HPT ? hpg - tig * HPT : HPT;
+            lb.store((T*)smem, sA2, sF, sE, nvh, tid);  // over x (already in registers)
+            lds_barrier();                              // L is complete
+        }
         if (!hvalid) return;
         // S_c as the A operand of C . S^T; k slots of step ks: n = 32ks + 4q + {0..3} and
         // 32ks + 16 + 4q + {0..3} (the accumulator layout), matched by the C reads below.
@@ -364,12 +544,13 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
 #pragma unroll
             for (int pb = 0; pb < MBP; ++pb)
                 sop[ks][pb] = __builtin_shufflevector(scb[2 * ks][pb], scb[2 * ks + 1][pb], 0, 1, 2, 3, 4, 5, 6, 7);
-        // x scaled by the column factor, for the blocks left of the diagonal
+        // x scaled by the column factor, for the blocks left of the diagonal (without L bands)
         frag xs[KS][MBP];
         const float* f_h = sF + hs * Q;
         const float* e_h = sE + hs * Q;
+        const T* sL_h = (const T*)smem + (size_t)hs * G_::SZ_LH / sizeof(T);
 #pragma unroll
-        for (int kk = 0; kk + 1 < KS; ++kk) {
+        for (int kk = 0; kk + 1 < (G_::L_LDS ? 0 : KS); ++kk) {
             const f32x4 f0 = *(const f32x4*)(f_h + kk * 32 + 8 * q);
             const f32x4 f1 = *(const f32x4*)(f_h + kk * 32 + 8 * q + 4);
 #pragma unroll
@@ -385,20 +566,6 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         }
         const float Dh = a.D ? a.D[h] : 0.f;
         const __amdgpu_buffer_rsrc_t cbr = make_rsrc(cbp, (uint32_t)(Q * Q * 4));
-        // x for the D x term in the y layout (x[ib*16 + r16][ph*PW + pb*16 + 4q .. +3]), read from
-        // HBM/L2 two row blocks ahead of its use; rows past the sequence read as zeros
-        const __amdgpu_buffer_rsrc_t xr =
-            make_rsrc((const T*)a.x + (((size_t)b * L + tok0) * H + h) * P, (uint32_t)(valid - 1) * xrs + P * 2);
-        auto xd_load = [&](int ib, int pb) -> v4 {
-            const uint32_t off = (uint32_t)(ib * 16 + r16) * xrs + (uint32_t)(ph * PW + pb * 16 + 4 * q) * 2;
-            return __builtin_bit_cast(v4, __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0));
-        };
-        v4 xd0[MBP], xd1[MBP];
-#pragma unroll
-        for (int pb = 0; pb < MBP; ++pb) {
-            xd0[pb] = xd_load(0, pb);
-            xd1[pb] = xd_load(1, pb);
-        }
         // y: written once and never read here, so non-temporal (nt) stores keep it from
         // pushing the state slots and CB out of the L2
         const __amdgpu_buffer_rsrc_t yr =
@@ -430,8 +597,17 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
 #pragma unroll
             for (int pb = 0; pb < MBP; ++pb) accY[pb] *= ei;
             const int kd = ib >> 1;  // the diagonal 32-column block of these 16 rows
+            if constexpr (G_::L_LDS) {
+                // L^T operand straight from the bands: lane (r16, q) takes L[i][32kk + 8q .. +7]
 #pragma unroll
-            for (int kk = 0; kk <= kd; ++kk) {
+                for (int kk = 0; kk <= kd; ++kk) {
+                    const frag lf = *(const frag*)(sL_h + lband_off<G_>(i, kk * 4 + q) * 8);
+#pragma unroll
+                    for (int pb = 0; pb < MBP; ++pb) accY[pb] = TT<T>::mma(xf[kk][pb], lf, accY[pb]);
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk <= (G_::L_LDS ? -1 : kd); ++kk) {
                 const int j0 = kk * 32 + 8 * q;
                 f32x4 c0, c1;
                 if constexpr (CB_LDS) {
@@ -465,9 +641,15 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             v4 xcur[MBP];
 #pragma unroll
             for (int pb = 0; pb < MBP; ++pb) {
-                xcur[pb] = xd0[pb];
-                xd0[pb] = xd1[pb];
-                if (ib + 2 < QB) xd1[pb] = xd_load(ib + 2, pb);
+                if constexpr (G_::L_LDS) {
+                    xcur[pb] = xd[ib][pb];
+                } else if constexpr (XD_LDS) {
+                    xcur[pb] = xd_load(ib, pb);
+                } else {
+                    xcur[pb] = xd[0][pb];
+                    xd[0][pb] = xd[1][pb];
+                    if (ib + 2 < QB) xd[1][pb] = xd_load(ib + 2, pb);
+                }
             }
             if (i < valid) {
 #pragma unroll
