@@ -8,6 +8,12 @@
 
 namespace ssd {
 
+// No-op cross-tile prefetch hooks (see PrefetchHook) for the unfused kernels.
+struct NoHook {
+    __device__ inline void claim() const {}
+    __device__ inline uint32_t touch() const { return 0u; }
+};
+
 // ---- unfused form: one kernel per step -------------------------------------------------
 template <typename T> __global__ __launch_bounds__(256) void k_chunk_cumsum(SsdArgs a) {
     const int c = blockIdx.x % a.nchunks, b = blockIdx.x / a.nchunks;
@@ -47,7 +53,7 @@ template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds_
     r /= a.ngroups;
     const int c = r % a.nchunks;
     const int b = r / a.nchunks;
-    chunk_tile16<T, P, N, Q, MODE>(a, b, c, g, tig, smem, cb_global(a, b, c, g));
+    chunk_tile16<T, P, N, Q, MODE>(a, b, c, g, tig, smem, cb_global(a, b, c, g), NoHook{});
 }
 
 // ---- fused form: a single launch ([KF] "高效内核融合技术揭秘") ------------------------------
@@ -95,10 +101,69 @@ __device__ inline const SsdArgs& fresh_args(const SsdArgs& a) {
     return *(const SsdArgs*)((const char*)&a + zero);
 }
 
-// chunk(args, b, c, g, tig, cb) runs one chunk tile after its cumsum and bmm tiles are done.
-template <int HPT, typename T, int N, typename ChunkFn>
+// The chain and chunk of chunk ticket t (t >= 2 * n_cs of partition f): the chains are taken
+// in groups of chain_group, one group after the other, chunk-major inside a group.
+struct ChunkItem {
+    int b, c, g, tig;
+    size_t slot;  // cs_done / bmm_done / cb slot of (pair, c)
+};
+__device__ inline ChunkItem chunk_item(const SsdArgs& a, const FusedPart& f, uint32_t t) {
+    const int nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
+    const uint32_t v = t - 2 * f.n_cs;
+    const int cg = a.chain_group < f.nu ? a.chain_group : f.nu;
+    const uint32_t per_group = (uint32_t)cg * nc;
+    const int grp = v / per_group;
+    const uint32_t w = v - grp * per_group;
+    const int gu0 = grp * cg;
+    const int gsz = f.nu - gu0 < cg ? f.nu - gu0 : cg;
+    const int u = f.u0 + gu0 + (int)(w % gsz);
+    const int pair = u / tpg;
+    ChunkItem it;
+    it.c = w / gsz;
+    it.tig = u % tpg;
+    it.b = pair / Gn;
+    it.g = pair % Gn;
+    it.slot = (size_t)(f.pb + pair - f.p0) * nc + it.c;
+    return it;
+}
+
+// Cross-tile prefetch of the fused form.  A chunk tile calls claim() once its round-2 reads are
+// issued (thread 0 takes the workgroup's next ticket, so the atomic overlaps the state hop) and
+// touch() once its L bands are built (every thread loads one word of each 128-byte line of the
+// next chunk tile's x rows, which are then in the L2 when that tile copies them).  The next
+// ticket is larger than the current one and runs only after it, so the claim order keeps
+// every wait finite.  touch() returns the loaded words, to be consumed (asm sink) at the end.
+template <int HPT, int P> struct PrefetchHook {
+    const SsdArgs& a;
+    const FusedPart& f;
+    int part;
+    uint32_t* s_next;  // LDS
+    __device__ inline void claim() const {
+        if (threadIdx.x == 0) *s_next = atomicAdd(a.ticket + part * kTicketStride, 1u);
+    }
+    __device__ inline uint32_t touch() const {
+        const uint32_t tn = __builtin_amdgcn_readfirstlane(*s_next);
+        if (tn < 2 * f.n_cs || tn >= f.n_total) return 0u;
+        const ChunkItem it = chunk_item(a, f, tn);
+        const int L = a.seqlen, H = a.nheads, Q = a.chunk, hpg = a.hpg;
+        const int tok0 = it.c * Q, valid = L - tok0 < Q ? L - tok0 : Q;
+        const int nvh = hpg - it.tig * HPT < HPT ? hpg - it.tig * HPT : HPT;
+        const uint32_t xrs = (uint32_t)H * P * 2;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(
+            (const char*)a.x + ((((size_t)it.b * L + tok0) * H + it.g * hpg + it.tig * HPT) * P) * 2,
+            (uint32_t)(valid - 1) * xrs + (uint32_t)nvh * P * 2);
+        constexpr int LPR = (HPT * P * 2 + 127) / 128;  // 128-byte lines per row
+        uint32_t acc = 0;
+        for (int k = tid_here(); k < Q * LPR; k += 256)
+            acc += __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(k / LPR) * xrs + (uint32_t)(k % LPR) * 128, 0, 0);
+        return acc;
+    }
+};
+
+// chunk(args, b, c, g, tig, cb, hook) runs one chunk tile after its cumsum and bmm tiles are done.
+template <int HPT, int P, typename T, int N, typename ChunkFn>
 __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
-    __shared__ uint32_t s_word;
+    __shared__ uint32_t s_word, s_next;
     const uint32_t raw = xcc_id();
     const int x = (int)(raw % (uint32_t)a0.nparts);
     const SsdArgs& a = a0;
@@ -110,12 +175,17 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     }
     __syncthreads();
     const bool mine = __builtin_amdgcn_readfirstlane(s_word) != 0u;
+    uint32_t pending = 0xffffffffu;  // a ticket the previous chunk tile claimed ahead
     while (mine) {
         lds_barrier();  // the previous tile is done with LDS and s_word (its stores may still fly)
         const SsdArgs& a = fresh_args(a0);
-        if (threadIdx.x == 0) s_word = atomicAdd(a.ticket + x * kTicketStride, 1u);
-        lds_barrier();
-        const uint32_t t = __builtin_amdgcn_readfirstlane(s_word);
+        uint32_t t = pending;
+        if (t == 0xffffffffu) {
+            if (threadIdx.x == 0) s_word = atomicAdd(a.ticket + x * kTicketStride, 1u);
+            lds_barrier();
+            t = __builtin_amdgcn_readfirstlane(s_word);
+        }
+        pending = 0xffffffffu;
         const FusedPart f = fused_part(a, x);
         const int nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg, hpg = a.hpg, Q = a.chunk;
         if (t >= f.n_total) break;
@@ -136,23 +206,16 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                 publish_flag_block(a.bmm_done + slot);
             }
         } else {
-            const uint32_t v = t - 2 * f.n_cs;
-            const int cg = a.chain_group < f.nu ? a.chain_group : f.nu;
-            const uint32_t per_group = (uint32_t)cg * nc;
-            const int grp = v / per_group;
-            const uint32_t w = v - grp * per_group;
-            const int gu0 = grp * cg;
-            const int gsz = f.nu - gu0 < cg ? f.nu - gu0 : cg;
-            const int c = w / gsz;
-            const int u = f.u0 + gu0 + (int)(w % gsz);
-            const int pair = u / tpg, tig = u % tpg, b = pair / Gn, g = pair % Gn;
-            const size_t slot = (size_t)(f.pb + pair - f.p0) * nc + c;
+            const ChunkItem it = chunk_item(a, f, t);
             if (threadIdx.x == 0) {
-                wait_flag(a.cs_done + slot, a);
-                wait_flag(a.bmm_done + slot, a);
+                wait_flag(a.cs_done + it.slot, a);
+                wait_flag(a.bmm_done + it.slot, a);
             }
             lds_barrier();  // every wave starts after the flags were seen
-            chunk(a, b, c, g, tig, a.cb + slot * Q * Q);
+            const PrefetchHook<HPT, P> hook{a, f, x, &s_next};
+            chunk(a, it.b, it.c, it.g, it.tig, a.cb + it.slot * Q * Q, hook);
+            lds_barrier();  // s_next holds the ticket claimed ahead
+            pending = __builtin_amdgcn_readfirstlane(s_next);
         }
     }
     // The last workgroup to leave checks that every partition's queue was emptied (a
@@ -170,15 +233,18 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
 
 template <typename T, int P, int N> __global__ __launch_bounds__(256) void k_fused(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo<T, P, N>::SMEM];
-    fused_loop<Geo<T, P, N>::HPT, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig, const float* cbp) {
+    fused_loop<Geo<T, P, N>::HPT, P, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig, const float* cbp,
+                                                  const auto& hook) {
+        hook.claim();
         chunk_tile<T, P, N, MODE_FUSED>(ai, b, c, g, tig, smem, cbp);
     });
 }
 
 template <typename T, int P, int N, int Q> __global__ __launch_bounds__(256, 2) void k_fused16(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
-    fused_loop<Geo16<T, P, N, Q>::HPT, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig, const float* cbp) {
-        chunk_tile16<T, P, N, Q, MODE_FUSED>(ai, b, c, g, tig, smem, cbp);
+    fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
+                                                       const float* cbp, const auto& hook) {
+        chunk_tile16<T, P, N, Q, MODE_FUSED>(ai, b, c, g, tig, smem, cbp, hook);
     });
 }
 
