@@ -207,11 +207,20 @@ __device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) 
 // once any wait has given up) it raises the abort word and the status word -- device-scope
 // accesses, since every partition must see them -- and returns false, so every workgroup
 // still runs to completion.  All lanes of the calling wave poll the same address.
+// Waiters further back sleep longer between polls (s_sleep n is about 64 n cycles): a chain's
+// counter is polled by every waiting tile of the chain, and a tight loop from all of them
+// would saturate its L2 channel -- slowing the very stores it waits for.
 __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a, uint32_t target = 1u) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(f, 4);
     uint32_t spins = 0;
     bool ok = true;
-    while (__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, AUX_L2) < target) {
+    uint32_t v;
+    while ((v = __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, AUX_L2)) < target) {
+        const uint32_t behind = target - v;  // hand-offs still to come before this one
+        if (behind > 3u)
+            __builtin_amdgcn_s_sleep(127);
+        else if (behind > 1u)
+            __builtin_amdgcn_s_sleep(24);
         ++spins;
         if ((spins & 31u) == 0u) {
             if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
