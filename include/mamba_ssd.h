@@ -140,20 +140,30 @@ const char* ssd_status_string(ssd_status_t s);
  *   cb      fp32 [B][nc][G][Q][Q]    CB[i][j] = C_i . B_j for j <= i; entries
  *                                    with j > i are never written nor read      bmm
  *           fused: [B*G + 7][nc][Q][Q], one [nc] run per (work partition, (b, g) pair)
- *   s       fp32 [B][nc][H][P][N]    chunk-end state from a zero start
- *                                    (unfused only; 0 bytes when fused)          chunk_state
+ *   s       fp32 [B][nc][H][P][N]    chunk-end state from a zero start            chunk_state
+ *           unfused: as shown; fused: 0 bytes, or with the relay form's buffers (below) a
+ *           ring of 32 chunk states per chain ([B][H][P][N] x 32 fp32) followed by a ring of
+ *           min(16, nc + 1) states in in_dtype ([B][H][P][N] x min(16, nc + 1)), both in the
+ *           fused kernel's own order
  *   states  state_dtype, K slots     state entering chunk c lives in slot c % K; slot 0
  *                                    holds the initial state, slot nc % K the final one
  *           unfused: [B][K = nc+1][H][P][N]                                      state_passing
- *           fused:   one slot (K = 1) per chain, updated in place chunk after chunk, in
- *                    an internal lane-major order (the fused kernel's own layout)
- *   sync    uint32 words: per-chain progress counters (one 128-byte line each),
- *           cumsum / bmm completion flags, one
+ *           fused:   K = 1 slot per chain, updated in place chunk after chunk (relay form:
+ *                    K = 2, the initial state in slot 0 and the final one in slot 1), in an
+ *                    internal lane-major order (the fused kernel's own layout)
+ *   sync    uint32 words: per-chain words (three 128-byte lines each: progress counter,
+ *           relay slot words), cumsum / bmm completion flags, one
  *           work counter and one owner word per partition, the exit counter and the
  *           abort word (fused only)
  *   status  uint32 device status word
  * The fused form splits its work into one partition per XCD of the device (at most 8);
- * the sizes above are bounds that hold for any such split.
+ * the sizes above are bounds that hold for any such split.  Shapes with at most 128
+ * chains (batch * ngroups * ceil(heads per group / heads per tile); 4 heads per tile
+ * for headdim <= 32, 2 for 64, 1 for 128) get the buffers of the fused relay form, in which a
+ * dedicated work item per chain passes the state from chunk to chunk (used when every
+ * partition has at least four workgroups per chain).  The environment variable
+ * MAMBA_SSD_RELAY = 0 / 1 forces the buffers off / on; it is read on every call, so
+ * workspace sizing and the call must see the same value.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
     size_t total_bytes;

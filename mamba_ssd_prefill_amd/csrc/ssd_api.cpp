@@ -14,8 +14,10 @@
 
 namespace {
 
-constexpr int kRingSlots = 1;        // fused form: one state slot per chain, updated in place
 constexpr size_t kAlign = 256;       // workspace region alignment
+// Fused form: shapes with at most this many chains (b, g, tile-in-group) get the relay form's
+// buffers and use it when every partition has enough workgroups (see set_partitions).
+constexpr int64_t kRelayMaxChains = 128;
 constexpr uint32_t kDefaultSpin = 1u << 22;
 
 size_t elem_size(int dt) { return dt == SSD_F32 ? 4 : 2; }
@@ -43,12 +45,33 @@ int chain_group_env() {
     return v;
 }
 
+// MAMBA_SSD_RELAY: "0" never uses the fused relay form, "1" uses it whenever a partition has
+// enough workgroups; unset: by shape (kRelayMaxChains).  Read on every call.
+int relay_env() {
+    const char* e = getenv("MAMBA_SSD_RELAY");
+    if (!e || !*e) return -1;
+    return e[0] == '0' ? 0 : 1;
+}
+
+int64_t chain_count(const ssd_params_t* p) {
+    const int64_t hpg = p->nheads / p->ngroups, hpt = ssd::heads_per_tile(p->headdim);
+    return (int64_t)p->batch * p->ngroups * ((hpg + hpt - 1) / hpt);
+}
+
+// Whether the workspace carries the relay form's buffers (fused form only).
+bool relay_capable(const ssd_params_t* p) {
+    if (p->impl != SSD_IMPL_FUSED) return false;
+    const int env = relay_env();
+    return env >= 0 ? env == 1 : chain_count(p) <= kRelayMaxChains;
+}
+
 struct Layout {
     ssd_workspace_layout_t w;
     // sync words: [flags | cs_done | bmm_done | tickets | owners | exit | abort | status]
     size_t nflags, nsync;
     size_t flags_w, cs_w, bmm_w, ticket_w, owner_w, exit_w, abort_w, status_w;
-    int tpg, wph;
+    size_t agg_bytes;  // relay form: bytes of the chunk-state ring at the start of `s`
+    int tpg, wph, op_slots;
 };
 
 // Upper bound of the fused form's (b, g) pair slots: the B*G pairs, plus one more for every
@@ -75,7 +98,7 @@ ssd_status_t validate(const ssd_params_t* p) {
     const int64_t hpg = p->nheads / p->ngroups;
     const int64_t tpg = (hpg + ssd::heads_per_tile(P) - 1) / ssd::heads_per_tile(P);
     const int64_t pairs = (int64_t)p->batch * p->ngroups;
-    const int64_t tickets = nc * (2 * (pairs + ssd::kMaxXcc) + pairs * tpg);
+    const int64_t tickets = nc * (2 * (pairs + ssd::kMaxXcc) + pairs * tpg) + 4 * pairs * tpg;
     if (tickets >= (int64_t)1 << 31) return SSD_ERR_INVALID_SHAPE;
     if ((int64_t)p->batch * p->seqlen * p->nheads >= (int64_t)1 << 40) return SSD_ERR_INVALID_SHAPE;
     return SSD_OK;
@@ -89,7 +112,10 @@ Layout layout(const ssd_params_t* p) {
     l.wph = ssd::waves_per_head(p->headdim);
     const int hpt = ssd::heads_per_tile(p->headdim);
     l.tpg = (int)((H / G + hpt - 1) / hpt);
-    const size_t K = fused ? (nc + 1 < (size_t)kRingSlots ? nc + 1 : (size_t)kRingSlots) : nc + 1;
+    // fused: one state slot per chain, updated in place; relay form: the initial and the final
+    // state (the states in between go through its operand ring)
+    const bool relay = relay_capable(p);
+    const size_t K = fused ? (relay ? 2 : 1) : nc + 1;
     ssd_workspace_layout_t& w = l.w;
     w.nchunks = (int)nc;
     w.state_slots = (int)K;
@@ -97,9 +123,13 @@ Layout layout(const ssd_params_t* p) {
     w.acs_bytes = w.dt_bytes;
     const size_t PS = fused ? pair_slots_max(p) : 0;
     w.cb_bytes = (fused ? PS : B * G) * nc * Q * Q * 4;
-    w.s_bytes = fused ? 0 : B * nc * H * P * N * 4;
+    // relay form: the chunk-state ring (fp32) and then the operand ring (input dtype)
+    l.op_slots = (int)(nc + 1 < (size_t)ssd::kRelaySlots ? nc + 1 : (size_t)ssd::kRelaySlots);
+    l.agg_bytes = B * H * P * N * 4 * ssd::kAggSlots;
+    w.s_bytes = fused ? (relay ? l.agg_bytes + B * H * P * N * elem_size(p->in_dtype) * l.op_slots : 0)
+                      : B * nc * H * P * N * 4;
     w.states_bytes = B * K * H * P * N * elem_size(p->state_dtype);
-    l.nflags = fused ? B * H * (size_t)l.wph * ssd::kChainCounterStride : 0;
+    l.nflags = fused ? B * H * (size_t)l.wph * ssd::kChainStride : 0;
     l.flags_w = 0;
     l.cs_w = l.nflags;
     l.bmm_w = l.cs_w + PS * nc;
@@ -151,6 +181,8 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.acs = (float*)(base + l.w.acs_offset);
     a.cb = (float*)(base + l.w.cb_offset);
     a.s = (float*)(base + l.w.s_offset);
+    a.opnd = base + l.w.s_offset + l.agg_bytes;
+    a.op_slots = l.op_slots;
     a.states = base + l.w.states_offset;
     uint32_t* sync = (uint32_t*)(base + l.w.sync_offset);
     a.flags = sync + l.flags_w;
@@ -217,7 +249,7 @@ void set_partitions(const ssd_params_t* p, const Layout& l, const DevInfo& d, ss
     a.nparts = d.nparts;
     a.cu_count = d.cus;
     a.chain_group = chain_group_env();
-    int pb = 0, maxw = 0;
+    int pb = 0, maxw = 0, maxu = 0;
     for (int x = 0; x <= d.nparts; ++x) {
         a.part_u0[x] = (int)(U * x / d.nparts);
         a.part_pb[x] = pb;
@@ -225,10 +257,17 @@ void set_partitions(const ssd_params_t* p, const Layout& l, const DevInfo& d, ss
         const int u0 = (int)(U * x / d.nparts), u1 = (int)(U * (x + 1) / d.nparts);
         const int np = u1 > u0 ? (u1 - 1) / l.tpg - u0 / l.tpg + 1 : 0;
         pb += np;
-        const int64_t work = nc * (2 * np + (u1 - u0));
+        const int64_t work = nc * (2 * np + (u1 - u0)) + 4 * (u1 - u0);
         if (work > maxw) maxw = (int)work;
+        if (u1 - u0 > maxu) maxu = u1 - u0;
     }
     a.part_max_work = maxw;
+    // The relay items (four per chain) hold one workgroup each for the whole launch: use them
+    // only while they take at most half of a partition's workgroups (two per CU) and leave
+    // room for two chunks of the partition's chunk tiles.
+    const int per_part = (d.cus / d.nparts > 0 ? d.cus / d.nparts : 1) * 2;
+    a.relay = (relay_capable(p) && 8 * maxu <= per_part && per_part - 4 * maxu >= 2 * maxu + 2) ? 1 : 0;
+    a.slots = a.relay ? l.w.state_slots : 1;
 }
 
 ssd_status_t check_ws(const ssd_params_t* p, void* ws, size_t ws_bytes, Layout* l) {
@@ -409,17 +448,17 @@ static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt
         if (e != hipSuccess) return hip_status(e);
         set_partitions(p, l, d, a);
         // initial state into the ring's slot 0; every sync word reset (chain counters to 1: the
-        // state entering chunk 0 is ready)
-        const int es = (int)elem_size(p->state_dtype), K = l.w.state_slots;
+        // state entering chunk 0 is ready -- in the relay form its relay waves publish it)
+        const int es = (int)elem_size(p->state_dtype), K = a.slots;
         e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, p->dstate, K, 0, es,
-                                  a.flags, l.nsync, l.nflags, (uint32_t)ssd::kChainCounterStride, st);
+                                  a.flags, l.nsync, l.nflags, (uint32_t)ssd::kChainStride, a.relay ? 0u : 1u, st);
         if (e == hipSuccess) e = mark(ev_begin);
         if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED, p, a, st);
         if (e == hipSuccess) e = mark(ev_end);
-        // final state out of the last chunk's slot
+        // final state out of the last chunk's slot (the relay form keeps it in slot 1)
         if (e == hipSuccess)
             e = ssd::launch_ring_copy(a.states, final_state, 0, p->batch, p->nheads, p->headdim, p->dstate, K,
-                                      l.w.nchunks % K, es, nullptr, 0, 0, 1, st);
+                                      a.relay ? 1 : l.w.nchunks % K, es, nullptr, 0, 0, 1, 0u, st);
         return hip_status(e);
     }
     e = mark(ev_begin);

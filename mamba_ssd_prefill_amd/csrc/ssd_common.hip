@@ -48,10 +48,12 @@ __global__ __launch_bounds__(256) void k_boundary(const char* src, size_t src_bs
 // Boundary copies of the fused form, between the callers' [B][H][P][N] states and the ring
 // layout (see ring_chain): to_ring = 1 copies src (or zeros) into slot `slot`, to_ring = 0
 // copies slot `slot` out to dst.  One thread per 4 consecutive n of one (b, h, p).  Also
-// resets sync words like k_boundary.
+// resets nsync sync words: word i becomes flag_init when i < nflags and i % flag_period < 4
+// (the progress counters of every chain, one per relay wave: 1 = the state entering chunk 0
+// is ready), else 0.
 __global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, int to_ring, int B, int H, int P,
                                                     int N, int K, int slot, int es, uint32_t* sync, size_t nsync,
-                                                    size_t nflags, uint32_t flag_period) {
+                                                    size_t nflags, uint32_t flag_period, uint32_t flag_init) {
     const int PW = P < 32 ? P : 32, WPH = P / PW, MBP = PW / 16, NB = N / 16;
     const size_t total = (size_t)B * H * P * (N / 4);
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -77,12 +79,12 @@ __global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, i
         }
     }
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsync; i += stride)
-        sync[i] = (i < nflags && (i % flag_period) == 0) ? 1u : 0u;
+        sync[i] = (i < nflags && (i % flag_period) < 4u) ? flag_init : 0u;
 }
 
 hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int N, int K, int slot,
                             int es, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
-                            hipStream_t st) {
+                            uint32_t flag_init, hipStream_t st) {
     const size_t work = (size_t)B * H * P * (N / 4);
     const size_t big = work > nsync ? work : nsync;
     size_t grid = (big + 255) / 256;
@@ -90,7 +92,7 @@ hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int 
     if (grid > 8192) grid = 8192;
     const char* s = (const char*)src;
     char* d = (char*)dst;
-    void* args[] = {&s, &d, &to_ring, &B, &H, &P, &N, &K, &slot, &es, &sync, &nsync, &nflags, &flag_period};
+    void* args[] = {&s, &d, &to_ring, &B, &H, &P, &N, &K, &slot, &es, &sync, &nsync, &nflags, &flag_period, &flag_init};
     return hipLaunchKernel((const void*)&k_ring_copy, dim3((unsigned)grid), dim3(256), args, 0, st);
 }
 

@@ -34,6 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -210,6 +211,19 @@ __device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) 
 // Waiters further back sleep longer between polls (s_sleep n is about 64 n cycles): a chain's
 // counter is polled by every waiting tile of the chain, and a tight loop from all of them
 // would saturate its L2 channel -- slowing the very stores it waits for.
+// Every 32nd poll of a wait: false once another wait gave up or this one has polled
+// spin_limit times (then it raises the abort and status words).
+__device__ inline bool spin_ok(uint32_t spins, const SsdArgs& a) {
+    if ((spins & 31u) != 0u) return true;
+    if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
+    if (spins > a.spin_limit) {
+        __hip_atomic_store(a.abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.status, 7u /* SSD_ERR_SYNC_TIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+    return true;
+}
+
 __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a, uint32_t target = 1u) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(f, 4);
     uint32_t spins = 0;
@@ -221,19 +235,9 @@ __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a, uint32_t t
             __builtin_amdgcn_s_sleep(127);
         else if (behind > 1u)
             __builtin_amdgcn_s_sleep(24);
-        ++spins;
-        if ((spins & 31u) == 0u) {
-            if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                ok = false;
-                break;
-            }
-            if (spins > a.spin_limit) {
-                __hip_atomic_store(a.abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.status, 7u /* SSD_ERR_SYNC_TIMEOUT */, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                ok = false;
-                break;
-            }
+        if (!spin_ok(++spins, a)) {
+            ok = false;
+            break;
         }
         __builtin_amdgcn_s_sleep(1);
     }
@@ -242,8 +246,68 @@ __device__ inline bool wait_flag(const uint32_t* f, const SsdArgs& a, uint32_t t
     return ok;
 }
 
+// wait_flag over the first n (<= 64) words at f: returns once every one is >= target.
+__device__ inline bool wait_words(const uint32_t* f, int n, const SsdArgs& a, uint32_t target) {
+    const uint32_t lane = (uint32_t)tid_here() & 63u;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(f, (uint32_t)n * 4);
+    uint32_t spins = 0;
+    bool ok = true;
+    for (;;) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, 0, AUX_L2);
+        const unsigned long long low = __ballot(lane < (uint32_t)n && v < target);
+        if (low == 0ull) break;
+        const uint32_t behind = target - __builtin_amdgcn_readlane(v, __builtin_ctzll(low));
+        if (behind > 3u)
+            __builtin_amdgcn_s_sleep(127);
+        else if (behind > 1u)
+            __builtin_amdgcn_s_sleep(24);
+        if (!spin_ok(++spins, a)) {
+            ok = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return ok;
+}
+
+// A row of per-slot words (at most 32, one 128-byte line), one slot per item modulo `slots`:
+// the number of consecutive items base, base + 1, ... (at most `slots`) whose slot word w
+// has w + bias >= item + 1.  One sc1 load per lane; the result is wave-uniform.
+__device__ inline int ready_run(const uint32_t* row, int slots, uint32_t base, uint32_t bias) {
+    const uint32_t lane = (uint32_t)tid_here() & 63u;
+    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(row, (uint32_t)slots * 4), lane * 4, 0, AUX_L2);
+    const uint32_t s0 = base % (uint32_t)slots;
+    const uint32_t k = (lane + (uint32_t)slots - s0) % (uint32_t)slots;  // item base + k lives in slot `lane`
+    const unsigned long long bad = __ballot(lane < (uint32_t)slots && v + bias < base + k + 1u);
+    const unsigned long long all = (1ull << slots) - 1ull;
+    const unsigned long long rot = ((bad >> s0) | (bad << ((uint32_t)slots - s0))) & all;  // bit k: item base + k
+    return rot ? __builtin_ctzll(rot) : slots;
+}
+
+// Polls ready_run until it is positive; bounded like wait_flag (0 when the wait gave up).
+__device__ inline int wait_run(const uint32_t* row, int slots, uint32_t base, uint32_t bias, const SsdArgs& a) {
+    uint32_t spins = 0;
+    for (;;) {
+        const int n = ready_run(row, slots, base, bias);
+        if (n > 0) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            return n;
+        }
+        if (!spin_ok(++spins, a)) return 0;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 // s_waitcnt vmcnt(0): every global load and store this wave issued has completed.
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt vmcnt(n): at most the n most recent global loads / stores of this wave are still
+// pending (vector memory operations complete in issue order; vmcnt is bits [3:0] and [15:14]).
+template <int n> __device__ inline void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
 
 // Workgroup barrier for LDS hand-offs only: this wave's LDS accesses have completed
 // (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() (whose workgroup fence waits for
@@ -270,7 +334,7 @@ __device__ inline void publish_flag_wave(uint32_t* f, uint32_t v = 1u) {
 // with cold data, or a first store that allocates a partial line, makes the next sc1 read
 // go to memory).  Value v: the states entering chunks 0 .. v-1 are published.
 __device__ inline uint32_t* chain_counter(const SsdArgs& a, int b, int h, int ph, int WPH) {
-    return a.flags + (((size_t)b * a.nheads + h) * WPH + ph) * kChainCounterStride;
+    return a.flags + (((size_t)b * a.nheads + h) * WPH + ph) * kChainStride;
 }
 
 // Whole workgroup: every wave's stores have reached the L2, then thread 0 sets *f.
@@ -281,14 +345,14 @@ __device__ inline void publish_flag_block(uint32_t* f) {
 }
 
 // ---- the fused form's inter-chunk state ring -----------------------------------------------
-// Slot layout: for every (b, slot, h, p-slice ph) the owning wave's accumulator tiles follow
+// Slot layout: for every (b, h, p-slice ph, slot) the owning wave's accumulator tiles follow
 // each other, lane after lane: element e of tile t held by lane l sits at
 // ring_chain(b, slot, h, ph) + (t * 64 + l) * 4 + e, where tile t = nb * MBP + pb covers
 // S[p = ph*PW + pb*16 + (l & 15)][n = nb*16 + 4*(l >> 4) + e].  Each lane therefore moves one
 // contiguous 16-byte (fp32) or 8-byte (16-bit) piece and a wave moves 1 KB / 512 B at once.
 // The boundary copies convert between this layout and the callers' [P][N] layout.
 __device__ inline size_t ring_chain(int b, int slot, int h, int ph, int K, int H, int WPH, int tiles) {
-    return ((((size_t)b * K + slot) * H + h) * WPH + ph) * (size_t)tiles * 256;
+    return ((((size_t)b * H + h) * WPH + ph) * K + slot) * (size_t)tiles * 256;
 }
 
 // Load (sc1: from the XCD's L2) / plain store of one lane's 4 ring elements at element offset
@@ -322,6 +386,217 @@ __device__ inline void ring_store(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t 
         const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off * 2, 0, 0);
     }
+}
+
+// ---- the relay form of the fused state passing ---------------------------------------------
+// With few chains per XCD the chunk-to-chunk hop inside the chunk tiles (each tile reads S_c,
+// writes S_{c+1} and releases the next tile) bounds the whole launch: its latency is paid once
+// per chunk, in series, and one wave issues a vector memory instruction only every few tens of
+// nanoseconds, so moving a wave's 16 KB of state costs microseconds.  The relay form gives every
+// chain (b, h, p-slice) a dedicated state-passing item whose relay waves each keep a share of S
+// (whole accumulator tiles) in fp32 registers and stream the chunk states through:
+//   chunk tile c:  s_c -> chunk-state ring slot c % kAggSlots (fp32), slot word = c + 1; wait
+//                  until every relay wave's counter >= c + 1, read S_c (operand type) from
+//                  operand slot c % op_slots, read word = c + 1
+//   relay wave:    for c = 0, 1, ...: S_{c+1} = exp(acs_c[Q-1]) S_c + s_c (its tiles) -> operand
+//                  slot (c + 1) % op_slots, its counter = c + 2 once stored; first S_0 (from
+//                  state ring slot 0) -> operand slot 0, counter = 1; at the end S_nc in the
+//                  state dtype -> state ring slot 1
+// The tiles read S_c only as an MFMA operand, so the relay hands it over already rounded to
+// the operand type (half the bytes and instructions of fp32).  A chunk tile overwrites its
+// chunk-state slot only after every relay wave has used the previous occupant (counters >=
+// c - kAggSlots + 2); a relay wave overwrites an operand slot only after the tile that read the
+// previous occupant said so (read word).  A relay wave loads s_{c+1} while s_c is being folded
+// in and publishes S_c one chunk later, once its stores are known complete.  Both rings keep
+// each lane's 16-byte pieces contiguous (see ring_chain): a chunk-state slot holds the NT
+// accumulator tiles as fp32, an operand slot holds them in units of 16 / (4 sizeof(T)) tiles.
+constexpr int kRelayWaves = 4;
+
+template <typename T> constexpr int tiles_per_unit() { return sizeof(T) == 2 ? 2 : 1; }
+
+// Relay waves of a chain whose chunk-tile wave holds NT accumulator tiles: each relay wave
+// takes the same number of whole operand units.
+template <typename T, int NT> constexpr int relay_waves() {
+    return NT / tiles_per_unit<T>() < kRelayWaves ? NT / tiles_per_unit<T>() : kRelayWaves;
+}
+
+__device__ inline size_t chain_index(const SsdArgs& a, int b, int h, int ph, int WPH) {
+    return ((size_t)b * a.nheads + h) * WPH + ph;
+}
+
+// The chunk-state ring slot of chain (b, h, ph): NT accumulator tiles of 64 lanes x 4 floats.
+template <int NT> __device__ inline __amdgpu_buffer_rsrc_t agg_rsrc(const SsdArgs& a, int b, int h, int ph, int WPH,
+                                                                     int slot) {
+    const size_t chain = chain_index(a, b, h, ph, WPH) * kAggSlots + slot;
+    return make_rsrc(a.s + chain * NT * 256, NT * 256 * 4);
+}
+
+// The operand ring slot of chain (b, h, ph): NT tiles of 64 lanes x 4 elements of T.
+template <typename T, int NT>
+__device__ inline __amdgpu_buffer_rsrc_t opnd_rsrc(const SsdArgs& a, int b, int h, int ph, int WPH, int slot) {
+    const size_t chain = chain_index(a, b, h, ph, WPH) * a.op_slots + slot;
+    return make_rsrc((const T*)a.opnd + chain * NT * 256, NT * 256 * sizeof(T));
+}
+
+// 16 bytes of operand ring: tiles u * TPU .. u * TPU + TPU - 1 of one lane, rounded to T.
+template <typename T> __device__ inline u32x4 pack_unit(const f32x4* v) {
+    if constexpr (sizeof(T) == 2) {
+        typedef typename TT<T>::v4 v4;
+        const v4 lo = cvt4<T>(v[0]), hi = cvt4<T>(v[1]);
+        return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+        return __builtin_bit_cast(u32x4, v[0]);
+    }
+}
+
+// Relay wave w of chain (b, h, ph): the state passing of tiles [w * TPW, (w + 1) * TPW) of the
+// chain's NT accumulator tiles, over every chunk.
+template <typename T, int NT> __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int w) {
+    constexpr int TPU = tiles_per_unit<T>(), TPW = NT / relay_waves<T, NT>();
+    static_assert(TPW % TPU == 0, "a relay wave holds whole operand units");
+    const uint32_t lane = (uint32_t)tid_here() & 63u;
+    const int H = a.nheads, nc = a.nchunks, Q = a.chunk, K = a.slots, KO = a.op_slots, sdt = a.state_dtype;
+    uint32_t* cnt = chain_counter(a, b, h, ph, WPH);
+    uint32_t* my_cnt = cnt + w;
+    const uint32_t* agg_words = cnt + kChainAggWords;
+    const uint32_t* read_words = cnt + kChainReadWords;
+    const uint32_t t0 = (uint32_t)(w * TPW);
+    f32x4 S[TPW], B0[TPW], B1[TPW];
+    float d0 = 0.f, d1 = 0.f;
+    {
+        const __amdgpu_buffer_rsrc_t r = ring_rsrc(a.states, sdt, ring_chain(b, 0, h, ph, K, H, WPH, NT), NT);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) S[t] = ring_load(r, sdt, ((t0 + t) * 64 + lane) * 4);
+        // S_0 into operand slot 0, then published (the counters start at 0 in this form)
+        const __amdgpu_buffer_rsrc_t ro = opnd_rsrc<T, NT>(a, b, h, ph, WPH, 0);
+#pragma unroll
+        for (int u = 0; u < TPW / TPU; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(pack_unit<T>(&S[u * TPU]), ro, ((t0 / TPU + u) * 64 + lane) * 16, 0, 0);
+        publish_flag_wave(my_cnt, 1u);
+    }
+    int agg_hi = 0;  // chunk states 0 .. agg_hi - 1 are known to be in their slots
+    int wr_hi = 0;   // states 0 .. wr_hi - 1 are known to be free to write
+    // L(c): TPW loads of s_c and one of acs_c[Q-1], into buf / d
+    auto issue_load = [&](int c, f32x4 (&buf)[TPW], float& d) {
+        const __amdgpu_buffer_rsrc_t r = agg_rsrc<NT>(a, b, h, ph, WPH, c % kAggSlots);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) buf[t] = bload_f32x4<AUX_L2>(r, ((t0 + t) * 64 + lane) * 16);
+        d = bload_f32<AUX_L2>(make_rsrc(a.acs + (((size_t)b * nc + c) * H + h) * Q, (uint32_t)Q * 4),
+                              (uint32_t)(Q - 1) * 4);
+    };
+    // Step c: issue L(c + 1) if s_{c+1} is known to be ready, wait for L(c), publish S_{c-1},
+    // else wait for s_{c+1} and issue L(c + 1) now; fold s_c in; store S_{c+1} (St(c + 1),
+    // TPW / TPU stores).  Issue order: ... L(c), St(c), L(c + 1), St(c + 1) ...: once at most
+    // |St(c)| + |L(c + 1)| operations are pending (|St(c)| alone if L(c + 1) is not issued yet),
+    // L(c) and everything before it (St(c - 1) too) are complete.  Any extra operation in
+    // between (a poll, a flag) only makes the count wait for more.
+    constexpr int NST = TPW / TPU, NLD = TPW + 1;
+    auto step = [&](int c, f32x4 (&cur)[TPW], float dcur, f32x4 (&nxt)[TPW], float& dnxt) -> bool {
+        const bool has_next = c + 1 < nc;
+        const bool early = has_next && c + 1 < agg_hi;
+        if (early) issue_load(c + 1, nxt, dnxt);
+        asm volatile("" ::: "memory");
+        if (early) {
+            if (c >= 1)
+                wait_vm<NST + NLD>();
+            else
+                wait_vm<NLD>();
+        } else {
+            if (c >= 1)
+                wait_vm<NST>();
+            else
+                wait_vm<0>();
+        }
+        asm volatile("" ::: "memory");
+        if (c >= 2) raise_flag(my_cnt, (uint32_t)c);  // states entering chunks 0 .. c-1 are stored
+        if (has_next && !early) {
+            const int n = wait_run(agg_words, kAggSlots, (uint32_t)c + 1, 0u, a);
+            if (n == 0) return false;
+            agg_hi = c + 1 + n;
+            asm volatile("" ::: "memory");
+            issue_load(c + 1, nxt, dnxt);
+            asm volatile("" ::: "memory");
+        }
+        const float dec = __expf(dcur);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) S[t] = dec * S[t] + cur[t];
+        const int m = c + 1;  // the state written now
+        if (m >= wr_hi) {
+            // slot m % KO last held S_{m-KO}: its reader must be done (bias KO: always true for m < KO)
+            const int n = wait_run(read_words, KO, (uint32_t)m, (uint32_t)KO, a);
+            if (n == 0) return false;
+            wr_hi = m + n;
+        }
+        asm volatile("" ::: "memory");
+        const __amdgpu_buffer_rsrc_t r = opnd_rsrc<T, NT>(a, b, h, ph, WPH, m % KO);
+#pragma unroll
+        for (int u = 0; u < NST; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(pack_unit<T>(&S[u * TPU]), r,
+                                                   ((t0 / TPU + u) * 64 + lane) * 16, 0, 0);
+        asm volatile("" ::: "memory");
+        return true;
+    };
+    bool ok = true;
+    {
+        const int n = wait_run(agg_words, kAggSlots, 0u, 0u, a);
+        ok = n > 0;
+        agg_hi = n;
+    }
+    if (ok) issue_load(0, B0, d0);
+    for (int c = 0; ok && c < nc; c += 2) {
+        ok = step(c, B0, d0, B1, d1);
+        if (ok && c + 1 < nc) ok = step(c + 1, B1, d1, B0, d0);
+    }
+    // the final state, in the state dtype, for the boundary copy
+    const __amdgpu_buffer_rsrc_t rf = ring_rsrc(a.states, sdt, ring_chain(b, 1, h, ph, K, H, WPH, NT), NT);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) ring_store(rf, sdt, ((t0 + t) * 64 + lane) * 4, S[t]);
+    wait_vm_all();
+    if (ok) raise_flag(my_cnt, (uint32_t)nc + 1);
+}
+
+// Relay form, chunk tile side: hand this wave's chunk state s_c (accumulator tiles) to the
+// chain's relay waves, then read S_c (operand type) into sv.  False when a wait gave up.
+template <typename T, int NB, int MBP>
+__device__ inline bool relay_handoff(const SsdArgs& a, int b, int c, int h, int ph, int WPH,
+                                     const f32x4 (&acc)[NB][MBP], typename TT<T>::v4 (&sv)[NB][MBP]) {
+    constexpr int NT = NB * MBP, RW = relay_waves<T, NT>(), TPU = tiles_per_unit<T>();
+    typedef typename TT<T>::v4 v4;
+    const uint32_t lane = (uint32_t)tid_here() & 63u;
+    uint32_t* cnt = chain_counter(a, b, h, ph, WPH);
+    // the slot's previous chunk state (chunk c - kAggSlots) has been folded in
+    bool ok = c < kAggSlots || wait_words(cnt, RW, a, (uint32_t)(c - kAggSlots) + 2u);
+    const __amdgpu_buffer_rsrc_t ra = agg_rsrc<NT>(a, b, h, ph, WPH, c % kAggSlots);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int pb = 0; pb < MBP; ++pb)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[nb][pb]), ra,
+                                                   ((uint32_t)(nb * MBP + pb) * 64 + lane) * 16, 0, 0);
+    publish_flag_wave(cnt + kChainAggWords + c % kAggSlots, (uint32_t)c + 1);
+    ok = wait_words(cnt, RW, a, (uint32_t)c + 1) && ok;
+    const int KO = a.op_slots;
+    const __amdgpu_buffer_rsrc_t rin = opnd_rsrc<T, NT>(a, b, h, ph, WPH, c % KO);
+    v4 unit[NT];
+#pragma unroll
+    for (int u = 0; u < NT / TPU; ++u) {
+        const u32x4 w = __builtin_bit_cast(u32x4, bload_f32x4<AUX_L2>(rin, ((uint32_t)u * 64 + lane) * 16));
+        if constexpr (TPU == 2) {
+            typedef typename TT<T>::frag frag;
+            const frag f = __builtin_bit_cast(frag, w);
+            unit[2 * u] = __builtin_shufflevector(f, f, 0, 1, 2, 3);
+            unit[2 * u + 1] = __builtin_shufflevector(f, f, 4, 5, 6, 7);
+        } else {
+            unit[u] = __builtin_bit_cast(v4, w);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int pb = 0; pb < MBP; ++pb) sv[nb][pb] = unit[nb * MBP + pb];
+    wait_vm_all();
+    raise_flag(cnt + kChainReadWords + c % KO, (uint32_t)c + 1);
+    return ok;
 }
 
 // ---- step 1: chunk_cumsum ([KF] item 4; [HW] segsum section: decay in log space) ------
@@ -567,6 +842,9 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                     }
             }
             return;
+        } else if (a.relay) {
+            // relay form: s_c to the chain's relay item, S_c back
+            if (hvalid) relay_handoff<T, NB, MBP>(a, b, c, h, ph, WPH, acc, sc);
         } else {
             // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c
             if (hvalid) {

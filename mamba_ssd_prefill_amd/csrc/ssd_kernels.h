@@ -63,17 +63,22 @@ template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds_
 // (b, g), and bmm tiles (pair, c) into its own CB slots.  Its queue, in claim order:
 //   [0, np*nc)             cumsum tiles, chunk-major
 //   [np*nc, 2*np*nc)       bmm tiles, chunk-major
-//   [2*np*nc, +nu*nc)      chunk tiles: the chains in groups of chain_group, one group after
+//   [2*np*nc, +4*nu)       relay form only: one relay item per chain part, i.e. per wave of the
+//                          chain's chunk tiles (see relay_chain)
+//   [first_chunk, +nu*nc)  chunk tiles: the chains in groups of chain_group, one group after
 //                          the other, chunk-major inside a group (so only one group's state
 //                          slots need to stay in the L2 at a time)
 // Workgroups are persistent: each reads the id of the XCD it runs on, takes tickets from that
 // partition's queue until it is empty, then leaves.  So every hand-off of a partition stays in
 // one L2 (see the coherence notes in ssd_device.h).  A chunk tile waits only on work with
 // smaller tickets of its own queue (its cumsum and bmm tiles and the previous chunk's tile of
-// its chains), claimed by workgroups that are running, so every wait ends.
+// its chains, or its chain's relay item), claimed by workgroups that are running, so every
+// wait ends.  A relay item waits on chunk tiles with larger tickets: the relay form is used
+// only when a partition has far more workgroups than chains (set at launch), so those tiles
+// are claimed by other workgroups while the relay items run.
 struct FusedPart {
     int u0, nu, p0, np, pb;
-    uint32_t n_cs, n_total;
+    uint32_t n_cs, first_chunk, n_total;
 };
 
 __device__ inline FusedPart fused_part(const SsdArgs& a, int x) {
@@ -84,7 +89,8 @@ __device__ inline FusedPart fused_part(const SsdArgs& a, int x) {
     f.np = f.nu > 0 ? (f.u0 + f.nu - 1) / a.tpg - f.p0 + 1 : 0;
     f.pb = a.part_pb[x];
     f.n_cs = (uint32_t)f.np * a.nchunks;
-    f.n_total = 2 * f.n_cs + (uint32_t)f.nu * a.nchunks;
+    f.first_chunk = 2 * f.n_cs + (a.relay ? 4u * (uint32_t)f.nu : 0u);  // 4 waves = parts per chunk tile
+    f.n_total = f.first_chunk + (uint32_t)f.nu * a.nchunks;
     return f;
 }
 
@@ -101,7 +107,7 @@ __device__ inline const SsdArgs& fresh_args(const SsdArgs& a) {
     return *(const SsdArgs*)((const char*)&a + zero);
 }
 
-// The chain and chunk of chunk ticket t (t >= 2 * n_cs of partition f): the chains are taken
+// The chain and chunk of chunk ticket t (t >= first_chunk of partition f): the chains are taken
 // in groups of chain_group, one group after the other, chunk-major inside a group.
 struct ChunkItem {
     int b, c, g, tig;
@@ -109,7 +115,7 @@ struct ChunkItem {
 };
 __device__ inline ChunkItem chunk_item(const SsdArgs& a, const FusedPart& f, uint32_t t) {
     const int nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
-    const uint32_t v = t - 2 * f.n_cs;
+    const uint32_t v = t - f.first_chunk;
     const int cg = a.chain_group < f.nu ? a.chain_group : f.nu;
     const uint32_t per_group = (uint32_t)cg * nc;
     const int grp = v / per_group;
@@ -143,7 +149,7 @@ template <int HPT, int P> struct PrefetchHook {
     }
     __device__ inline uint32_t touch() const {
         const uint32_t tn = __builtin_amdgcn_readfirstlane(*s_next);
-        if (tn < 2 * f.n_cs || tn >= f.n_total) return 0u;
+        if (tn < f.first_chunk || tn >= f.n_total) return 0u;
         const ChunkItem it = chunk_item(a, f, tn);
         const int L = a.seqlen, H = a.nheads, Q = a.chunk, hpg = a.hpg;
         const int tok0 = it.c * Q, valid = L - tok0 < Q ? L - tok0 : Q;
@@ -205,6 +211,15 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                 bmm_tile<T, N>(a, b, c, g, a.cb + slot * Q * Q);
                 publish_flag_block(a.bmm_done + slot);
             }
+        } else if (t < f.first_chunk) {
+            // relay item of chain u's part (head hs, p-slice ph) = its tile's wave `part`
+            constexpr int PW = P < 32 ? P : 32, WPH = P / PW, NT = (N / 16) * (PW / 16);
+            const uint32_t r = t - 2 * f.n_cs;
+            const int u = f.u0 + (int)(r / 4), part = (int)(r % 4), pair = u / tpg, tig = u % tpg;
+            const int hs = part / WPH, ph = part % WPH;
+            const int wave = __builtin_amdgcn_readfirstlane(tid_here() >> 6);
+            if (tig * HPT + hs < hpg && wave < relay_waves<T, NT>())
+                relay_chain<T, NT>(a, pair / Gn, (pair % Gn) * hpg + tig * HPT + hs, ph, WPH, wave);
         } else {
             const ChunkItem it = chunk_item(a, f, t);
             if (threadIdx.x == 0) {

@@ -24,9 +24,10 @@ struct SsdArgs {
     float* dtf;          // [B][nc][H][Q]
     float* acs;          // [B][nc][H][Q]
     float* cb;           // unfused: [B][nc][G][Q][Q]; fused: [pair slot][nc][Q][Q]
-    float* s;            // [B][nc][H][P][N] (unfused form)
-    void* states;        // unfused: [B][K][H][P][N]; fused: one ring slot per chain
-    uint32_t* flags;     // fused: per-chain progress counters [B][H][WPH], 32 words apart
+    float* s;            // unfused: [B][nc][H][P][N]; fused relay form: the chunk-state ring
+    void* states;        // unfused: [B][K][H][P][N]; fused: K ring slots per chain
+    void* opnd;          // fused relay form: S_c in the operand type, op_slots slots per chain
+    uint32_t* flags;     // fused: per-chain words [B][H][WPH], kChainStride words apart
     uint32_t* cs_done;   // fused: [pair slot][nc]
     uint32_t* bmm_done;  // fused: [pair slot][nc]
     uint32_t* ticket;    // fused: one work counter per partition, kTicketStride words apart
@@ -34,7 +35,7 @@ struct SsdArgs {
     uint32_t* exit_count;
     uint32_t* abort_word;
     uint32_t* status;
-    int batch, seqlen, nheads, ngroups, chunk, nchunks, hpg, tpg, slots;
+    int batch, seqlen, nheads, ngroups, chunk, nchunks, hpg, tpg, slots, op_slots;
     int state_dtype, softplus;
     uint32_t spin_limit;
     // fused form: the chains (b, g, tile-in-group), numbered u = (b * G + g) * tpg + tig, are
@@ -45,12 +46,21 @@ struct SsdArgs {
     int part_u0[kMaxXcc + 1];
     int part_pb[kMaxXcc + 1];
     int chain_group;    // chains whose chunk tiles are claimed together (0: set at launch)
+    int relay;          // fused form: 1 = dedicated state-passing items (see relay_chain)
     int part_max_work;  // host only: the longest partition queue
     int cu_count;       // host only: compute units of the device
 };
 
-constexpr int kTicketStride = 32;        // one 128-byte line per partition counter
-constexpr int kChainCounterStride = 32;  // one 128-byte line per chain progress counter
+constexpr int kTicketStride = 32;  // one 128-byte line per partition counter
+// Fused form, per chain (b, h, p-slice): three 128-byte lines of sync words -- the progress
+// counter, then (relay form) the chunk-state slot words and the state read words.
+constexpr int kChainStride = 96;
+constexpr int kChainAggWords = 32;
+constexpr int kChainReadWords = 64;
+// Relay form: operand ring slots and chunk-state ring slots per chain (each at most 32, one
+// line of slot words).  Its state ring has two slots: the initial state and the final one.
+constexpr int kRelaySlots = 16;
+constexpr int kAggSlots = 32;
 
 enum : int {
     STEP_CUMSUM = 0,
@@ -83,7 +93,7 @@ hipError_t launch_step_bf16_q256(int step, int P, int N, SsdArgs& a, hipStream_t
 hipError_t launch_state_passing(SsdArgs& a, int PN, hipStream_t st);
 hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int N, int K, int slot,
                             int es, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
-                            hipStream_t st);
+                            uint32_t flag_init, hipStream_t st);
 hipError_t launch_boundary(const void* src, size_t src_bs, void* dst, size_t dst_bs, size_t bytes_per_b,
                            int batch, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
                            hipStream_t st);

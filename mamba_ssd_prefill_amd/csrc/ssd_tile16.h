@@ -370,7 +370,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     // not used (the state may not be written yet).
     uint32_t pf0 = 0, pf1 = 0;
     if constexpr (MODE == MODE_FUSED) {
-        if (hvalid) {
+        if (hvalid && !a.relay) {
             const int K = a.slots;
             const __amdgpu_buffer_rsrc_t rpf =
                 ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
@@ -443,8 +443,11 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             else if constexpr (CB_LDS)
                 dma_cb_bands<Q, CB_AUX>(sCB, cbp);
             hook.claim();
-            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c, in place in the chain's slot
-            if (hvalid) {
+            if (a.relay) {
+                // relay form: s_c to the chain's relay item, S_c back
+                if (hvalid) relay_handoff<T, NB, MBP>(a, b, c, h, ph, WPH, acc, scb);
+            } else if (hvalid) {
+                // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c, in place in the chain's slot
                 uint32_t* fl = chain_counter(a, b, h, ph, WPH);
                 wait_flag(fl, a, (uint32_t)c + 1);
                 asm volatile("" ::"v"(pf0), "v"(pf1));  // the touch loads are complete (long ago)

@@ -1,4 +1,6 @@
 """Helpers shared by the GPU parity tests: run the HIP path, compare with the oracle."""
+import contextlib
+import os
 import sys
 
 import numpy as np
@@ -26,8 +28,29 @@ def say(*a):
 _STATE_CODE = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 
 
+@contextlib.contextmanager
+def fused_form(impl):
+    """impl "fused_hop" / "fused_relay": the fused form with the chunk tiles' own state hop /
+    with relay items (MAMBA_SSD_RELAY = 0 / 1); "fused" and "unfused" leave the choice to the
+    library.  Yields the impl name the binding takes."""
+    old = os.environ.pop("MAMBA_SSD_RELAY", None)
+    if impl in ("fused_hop", "fused_relay"):
+        os.environ["MAMBA_SSD_RELAY"] = "1" if impl == "fused_relay" else "0"
+    try:
+        yield "fused" if impl.startswith("fused") else impl
+    finally:
+        os.environ.pop("MAMBA_SSD_RELAY", None)
+        if old is not None:
+            os.environ["MAMBA_SSD_RELAY"] = old
+
+
 def run_gpu(inp, chunk_size, impl, state_dtype=None, dev="cuda:0"):
     """One ssd_prefill on the GPU; also requires the device status word to read SSD_OK."""
+    with fused_form(impl) as name:
+        return _run_gpu(inp, chunk_size, name, state_dtype, dev)
+
+
+def _run_gpu(inp, chunk_size, impl, state_dtype, dev):
     g = inp.to(dev)
     if state_dtype is None:
         state_dtype = g.h0.dtype if g.h0 is not None else torch.float32

@@ -91,21 +91,28 @@ def test_validate_rejects_ticket_overflow(lib):
 
 @pytest.mark.parametrize("impl", ["fused", "unfused"])
 @pytest.mark.parametrize("state", ["f32", "f16"])
-def test_workspace_layout_arithmetic(lib, impl, state):
+@pytest.mark.parametrize("relay", ["0", "1", ""])
+def test_workspace_layout_arithmetic(lib, impl, state, relay, monkeypatch):
+    monkeypatch.setenv("MAMBA_SSD_RELAY", relay)
     p = base(impl=impl, state_dtype=state)
     lay = ssd.workspace_layout(p)
     Bt, L, H, P, N, G, Q = 2, 300, 8, 64, 128, 2, 128
     nc = -(-L // Q)
     es = 4 if state == "f32" else 2
     fused = impl == "fused"
+    # the relay form's buffers: forced on or off, else by shape (8 chains here: on)
+    relay_ws = fused and relay != "0"
     assert lay.nchunks == nc
-    K = 1 if fused else nc + 1
+    K = (2 if relay_ws else 1) if fused else nc + 1
     assert lay.state_slots == K
     assert lay.dt_bytes == Bt * nc * H * Q * 4 == lay.acs_bytes
     # fused: one CB run per (partition, (b, g) pair); at most B*G + 7 with up to 8 partitions
     pair_slots = Bt * G + 7
     assert lay.cb_bytes == (pair_slots if fused else Bt * G) * nc * Q * Q * 4
-    assert lay.s_bytes == (0 if fused else Bt * nc * H * P * N * 4)
+    # fused relay form: a 32-slot fp32 chunk-state ring and a min(16, nc + 1)-slot operand ring
+    # (input dtype, bf16 here) per chain
+    relay_bytes = Bt * H * P * N * (4 * 32 + 2 * min(16, nc + 1))
+    assert lay.s_bytes == ((relay_bytes if relay_ws else 0) if fused else Bt * nc * H * P * N * 4)
     assert lay.states_bytes == Bt * K * H * P * N * es
     regions = sorted([(lay.dt_offset, lay.dt_bytes), (lay.acs_offset, lay.acs_bytes), (lay.cb_offset, lay.cb_bytes),
                       (lay.s_offset, lay.s_bytes), (lay.states_offset, lay.states_bytes),
@@ -116,9 +123,10 @@ def test_workspace_layout_arithmetic(lib, impl, state):
     assert lay.total_bytes >= lay.sync_offset + lay.sync_bytes
     assert ssd.workspace_size(p) == lay.total_bytes
     if fused:
-        # chain counters [B][H][P/32] 32 words apart, cs_done and bmm_done [pair slots][nc],
-        # 8 partition tickets 32 words apart, 8 owner words, exit counter, abort, status
-        assert lay.sync_bytes == 4 * (Bt * H * 2 * 32 + 2 * pair_slots * nc + 8 * 32 + 8 + 3)
+        # per-chain words [B][H][P/32] (three 128-byte lines each), cs_done and bmm_done
+        # [pair slots][nc], 8 partition tickets 32 words apart, 8 owner words, exit counter,
+        # abort, status
+        assert lay.sync_bytes == 4 * (Bt * H * 2 * 96 + 2 * pair_slots * nc + 8 * 32 + 8 + 3)
     else:
         assert lay.sync_bytes == 8  # abort and status words
 

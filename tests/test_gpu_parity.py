@@ -23,7 +23,8 @@ def dev():
     return require_gpu()
 
 
-IMPLS = ["unfused", "fused"]
+# the fused form both with the chunk tiles' own state hop and with relay items
+IMPLS = ["unfused", "fused_hop", "fused_relay"]
 
 
 @pytest.mark.parametrize("impl", IMPLS)
@@ -122,10 +123,11 @@ def test_zero_step_keeps_state(impl):
     check_full(inp, y, fin, "dt0")
 
 
-def test_fused_is_deterministic_and_matches_unfused():
+@pytest.mark.parametrize("form", ["fused_hop", "fused_relay"])
+def test_fused_is_deterministic_and_matches_unfused(form):
     inp = make_inputs(2, 1000, 8, 64, 128, 2, dtype="bf16", has_h0=True, seed=9)
-    y1, f1 = run_gpu(inp, 128, "fused")
-    y2, f2 = run_gpu(inp, 128, "fused")
+    y1, f1 = run_gpu(inp, 128, form)
+    y2, f2 = run_gpu(inp, 128, form)
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
     yu, fu = run_gpu(inp, 128, "unfused")
     # both evaluate the same arithmetic per tile; only the state chain's rounding differs

@@ -29,7 +29,9 @@ def inputs_for(name):
     return _cache[name]
 
 
-@pytest.mark.parametrize("impl", ["fused", "unfused"])
+# "fused" is the form the library picks (relay items here and for the long contexts); the
+# chunk tiles' own hop is covered at these sizes too
+@pytest.mark.parametrize("impl", ["fused", "fused_hop", "unfused"])
 def test_mamba2_130m_full(impl):
     w = WORKLOADS["mamba2_130m_f16"]
     inp = inputs_for(w.name)
@@ -62,8 +64,9 @@ def test_short_g8_sampled(impl):
     check_sampled(inp, y, fin, [(0, 0), (31, 127), (9, 16), (17, 15), (20, 100)], w.name + " " + impl)
 
 
-@pytest.mark.parametrize("name", ["long_131k_f16", "long_262k_f16"])
-@pytest.mark.parametrize("impl", ["fused", "unfused"])
+@pytest.mark.parametrize("name,impl", [("long_131k_f16", "fused"), ("long_131k_f16", "fused_hop"),
+                                       ("long_131k_f16", "unfused"), ("long_262k_f16", "fused"),
+                                       ("long_262k_f16", "unfused")])
 def test_long_context_sampled(name, impl):
     w = WORKLOADS[name]
     inp = inputs_for(name)
