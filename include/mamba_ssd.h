@@ -159,11 +159,12 @@ const char* ssd_status_string(ssd_status_t s);
  * The fused form splits its work into one partition per XCD of the device (at most 8);
  * the sizes above are bounds that hold for any such split.  Shapes with at most 128
  * chains (batch * ngroups * ceil(heads per group / heads per tile); 4 heads per tile
- * for headdim <= 32, 2 for 64, 1 for 128) get the buffers of the fused relay form, in which a
- * dedicated work item per chain passes the state from chunk to chunk (used when every
- * partition has at least four workgroups per chain).  The environment variable
- * MAMBA_SSD_RELAY = 0 / 1 forces the buffers off / on; it is read on every call, so
- * workspace sizing and the call must see the same value.
+ * for headdim <= 32, 2 for 64, 1 for 128) get the buffers of the fused relay form, in which
+ * dedicated work items (2 or 4 per chain) pass the state from chunk to chunk; it is used
+ * when they take at most half of every partition's workgroups.  The environment variable
+ * MAMBA_SSD_RELAY = 0 / 1 forces the buffers off / on (2 / 4: on, with that many items per
+ * chain); it is read on every call, so workspace sizing and the call must see the same
+ * value.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
     size_t total_bytes;

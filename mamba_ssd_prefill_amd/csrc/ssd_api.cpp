@@ -45,12 +45,13 @@ int chain_group_env() {
     return v;
 }
 
-// MAMBA_SSD_RELAY: "0" never uses the fused relay form, "1" uses it whenever a partition has
-// enough workgroups; unset: by shape (kRelayMaxChains).  Read on every call.
+// MAMBA_SSD_RELAY: "0" never uses the fused relay form; "1" uses it whenever a partition has
+// enough workgroups, "2" / "4" also fix its relay waves per chain part; unset: by shape
+// (kRelayMaxChains).  Read on every call.
 int relay_env() {
     const char* e = getenv("MAMBA_SSD_RELAY");
     if (!e || !*e) return -1;
-    return e[0] == '0' ? 0 : 1;
+    return e[0] == '0' ? 0 : (e[0] == '2' ? 2 : (e[0] == '4' ? 4 : 1));
 }
 
 int64_t chain_count(const ssd_params_t* p) {
@@ -62,7 +63,7 @@ int64_t chain_count(const ssd_params_t* p) {
 bool relay_capable(const ssd_params_t* p) {
     if (p->impl != SSD_IMPL_FUSED) return false;
     const int env = relay_env();
-    return env >= 0 ? env == 1 : chain_count(p) <= kRelayMaxChains;
+    return env >= 0 ? env != 0 : chain_count(p) <= kRelayMaxChains;
 }
 
 struct Layout {
@@ -262,11 +263,23 @@ void set_partitions(const ssd_params_t* p, const Layout& l, const DevInfo& d, ss
         if (u1 - u0 > maxu) maxu = u1 - u0;
     }
     a.part_max_work = maxw;
-    // The relay items (four per chain) hold one workgroup each for the whole launch: use them
-    // only while they take at most half of a partition's workgroups (two per CU) and leave
-    // room for two chunks of the partition's chunk tiles.
+    // The relay items (R per chain, R = relay waves per chain part) hold one workgroup each
+    // for the whole launch: use them only while they take at most half of a partition's
+    // workgroups (two per CU) and leave room for two chunks of the partition's chunk tiles.
+    // R = 4 halves each relay wave's share of the state (faster hand-offs) and is used while
+    // the chunk tiles still have 16 workgroups per chain; else R = 2 (more chunk tiles at once).
     const int per_part = (d.cus / d.nparts > 0 ? d.cus / d.nparts : 1) * 2;
-    a.relay = (relay_capable(p) && 8 * maxu <= per_part && per_part - 4 * maxu >= 2 * maxu + 2) ? 1 : 0;
+    auto usable = [&](int R) { return 2 * R * maxu <= per_part && per_part - R * maxu >= 2 * maxu + 2; };
+    const int env = relay_env();
+    a.relay = 0;
+    if (relay_capable(p)) {
+        if (env == 2 || env == 4)
+            a.relay = usable(env) ? env : 0;
+        else if (per_part - 4 * maxu >= 16 * maxu)
+            a.relay = 4;
+        else if (usable(2))
+            a.relay = 2;
+    }
     a.slots = a.relay ? l.w.state_slots : 1;
 }
 

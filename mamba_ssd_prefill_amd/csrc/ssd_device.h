@@ -410,14 +410,15 @@ __device__ inline void ring_store(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t 
 // in and publishes S_c one chunk later, once its stores are known complete.  Both rings keep
 // each lane's 16-byte pieces contiguous (see ring_chain): a chunk-state slot holds the NT
 // accumulator tiles as fp32, an operand slot holds them in units of 16 / (4 sizeof(T)) tiles.
-constexpr int kRelayWaves = 4;
-
 template <typename T> constexpr int tiles_per_unit() { return sizeof(T) == 2 ? 2 : 1; }
 
-// Relay waves of a chain whose chunk-tile wave holds NT accumulator tiles: each relay wave
-// takes the same number of whole operand units.
-template <typename T, int NT> constexpr int relay_waves() {
-    return NT / tiles_per_unit<T>() < kRelayWaves ? NT / tiles_per_unit<T>() : kRelayWaves;
+// Relay waves of a chain whose chunk-tile wave holds NT accumulator tiles, at most RWM (the
+// launch's choice, 2 or 4): each relay wave takes the same number of whole operand units.
+template <typename T, int NT, int RWM> constexpr int relay_waves() {
+    return NT / tiles_per_unit<T>() < RWM ? NT / tiles_per_unit<T>() : RWM;
+}
+template <typename T, int NT> __device__ inline int relay_waves_of(const SsdArgs& a) {
+    return a.relay == 4 ? relay_waves<T, NT, 4>() : relay_waves<T, NT, 2>();
 }
 
 __device__ inline size_t chain_index(const SsdArgs& a, int b, int h, int ph, int WPH) {
@@ -451,8 +452,9 @@ template <typename T> __device__ inline u32x4 pack_unit(const f32x4* v) {
 
 // Relay wave w of chain (b, h, ph): the state passing of tiles [w * TPW, (w + 1) * TPW) of the
 // chain's NT accumulator tiles, over every chunk.
-template <typename T, int NT> __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int w) {
-    constexpr int TPU = tiles_per_unit<T>(), TPW = NT / relay_waves<T, NT>();
+template <typename T, int NT, int RWM>
+__device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int w) {
+    constexpr int TPU = tiles_per_unit<T>(), TPW = NT / relay_waves<T, NT, RWM>();
     static_assert(TPW % TPU == 0, "a relay wave holds whole operand units");
     const uint32_t lane = (uint32_t)tid_here() & 63u;
     const int H = a.nheads, nc = a.nchunks, Q = a.chunk, K = a.slots, KO = a.op_slots, sdt = a.state_dtype;
@@ -510,6 +512,12 @@ template <typename T, int NT> __device__ void relay_chain(const SsdArgs& a, int 
         asm volatile("" ::: "memory");
         if (c >= 2) raise_flag(my_cnt, (uint32_t)c);  // states entering chunks 0 .. c-1 are stored
         if (has_next && !early) {
+            // about to wait for s_{c+1} anyway: let St(c) complete and publish S_c now, so
+            // chunk tile c does not wait for chunk tile c + 1
+            if (c >= 1) {
+                wait_vm<0>();
+                raise_flag(my_cnt, (uint32_t)c + 1);
+            }
             const int n = wait_run(agg_words, kAggSlots, (uint32_t)c + 1, 0u, a);
             if (n == 0) return false;
             agg_hi = c + 1 + n;
@@ -560,7 +568,8 @@ template <typename T, int NT> __device__ void relay_chain(const SsdArgs& a, int 
 template <typename T, int NB, int MBP>
 __device__ inline bool relay_handoff(const SsdArgs& a, int b, int c, int h, int ph, int WPH,
                                      const f32x4 (&acc)[NB][MBP], typename TT<T>::v4 (&sv)[NB][MBP]) {
-    constexpr int NT = NB * MBP, RW = relay_waves<T, NT>(), TPU = tiles_per_unit<T>();
+    constexpr int NT = NB * MBP, TPU = tiles_per_unit<T>();
+    const int RW = relay_waves_of<T, NT>(a);
     typedef typename TT<T>::v4 v4;
     const uint32_t lane = (uint32_t)tid_here() & 63u;
     uint32_t* cnt = chain_counter(a, b, h, ph, WPH);

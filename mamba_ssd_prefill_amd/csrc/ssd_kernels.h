@@ -63,8 +63,9 @@ template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds_
 // (b, g), and bmm tiles (pair, c) into its own CB slots.  Its queue, in claim order:
 //   [0, np*nc)             cumsum tiles, chunk-major
 //   [np*nc, 2*np*nc)       bmm tiles, chunk-major
-//   [2*np*nc, +4*nu)       relay form only: one relay item per chain part, i.e. per wave of the
-//                          chain's chunk tiles (see relay_chain)
+//   [2*np*nc, +R*nu)       relay form only: R relay items per chain (R = relay waves per part,
+//                          2 or 4), each serving 4 / R parts of it (the parts are the waves of
+//                          its chunk tiles)
 //   [first_chunk, +nu*nc)  chunk tiles: the chains in groups of chain_group, one group after
 //                          the other, chunk-major inside a group (so only one group's state
 //                          slots need to stay in the L2 at a time)
@@ -89,7 +90,7 @@ __device__ inline FusedPart fused_part(const SsdArgs& a, int x) {
     f.np = f.nu > 0 ? (f.u0 + f.nu - 1) / a.tpg - f.p0 + 1 : 0;
     f.pb = a.part_pb[x];
     f.n_cs = (uint32_t)f.np * a.nchunks;
-    f.first_chunk = 2 * f.n_cs + (a.relay ? 4u * (uint32_t)f.nu : 0u);  // 4 waves = parts per chunk tile
+    f.first_chunk = 2 * f.n_cs + (uint32_t)a.relay * f.nu;
     f.n_total = f.first_chunk + (uint32_t)f.nu * a.nchunks;
     return f;
 }
@@ -212,14 +213,21 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                 publish_flag_block(a.bmm_done + slot);
             }
         } else if (t < f.first_chunk) {
-            // relay item of chain u's part (head hs, p-slice ph) = its tile's wave `part`
+            // relay item k of chain u (its chunk tiles' 4 waves are 4 parts, (head hs, p-slice ph)):
+            // parts k * PPI .. k * PPI + PPI - 1, R = a.relay waves each
             constexpr int PW = P < 32 ? P : 32, WPH = P / PW, NT = (N / 16) * (PW / 16);
+            const int R = a.relay, PPI = 4 / R;
             const uint32_t r = t - 2 * f.n_cs;
-            const int u = f.u0 + (int)(r / 4), part = (int)(r % 4), pair = u / tpg, tig = u % tpg;
-            const int hs = part / WPH, ph = part % WPH;
-            const int wave = __builtin_amdgcn_readfirstlane(tid_here() >> 6);
-            if (tig * HPT + hs < hpg && wave < relay_waves<T, NT>())
-                relay_chain<T, NT>(a, pair / Gn, (pair % Gn) * hpg + tig * HPT + hs, ph, WPH, wave);
+            const int wave = __builtin_amdgcn_readfirstlane(tid_here() >> 6), rw = wave % R;
+            const int u = f.u0 + (int)(r / R), part = (int)(r % R) * PPI + wave / R;
+            const int pair = u / tpg, tig = u % tpg, hs = part / WPH, ph = part % WPH;
+            const int b = pair / Gn, h = (pair % Gn) * hpg + tig * HPT + hs;
+            if (tig * HPT + hs < hpg && rw < relay_waves_of<T, NT>(a)) {
+                if (R == 4)
+                    relay_chain<T, NT, 4>(a, b, h, ph, WPH, rw);
+                else
+                    relay_chain<T, NT, 2>(a, b, h, ph, WPH, rw);
+            }
         } else {
             const ChunkItem it = chunk_item(a, f, t);
             if (threadIdx.x == 0) {

@@ -46,7 +46,7 @@ struct SsdArgs {
     int part_u0[kMaxXcc + 1];
     int part_pb[kMaxXcc + 1];
     int chain_group;    // chains whose chunk tiles are claimed together (0: set at launch)
-    int relay;          // fused form: 1 = dedicated state-passing items (see relay_chain)
+    int relay;          // fused form: relay waves per chain part (2 or 4), 0 = no relay items
     int part_max_work;  // host only: the longest partition queue
     int cu_count;       // host only: compute units of the device
 };
@@ -61,6 +61,7 @@ constexpr int kChainReadWords = 64;
 // line of slot words).  Its state ring has two slots: the initial state and the final one.
 constexpr int kRelaySlots = 16;
 constexpr int kAggSlots = 32;
+
 
 enum : int {
     STEP_CUMSUM = 0,

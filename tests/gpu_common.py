@@ -30,12 +30,14 @@ _STATE_CODE = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16
 
 @contextlib.contextmanager
 def fused_form(impl):
-    """impl "fused_hop" / "fused_relay": the fused form with the chunk tiles' own state hop /
-    with relay items (MAMBA_SSD_RELAY = 0 / 1); "fused" and "unfused" leave the choice to the
-    library.  Yields the impl name the binding takes."""
+    """impl "fused_hop" / "fused_relay" / "fused_relay2" / "fused_relay4": the fused form with
+    the chunk tiles' own state hop / with relay items (MAMBA_SSD_RELAY = 0 / 1, or 2 / 4 relay
+    waves per chain part); "fused" and "unfused" leave the choice to the library.  Yields the
+    impl name the binding takes."""
     old = os.environ.pop("MAMBA_SSD_RELAY", None)
-    if impl in ("fused_hop", "fused_relay"):
-        os.environ["MAMBA_SSD_RELAY"] = "1" if impl == "fused_relay" else "0"
+    forms = {"fused_hop": "0", "fused_relay": "1", "fused_relay2": "2", "fused_relay4": "4"}
+    if impl in forms:
+        os.environ["MAMBA_SSD_RELAY"] = forms[impl]
     try:
         yield "fused" if impl.startswith("fused") else impl
     finally:

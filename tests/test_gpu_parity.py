@@ -23,8 +23,9 @@ def dev():
     return require_gpu()
 
 
-# the fused form both with the chunk tiles' own state hop and with relay items
-IMPLS = ["unfused", "fused_hop", "fused_relay"]
+# the fused form both with the chunk tiles' own state hop and with relay items (2 and 4
+# relay waves per chain part)
+IMPLS = ["unfused", "fused_hop", "fused_relay2", "fused_relay4"]
 
 
 @pytest.mark.parametrize("impl", IMPLS)
@@ -123,7 +124,7 @@ def test_zero_step_keeps_state(impl):
     check_full(inp, y, fin, "dt0")
 
 
-@pytest.mark.parametrize("form", ["fused_hop", "fused_relay"])
+@pytest.mark.parametrize("form", ["fused_hop", "fused_relay2", "fused_relay4"])
 def test_fused_is_deterministic_and_matches_unfused(form):
     inp = make_inputs(2, 1000, 8, 64, 128, 2, dtype="bf16", has_h0=True, seed=9)
     y1, f1 = run_gpu(inp, 128, form)
