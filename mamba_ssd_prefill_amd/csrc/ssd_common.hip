@@ -47,13 +47,15 @@ __global__ __launch_bounds__(256) void k_boundary(const char* src, size_t src_bs
 
 // Boundary copies of the fused form, between the callers' [B][H][P][N] states and the ring
 // layout (see ring_chain): to_ring = 1 copies src (or zeros) into slot `slot`, to_ring = 0
-// copies slot `slot` out to dst.  One thread per 4 consecutive n of one (b, h, p).  Also
+// copies slot `slot` out to dst.  One thread per 4 consecutive n of one (b, h, p).  pperm = 1:
+// the 16-bit tile's interleaved p order (Geo16::pcol), else p block pb = pw / 16, lane pw % 16.  Also
 // resets nsync sync words: word i becomes flag_init when i < nflags and i % flag_period < 4
 // (the progress counters of every chain, one per relay wave: 1 = the state entering chunk 0
 // is ready), else 0.
 __global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, int to_ring, int B, int H, int P,
-                                                    int N, int K, int slot, int es, uint32_t* sync, size_t nsync,
-                                                    size_t nflags, uint32_t flag_period, uint32_t flag_init) {
+                                                    int N, int K, int slot, int es, int pperm, uint32_t* sync,
+                                                    size_t nsync, size_t nflags, uint32_t flag_period,
+                                                    uint32_t flag_init) {
     const int PW = P < 32 ? P : 32, WPH = P / PW, MBP = PW / 16, NB = N / 16;
     const size_t total = (size_t)B * H * P * (N / 4);
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -63,7 +65,13 @@ __global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, i
         const int p = (int)(r % P);
         const int h = (int)((r / P) % H);
         const int b = (int)(r / ((size_t)P * H));
-        const int ph = p / PW, pw = p % PW, pb = pw / 16, r16 = pw % 16;
+        const int ph = p / PW, pw = p % PW;
+        int pb = pw / 16, r16 = pw % 16;
+        if (pperm) {
+            const int q8 = pw / (4 * MBP), rem = pw % (4 * MBP);
+            pb = rem >> 2;
+            r16 = 4 * q8 + (rem & 3);
+        }
         const int nb = n / 16, q = (n % 16) / 4;
         const size_t ring = ring_chain(b, slot, h, ph, K, H, WPH, NB * MBP) + ((size_t)(nb * MBP + pb) * 64 + 16 * q + r16) * 4;
         const size_t user = (((size_t)b * H + h) * P + p) * N + n;
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, i
 }
 
 hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int N, int K, int slot,
-                            int es, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
+                            int es, int pperm, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
                             uint32_t flag_init, hipStream_t st) {
     const size_t work = (size_t)B * H * P * (N / 4);
     const size_t big = work > nsync ? work : nsync;
@@ -92,7 +100,7 @@ hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int 
     if (grid > 8192) grid = 8192;
     const char* s = (const char*)src;
     char* d = (char*)dst;
-    void* args[] = {&s, &d, &to_ring, &B, &H, &P, &N, &K, &slot, &es, &sync, &nsync, &nflags, &flag_period, &flag_init};
+    void* args[] = {&s, &d, &to_ring, &B, &H, &P, &N, &K, &slot, &es, &pperm, &sync, &nsync, &nflags, &flag_period, &flag_init};
     return hipLaunchKernel((const void*)&k_ring_copy, dim3((unsigned)grid), dim3(256), args, 0, st);
 }
 

@@ -29,6 +29,10 @@ template <typename T, int P, int N, int Q> struct Geo16 {
     static constexpr int WPH = P / PW;          // waves per head
     static constexpr int HPT = 4 / WPH;         // heads per tile
     static constexpr int MBP = PW / 16;
+    // p columns of the accumulator layout: lane r16 of p block pb holds column pcol(pb, r16)
+    // of its wave's PW.  The interleave gives output lane q of y^T the 4 MBP consecutive columns
+    // 4 MBP q .. +4 MBP - 1 across its p blocks, so y and the D x term move as one piece per lane.
+    static constexpr int pcol(int pb, int r16) { return (r16 >> 2) * 4 * MBP + 4 * pb + (r16 & 3); }
     static constexpr int NB = N / 16;
     static constexpr int KS = Q / 32;  // 32-token k-steps
     static constexpr int QB = Q / 16;  // 16-token row blocks
@@ -109,6 +113,14 @@ template <int COLS> __device__ inline int tr_lane_off(int col0) {
     const int lane = tid_here() & 63;
     const int q = lane >> 4, m = (lane & 15) >> 2, jj = lane & 3;
     return sw_off<COLS>(8 * q + m, col0 + 4 * jj);
+}
+
+// tr_lane_off for the x operand in the interleaved column order of Geo16::pcol: the four
+// column quads of p block pb start at c0 + 4 MBP jj + 4 pb.
+template <int COLS, int MBP> __device__ inline int tr_lane_off_p(int c0, int pb) {
+    const int lane = tid_here() & 63;
+    const int q = lane >> 4, m = (lane & 15) >> 2, jj = lane & 3;
+    return sw_off<COLS>(8 * q + m, c0 + 4 * MBP * jj + 4 * pb);
 }
 
 template <typename T, int COLS> __device__ inline typename TT<T>::frag tr_frag_at(const T* tile, int lane_off, int k0) {
@@ -379,14 +391,14 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         }
     }
 
-    // x operand, token-major: xf[kk][pb] holds x[kk*32 + 8q .. +7][ph*PW + pb*16 + r16]
+    // x operand, token-major: xf[kk][pb] holds x[kk*32 + 8q .. +7][ph*PW + pcol(pb, r16)]
     frag xf[KS][MBP];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int pb = 0; pb < MBP; ++pb) xf[kk][pb] = tr_frag_at<T, P>(sX + hs * Q * P, tr_lane_off<P>(ph * PW + pb * 16), kk * 32);
+        for (int pb = 0; pb < MBP; ++pb) xf[kk][pb] = tr_frag_at<T, P>(sX + hs * Q * P, tr_lane_off_p<P, MBP>(ph * PW, pb), kk * 32);
 
-    // S_c in accumulator layout, rounded to T: tile (nb, pb), lane -> S[p = ph*PW + pb*16 + r16][n = nb*16 + 4q + r]
+    // S_c in accumulator layout, rounded to T: tile (nb, pb), lane -> S[p = ph*PW + pcol(pb, r16)][n = nb*16 + 4q + r]
     v4 scb[NB][MBP];
     LBuild<T, G_, AUX> lb;  // the L bands' CB pieces, read early (Q <= 128 with room for L)
     if constexpr (MODE != MODE_SCAN) {
@@ -427,7 +439,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) {
-                        const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
+                        const int p = ph * PW + G_::pcol(pb, r16), n = nb * 16 + 4 * q;
                         *(f32x4*)(a.s + ((((size_t)b * nc + c) * H + h) * P + p) * N + n) = acc[nb][pb];
                     }
             }
@@ -485,7 +497,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int pb = 0; pb < MBP; ++pb) {
-                    const int p = ph * PW + pb * 16 + r16, n = nb * 16 + 4 * q;
+                    const int p = ph * PW + G_::pcol(pb, r16), n = nb * 16 + 4 * q;
                     scb[nb][pb] = cvt4<T>(load_state4(a.states, a.state_dtype, ((((size_t)b * K + slot) * H + h) * P + p) * N + n));
                 }
         }
@@ -507,7 +519,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         // exp2(acs_i log2(e) - sE[j]) = exp(acs_i - acs_j) dt_j.
         // (With the L bands, the column factors end at 16-token blocks instead: see LBuild.)
         //
-        // x for the D x term in the y layout (x[ib*16 + r16][ph*PW + pb*16 + 4q .. +3]).  While the
+        // x for the D x term in the y layout (x[ib*16 + r16][ph*PW + 4 MBP q + 4 pb .. +3]).  While the
         // x tile is still in LDS (it is, unless the CB bands were copied over it) it comes from
         // there: with the L bands, which replace it next, every row block is read now; without
         // CB in LDS, at its use.  Otherwise it is read again from HBM/L2, two blocks ahead.
@@ -518,8 +530,8 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         const T* sX_h = sX + hs * Q * P;
         auto xd_load = [&](int ib, int pb) -> v4 {
             if constexpr (XD_LDS)
-                return *(const v4*)(sX_h + sw_off<P>(ib * 16 + r16, ph * PW + pb * 16 + 4 * q));
-            const uint32_t off = (uint32_t)(ib * 16 + r16) * xrs + (uint32_t)(ph * PW + pb * 16 + 4 * q) * 2;
+                return *(const v4*)(sX_h + sw_off<P>(ib * 16 + r16, ph * PW + 4 * MBP * q + 4 * pb));
+            const uint32_t off = (uint32_t)(ib * 16 + r16) * xrs + (uint32_t)(ph * PW + 4 * MBP * q + 4 * pb) * 2;
             return __builtin_bit_cast(v4, __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0));
         };
         v4 xd[XDA][MBP];
@@ -648,7 +660,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     for (int pb = 0; pb < MBP; ++pb) accY[pb] = TT<T>::mma(xf[kk][pb], lf, accY[pb]);
                 }
             }
-            // y = acc + D x, 4 consecutive p per lane
+            // y = acc + D x: 4 MBP consecutive p per lane (see Geo16::pcol)
             v4 xcur[MBP];
 #pragma unroll
             for (int pb = 0; pb < MBP; ++pb) {
@@ -663,18 +675,24 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 }
             }
             if (i < valid) {
+                v4 yo[MBP];
 #pragma unroll
                 for (int pb = 0; pb < MBP; ++pb) {
-                    const int p = ph * PW + pb * 16 + 4 * q;
                     f32x4 yv = accY[pb];
                     yv[0] += Dh * (float)xcur[pb][0];
                     yv[1] += Dh * (float)xcur[pb][1];
                     yv[2] += Dh * (float)xcur[pb][2];
                     yv[3] += Dh * (float)xcur[pb][3];
-                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4<T>(yv)), yr,
-                                                          (uint32_t)i * xrs + (uint32_t)p * 2, 0, 2);
+                    yo[pb] = cvt4<T>(yv);
                 }
+                const uint32_t yoff = (uint32_t)i * xrs + (uint32_t)(ph * PW + 4 * MBP * q) * 2;
+                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                if constexpr (MBP == 2)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4, __builtin_shufflevector(yo[0], yo[1], 0, 1, 2, 3, 4, 5, 6, 7)), yr, yoff,
+                        0, 2);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yo[0]), yr, yoff, 0, 2);
             }
         }
         asm volatile("" ::"v"(touched));  // the touch loads are long complete
