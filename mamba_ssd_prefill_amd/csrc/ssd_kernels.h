@@ -11,7 +11,7 @@ namespace ssd {
 // No-op cross-tile prefetch hooks (see PrefetchHook) for the unfused kernels.
 struct NoHook {
     __device__ inline void claim() const {}
-    __device__ inline uint32_t touch() const { return 0u; }
+    __device__ inline u32x2 touch() const { return u32x2{0u, 0u}; }
 };
 
 // ---- unfused form: one kernel per step -------------------------------------------------
@@ -139,7 +139,8 @@ __device__ inline ChunkItem chunk_item(const SsdArgs& a, const FusedPart& f, uin
 // touch() once its L bands are built (every thread loads one word of each 128-byte line of the
 // next chunk tile's x rows, which are then in the L2 when that tile copies them).  The next
 // ticket is larger than the current one and runs only after it, so the claim order keeps
-// every wait finite.  touch() returns the loaded words, to be consumed (asm sink) at the end.
+// every wait finite.  touch() returns the loaded words unused, to be consumed (asm sink) at
+// the end of the tile: a use any earlier would wait for the loads.
 template <int HPT, int P> struct PrefetchHook {
     const SsdArgs& a;
     const FusedPart& f;
@@ -148,9 +149,9 @@ template <int HPT, int P> struct PrefetchHook {
     __device__ inline void claim() const {
         if (threadIdx.x == 0) *s_next = atomicAdd(a.ticket + part * kTicketStride, 1u);
     }
-    __device__ inline uint32_t touch() const {
+    __device__ inline u32x2 touch() const {
         const uint32_t tn = __builtin_amdgcn_readfirstlane(*s_next);
-        if (tn < f.first_chunk || tn >= f.n_total) return 0u;
+        if (tn < f.first_chunk || tn >= f.n_total) return u32x2{0u, 0u};
         const ChunkItem it = chunk_item(a, f, tn);
         const int L = a.seqlen, H = a.nheads, Q = a.chunk, hpg = a.hpg;
         const int tok0 = it.c * Q, valid = L - tok0 < Q ? L - tok0 : Q;
@@ -159,11 +160,15 @@ template <int HPT, int P> struct PrefetchHook {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(
             (const char*)a.x + ((((size_t)it.b * L + tok0) * H + it.g * hpg + it.tig * HPT) * P) * 2,
             (uint32_t)(valid - 1) * xrs + (uint32_t)nvh * P * 2);
-        constexpr int LPR = (HPT * P * 2 + 127) / 128;  // 128-byte lines per row
-        uint32_t acc = 0;
-        for (int k = tid_here(); k < Q * LPR; k += 256)
-            acc += __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(k / LPR) * xrs + (uint32_t)(k % LPR) * 128, 0, 0);
-        return acc;
+        constexpr int LPR = (HPT * P * 2 + 127) / 128;  // 128-byte lines per row (at most 2)
+        static_assert(LPR <= 2, "a tile row spans at most two lines");
+        const int k0 = tid_here(), k1 = k0 + 256;  // Q * LPR <= 512 lines
+        u32x2 v = {0u, 0u};
+        if (k0 < Q * LPR)
+            v.x = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(k0 / LPR) * xrs + (uint32_t)(k0 % LPR) * 128, 0, 0);
+        if (k1 < Q * LPR)
+            v.y = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(k1 / LPR) * xrs + (uint32_t)(k1 % LPR) * 128, 0, 0);
+        return v;
     }
 };
 

@@ -339,6 +339,9 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     float* sF = sW;
     float* sE = sDt;
 
+    // read now: a load issued just before its use in the y loop would make every row block wait
+    // for all of the tile's outstanding memory operations
+    const float Dh = (MODE != MODE_STATE && a.D && hvalid) ? a.D[h] : 0.f;
     const uint32_t xrs = (uint32_t)H * P * 2, bcrs = (uint32_t)Gn * N * 2;
     const uint32_t bc_bytes = (uint32_t)(valid - 1) * bcrs + N * 2;
     const size_t bc_off = (((size_t)b * L + tok0) * Gn + g) * N;
@@ -414,6 +417,11 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         if (hvalid) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
+                // every B fragment of this k step is read before the first product, so the LDS
+                // reads overlap one another instead of each waiting out its own latency
+                frag af[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) af[nb] = tr_frag_at<T, N>(sBC, boff[nb], kk * 32);
                 const f32x4 w0 = *(const f32x4*)(sW + hs * Q + kk * 32 + 8 * q);
                 const f32x4 w1 = *(const f32x4*)(sW + hs * Q + kk * 32 + 8 * q + 4);
                 frag xw[MBP];
@@ -426,11 +434,9 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     }
                 }
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const frag af = tr_frag_at<T, N>(sBC, boff[nb], kk * 32);
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int pb = 0; pb < MBP; ++pb) acc[nb][pb] = TT<T>::mma(af, xw[pb], acc[nb][pb]);
-                }
+                    for (int pb = 0; pb < MBP; ++pb) acc[nb][pb] = TT<T>::mma(af[nb], xw[pb], acc[nb][pb]);
             }
         }
         if constexpr (MODE == MODE_STATE) {
@@ -554,9 +560,9 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             lb.store((T*)smem, sA2, sF, sE, nvh, tid);  // over x (already in registers)
             lds_barrier();                              // L is complete
         }
-        const uint32_t touched = hook.touch();
+        const u32x2 touched = hook.touch();
         if (!hvalid) {
-            asm volatile("" ::"v"(touched));
+            asm volatile("" ::"v"(touched.x), "v"(touched.y));
             return;
         }
         // S_c as the A operand of C . S^T; k slots of step ks: n = 32ks + 4q + {0..3} and
@@ -587,7 +593,6 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 xs[kk][pb] = pack8<T>(lo, hi);
             }
         }
-        const float Dh = a.D ? a.D[h] : 0.f;
         const __amdgpu_buffer_rsrc_t cbr = make_rsrc(cbp, (uint32_t)(Q * Q * 4));
         // y: written once and never read here, so non-temporal (nt) stores keep it from
         // pushing the state slots and CB out of the L2
@@ -601,6 +606,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             clo[ks] = sw_off<N, SWZ_ROW>(r16, ks * 32 + 4 * q);
             chi[ks] = sw_off<N, SWZ_ROW>(r16, ks * 32 + 16 + 4 * q);
         }
+        v4 yo[QB][MBP];  // y rows of this lane, in T
 #pragma unroll
         for (int ib = 0; ib < QB; ++ib) {
             const int i = ib * 16 + r16;  // this lane's output row (column of y^T)
@@ -674,28 +680,33 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     if (ib + 2 < QB) xd[1][pb] = xd_load(ib + 2, pb);
                 }
             }
-            if (i < valid) {
-                v4 yo[MBP];
 #pragma unroll
-                for (int pb = 0; pb < MBP; ++pb) {
-                    f32x4 yv = accY[pb];
-                    yv[0] += Dh * (float)xcur[pb][0];
-                    yv[1] += Dh * (float)xcur[pb][1];
-                    yv[2] += Dh * (float)xcur[pb][2];
-                    yv[3] += Dh * (float)xcur[pb][3];
-                    yo[pb] = cvt4<T>(yv);
-                }
-                const uint32_t yoff = (uint32_t)i * xrs + (uint32_t)(ph * PW + 4 * MBP * q) * 2;
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                if constexpr (MBP == 2)
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(u32x4, __builtin_shufflevector(yo[0], yo[1], 0, 1, 2, 3, 4, 5, 6, 7)), yr, yoff,
-                        0, 2);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yo[0]), yr, yoff, 0, 2);
+            for (int pb = 0; pb < MBP; ++pb) {
+                f32x4 yv = accY[pb];
+                yv[0] += Dh * (float)xcur[pb][0];
+                yv[1] += Dh * (float)xcur[pb][1];
+                yv[2] += Dh * (float)xcur[pb][2];
+                yv[3] += Dh * (float)xcur[pb][3];
+                yo[ib][pb] = cvt4<T>(yv);
             }
         }
-        asm volatile("" ::"v"(touched));  // the touch loads are long complete
+        // The stores go out together after the loop: a store's registers stay reserved until it
+        // completes, so reusing them block after block would make every block wait for the
+        // previous block's store.  (yo takes the registers the D x operand frees.)
+#pragma unroll
+        for (int ib = 0; ib < QB; ++ib) {
+            const int i = ib * 16 + r16;
+            if (i < valid) {
+                const uint32_t yoff = (uint32_t)i * xrs + (uint32_t)(ph * PW + 4 * MBP * q) * 2;
+                if constexpr (MBP == 2)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4, __builtin_shufflevector(yo[ib][0], yo[ib][1], 0, 1, 2, 3, 4, 5, 6, 7)),
+                        yr, yoff, 0, 2);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yo[ib][0]), yr, yoff, 0, 2);
+            }
+        }
+        asm volatile("" ::"v"(touched.x), "v"(touched.y));  // the touch loads are long complete
     }
 }
 
