@@ -150,7 +150,8 @@ const char* ssd_status_string(ssd_status_t s);
  *           unfused: [B][K = nc+1][H][P][N]                                      state_passing
  *           fused:   K = 1 slot per chain, updated in place chunk after chunk (relay form:
  *                    K = 2, the initial state in slot 0 and the final one in slot 1), in an
- *                    internal lane-major order (the fused kernel's own layout)
+ *                    internal lane-major order (the fused kernel's own layout); without an
+ *                    initial state slot 0 is not filled (the kernel takes S_0 = 0)
  *   sync    uint32 words: per-chain words (three 128-byte lines each: progress counter,
  *           relay slot words), cumsum / bmm completion flags, one
  *           work counter and one owner word per partition, the exit counter and the

@@ -453,6 +453,7 @@ static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt
     a.D = D;
     a.dt_bias = dt_bias;
     a.y = y;
+    a.has_h0 = initial_state != nullptr;
     hipError_t e;
     auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, st) : hipSuccess; };
     if (p->impl == SSD_IMPL_FUSED) {

@@ -46,8 +46,9 @@ __global__ __launch_bounds__(256) void k_boundary(const char* src, size_t src_bs
 }
 
 // Boundary copies of the fused form, between the callers' [B][H][P][N] states and the ring
-// layout (see ring_chain): to_ring = 1 copies src (or zeros) into slot `slot`, to_ring = 0
-// copies slot `slot` out to dst.  One thread per 4 consecutive n of one (b, h, p).  pperm = 1:
+// layout (see ring_chain): to_ring = 1 copies src into slot `slot`, to_ring = 0
+// copies slot `slot` out to dst (src == nullptr: no initial state, nothing is copied).  One
+// thread per 4 consecutive n of one (b, h, p).  pperm = 1:
 // the 16-bit tile's interleaved p order (Geo16::pcol), else p block pb = pw / 16, lane pw % 16.  Also
 // resets nsync sync words: word i becomes flag_init when i < nflags and i % flag_period < 4
 // (the progress counters of every chain, one per relay wave: 1 = the state entering chunk 0
@@ -57,7 +58,8 @@ __global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, i
                                                     size_t nsync, size_t nflags, uint32_t flag_period,
                                                     uint32_t flag_init) {
     const int PW = P < 32 ? P : 32, WPH = P / PW, MBP = PW / 16, NB = N / 16;
-    const size_t total = (size_t)B * H * P * (N / 4);
+    // no initial state: the fused kernel never reads slot 0 before writing it, so nothing to copy
+    const size_t total = (to_ring && src == nullptr) ? 0 : (size_t)B * H * P * (N / 4);
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
         const int n = (int)(i % (N / 4)) * 4;

@@ -272,6 +272,26 @@ __device__ inline bool wait_words(const uint32_t* f, int n, const SsdArgs& a, ui
     return ok;
 }
 
+// One wave: wait until base[o0] >= 1 and base[o1] >= 1 (lanes 0 and 1 poll one word each).
+__device__ inline bool wait_pair(const uint32_t* base, uint32_t o0, uint32_t o1, const SsdArgs& a) {
+    const uint32_t lane = (uint32_t)tid_here() & 63u;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, ((o0 > o1 ? o0 : o1) + 1) * 4);
+    const uint32_t off = (lane == 1 ? o1 : o0) * 4;
+    uint32_t spins = 0;
+    bool ok = true;
+    for (;;) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX_L2);
+        if (__ballot(lane < 2 && v < 1u) == 0ull) break;
+        if (!spin_ok(++spins, a)) {
+            ok = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return ok;
+}
+
 // A row of per-slot words (at most 32, one 128-byte line), one slot per item modulo `slots`:
 // the number of consecutive items base, base + 1, ... (at most `slots`) whose slot word w
 // has w + bias >= item + 1.  One sc1 load per lane; the result is wave-uniform.
@@ -469,7 +489,7 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     {
         const __amdgpu_buffer_rsrc_t r = ring_rsrc(a.states, sdt, ring_chain(b, 0, h, ph, K, H, WPH, NT), NT);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) S[t] = ring_load(r, sdt, ((t0 + t) * 64 + lane) * 4);
+        for (int t = 0; t < TPW; ++t) S[t] = a.has_h0 ? ring_load(r, sdt, ((t0 + t) * 64 + lane) * 4) : vzero<f32x4>();
         // S_0 into operand slot 0, then published (the counters start at 0 in this form)
         const __amdgpu_buffer_rsrc_t ro = opnd_rsrc<T, NT>(a, b, h, ph, WPH, 0);
 #pragma unroll
@@ -866,12 +886,13 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                 const __amdgpu_buffer_rsrc_t rout =
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const float dec = __expf(acs_last);
+                const bool zero0 = c == 0 && !a.has_h0;  // S_0 = 0: nothing to read
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) {
                         const uint32_t off = ((nb * MBP + pb) * 64 + lane) * 4;
-                        sc[nb][pb] = ring_load(rin, a.state_dtype, off);
+                        sc[nb][pb] = zero0 ? vzero<f32x4>() : ring_load(rin, a.state_dtype, off);
                         ring_store(rout, a.state_dtype, off, dec * sc[nb][pb] + acc[nb][pb]);
                     }
                 publish_flag_wave(fl, (uint32_t)c + 2);

@@ -235,10 +235,8 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
             }
         } else {
             const ChunkItem it = chunk_item(a, f, t);
-            if (threadIdx.x == 0) {
-                wait_flag(a.cs_done + it.slot, a);
-                wait_flag(a.bmm_done + it.slot, a);
-            }
+            if (tid_here() < 64)  // wave 0: both flags with one poll
+                wait_pair(a.cs_done, (uint32_t)it.slot, (uint32_t)(a.bmm_done - a.cs_done + it.slot), a);
             lds_barrier();  // every wave starts after the flags were seen
             const PrefetchHook<HPT, P> hook{a, f, x, &s_next};
             chunk(a, it.b, it.c, it.g, it.tig, a.cb + it.slot * Q * Q, hook);

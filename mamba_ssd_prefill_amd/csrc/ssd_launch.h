@@ -37,6 +37,7 @@ struct SsdArgs {
     uint32_t* status;
     int batch, seqlen, nheads, ngroups, chunk, nchunks, hpg, tpg, slots, op_slots;
     int state_dtype, softplus;
+    int has_h0;  // fused form: 0 = no initial state (S_0 = 0 is never read from the ring)
     uint32_t spin_limit;
     // fused form: the chains (b, g, tile-in-group), numbered u = (b * G + g) * tpg + tig, are
     // split into nparts contiguous ranges [part_u0[x], part_u0[x + 1]); partition x runs on

@@ -475,12 +475,13 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 const __amdgpu_buffer_rsrc_t rout =
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const float dec = __builtin_amdgcn_exp2f(a2_h[Q - 1]);
+                const bool zero0 = c == 0 && !a.has_h0;  // S_0 = 0: nothing to read
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) {
                         const uint32_t off = ((nb * MBP + pb) * 64 + lane) * 4;
-                        const f32x4 sv = ring_load(rin, a.state_dtype, off);
+                        const f32x4 sv = zero0 ? vzero<f32x4>() : ring_load(rin, a.state_dtype, off);
                         ring_store(rout, a.state_dtype, off, dec * sv + acc[nb][pb]);
                         scb[nb][pb] = cvt4<T>(sv);
                     }
