@@ -266,7 +266,8 @@ template <typename T, int P, int N> __global__ __launch_bounds__(256) void k_fus
     });
 }
 
-template <typename T, int P, int N, int Q> __global__ __launch_bounds__(256, 2) void k_fused16(SsdArgs a) {
+template <typename T, int P, int N, int Q>
+__global__ __launch_bounds__(256, (Geo16<T, P, N, Q>::OCC)) void k_fused16(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
     fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
                                                        const float* cbp, const auto& hook) {

@@ -61,6 +61,9 @@ template <typename T, int P, int N, int Q> struct Geo16 {
     static constexpr int SZ_LH = lband_base(KS) * 16;                          // bytes per head
     static constexpr bool L_LDS = CB_LDS && HPT * SZ_LH <= SZ_R1;
     static constexpr int SMEM = SZ_R1 + SZ_BC + SZ_V;
+    // fused kernel's workgroups per CU: 64-token chunks leave room (LDS and, at most 168, registers)
+    // for three
+    static constexpr int OCC = Q == 64 ? 3 : 2;
     static_assert(Q % 32 == 0 && Q <= 256, "Q must be a multiple of 32, at most 256");
     static_assert(N % 32 == 0, "N % 32 == 0");
 };
