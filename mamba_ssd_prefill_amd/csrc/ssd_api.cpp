@@ -465,15 +465,16 @@ static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt
         // state entering chunk 0 is ready -- in the relay form its relay waves publish it)
         // the 16-bit tile keeps p in its interleaved order; the fp32 tile in plain order
         const int es = (int)elem_size(p->state_dtype), K = a.slots, pperm = p->in_dtype != SSD_F32;
-        e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, p->dstate, K, 0, es,
-                                  pperm, a.flags, l.nsync, l.nflags, (uint32_t)ssd::kChainStride, a.relay ? 0u : 1u,
-                                  st);
+        const int pw = ssd::p_per_wave(p->headdim);
+        e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, pw, p->dstate, K, 0,
+                                  es, pperm, a.flags, l.nsync, l.nflags, (uint32_t)ssd::kChainStride,
+                                  a.relay ? 0u : 1u, st);
         if (e == hipSuccess) e = mark(ev_begin);
         if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED, p, a, st);
         if (e == hipSuccess) e = mark(ev_end);
         // final state out of the last chunk's slot (the relay form keeps it in slot 1)
         if (e == hipSuccess)
-            e = ssd::launch_ring_copy(a.states, final_state, 0, p->batch, p->nheads, p->headdim, p->dstate, K,
+            e = ssd::launch_ring_copy(a.states, final_state, 0, p->batch, p->nheads, p->headdim, pw, p->dstate, K,
                                       a.relay ? 1 : l.w.nchunks % K, es, pperm, nullptr, 0, 0, 1, 0u, st);
         return hip_status(e);
     }

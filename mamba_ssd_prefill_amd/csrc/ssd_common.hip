@@ -54,55 +54,59 @@ __global__ __launch_bounds__(256) void k_boundary(const char* src, size_t src_bs
 // (the progress counters of every chain, one per relay wave: 1 = the state entering chunk 0
 // is ready), else 0.
 __global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, int to_ring, int B, int H, int P,
-                                                    int N, int K, int slot, int es, int pperm, uint32_t* sync,
-                                                    size_t nsync, size_t nflags, uint32_t flag_period,
-                                                    uint32_t flag_init) {
-    const int PW = P < 32 ? P : 32, WPH = P / PW, MBP = PW / 16, NB = N / 16;
+                                                    int PW, int N, int K, int slot, int es, int pperm,
+                                                    uint32_t* sync, size_t nsync, size_t nflags,
+                                                    uint32_t flag_period, uint32_t flag_init) {
+    const int WPH = P / PW, MBP = PW / 16, NB = N / 16;
+    const int n4 = N / 4, per_bh = P * n4;  // items (4 consecutive n) per (b, h); P, N powers of 2
+    const int nsh = __builtin_ctz((unsigned)n4);
     // no initial state: the fused kernel never reads slot 0 before writing it, so nothing to copy
-    const size_t total = (to_ring && src == nullptr) ? 0 : (size_t)B * H * P * (N / 4);
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-        const int n = (int)(i % (N / 4)) * 4;
-        const size_t r = i / (N / 4);
-        const int p = (int)(r % P);
-        const int h = (int)((r / P) % H);
-        const int b = (int)(r / ((size_t)P * H));
-        const int ph = p / PW, pw = p % PW;
-        int pb = pw / 16, r16 = pw % 16;
-        if (pperm) {
-            const int q8 = pw / (4 * MBP), rem = pw % (4 * MBP);
-            pb = rem >> 2;
-            r16 = 4 * q8 + (rem & 3);
-        }
-        const int nb = n / 16, q = (n % 16) / 4;
-        const size_t ring = ring_chain(b, slot, h, ph, K, H, WPH, NB * MBP) + ((size_t)(nb * MBP + pb) * 64 + 16 * q + r16) * 4;
-        const size_t user = (((size_t)b * H + h) * P + p) * N + n;
-        const size_t from = to_ring ? user : ring, to = to_ring ? ring : user;
-        if (es == 4) {
-            uint4 v = {0u, 0u, 0u, 0u};
-            if (src) v = *(const uint4*)(src + from * 4);
-            *(uint4*)(dst + to * 4) = v;
-        } else {
-            uint2 v = {0u, 0u};
-            if (src) v = *(const uint2*)(src + from * 2);
-            *(uint2*)(dst + to * 2) = v;
+    const size_t nbh = (to_ring && src == nullptr) ? 0 : (size_t)B * H;
+    // one workgroup per (b, h) at a time, 32-bit index arithmetic inside it
+    for (size_t bh = blockIdx.x; bh < nbh; bh += gridDim.x) {
+        const int b = (int)(bh / (size_t)H), h = (int)(bh - (size_t)b * H);
+        const size_t user0 = bh * P * N;
+        for (int e = threadIdx.x; e < per_bh; e += 256) {
+            const int p = e >> nsh, n = (e & (n4 - 1)) * 4;
+            const int ph = p / PW, pw = p - ph * PW;
+            int pb = pw >> 4, r16 = pw & 15;
+            if (pperm) {
+                const int q8 = pw / (4 * MBP), rem = pw - q8 * 4 * MBP;
+                pb = rem >> 2;
+                r16 = 4 * q8 + (rem & 3);
+            }
+            const int nb = n >> 4, q = (n & 15) >> 2;
+            const size_t ring =
+                ring_chain(b, slot, h, ph, K, H, WPH, NB * MBP) + (size_t)(((nb * MBP + pb) * 64 + 16 * q + r16) * 4);
+            const size_t user = user0 + (size_t)(p * N + n);
+            const size_t from = to_ring ? user : ring, to = to_ring ? ring : user;
+            if (es == 4) {
+                uint4 v = {0u, 0u, 0u, 0u};
+                if (src) v = *(const uint4*)(src + from * 4);
+                *(uint4*)(dst + to * 4) = v;
+            } else {
+                uint2 v = {0u, 0u};
+                if (src) v = *(const uint2*)(src + from * 2);
+                *(uint2*)(dst + to * 2) = v;
+            }
         }
     }
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsync; i += stride)
         sync[i] = (i < nflags && (i % flag_period) < 4u) ? flag_init : 0u;
 }
 
-hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int N, int K, int slot,
-                            int es, int pperm, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
-                            uint32_t flag_init, hipStream_t st) {
-    const size_t work = (size_t)B * H * P * (N / 4);
-    const size_t big = work > nsync ? work : nsync;
-    size_t grid = (big + 255) / 256;
+hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int PW, int N, int K,
+                            int slot, int es, int pperm, uint32_t* sync, size_t nsync, size_t nflags,
+                            uint32_t flag_period, uint32_t flag_init, hipStream_t st) {
+    const size_t bh = (size_t)B * H, sync_blocks = (nsync + 255) / 256;
+    size_t grid = bh > sync_blocks ? bh : sync_blocks;
     if (grid < 1) grid = 1;
     if (grid > 8192) grid = 8192;
     const char* s = (const char*)src;
     char* d = (char*)dst;
-    void* args[] = {&s, &d, &to_ring, &B, &H, &P, &N, &K, &slot, &es, &pperm, &sync, &nsync, &nflags, &flag_period, &flag_init};
+    void* args[] = {&s, &d, &to_ring, &B, &H, &P, &PW, &N, &K, &slot, &es, &pperm, &sync, &nsync, &nflags,
+                    &flag_period, &flag_init};
     return hipLaunchKernel((const void*)&k_ring_copy, dim3((unsigned)grid), dim3(256), args, 0, st);
 }
 
