@@ -135,7 +135,8 @@ def traffic(fetch_dir, write_dir, workload, chunk, out, fetch_cmd, write_cmd):
 
 
 def counters(d, out, command):
-    """Per-kernel averages of every counter of one --pmc run, and per-wave ratios."""
+    """Per-kernel averages of every counter of one --pmc run, with per-wave instruction counts
+    (when SQ_WAVES was collected) or the share of wave cycles (when SQ_WAVE_CYCLES was)."""
     acc = {}
     for r in _rows(d, "*counter_collection.csv"):
         k = short(r["Kernel_Name"])
@@ -143,17 +144,25 @@ def counters(d, out, command):
             continue
         acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     names = sorted({c for v in acc.values() for c in v})
+    per_wave = [c for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS") if c in names and "SQ_WAVES" in names]
+    shares = [c for c in names if "SQ_WAVE_CYCLES" in names and c.startswith(("SQ_WAIT", "SQ_ACTIVE"))]
+    extra = ["%s per wave" % c[len("SQ_INSTS_"):] for c in per_wave] + ["%s share" % c[len("SQ_"):] for c in shares]
+    if per_wave:
+        note = "Average per dispatch; the `per wave` columns divide by SQ_WAVES."
+    else:
+        note = "Average per dispatch; the `share` columns divide by SQ_WAVE_CYCLES (the fraction of its life a wave spends so)."
     lines = ["# SQ counters: %s" % os.path.basename(out).rsplit(".", 1)[0], "",
-             "Command (from the repository root, on one MI355X):", "", "    " + command, "",
-             "Average per dispatch; the `per wave` columns divide by SQ_WAVES.", "",
-             "| kernel | " + " | ".join(names) + " | VALU per wave | MFMA per wave | LDS per wave |",
-             "|---|" + "---:|" * (len(names) + 3)]
+             "Command (from the repository root, on one MI355X):", "", "    " + command, "", note, "",
+             "| kernel | " + " | ".join(names + extra) + " |",
+             "|---|" + "---:|" * (len(names) + len(extra))]
     for k, v in sorted(acc.items()):
         avg = {c: sum(x) / len(x) for c, x in v.items()}
         wv = avg.get("SQ_WAVES", 0.0) or 1.0
-        lines.append("| %s | %s | %.0f | %.0f | %.0f |" % (
-            k, " | ".join("%.4g" % avg.get(c, float("nan")) for c in names), avg.get("SQ_INSTS_VALU", 0) / wv,
-            avg.get("SQ_INSTS_MFMA", 0) / wv, avg.get("SQ_INSTS_LDS", 0) / wv))
+        wc = avg.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+        cells = ["%.4g" % avg.get(c, float("nan")) for c in names]
+        cells += ["%.0f" % (avg.get(c, 0.0) / wv) for c in per_wave]
+        cells += ["%.3f" % (avg.get(c, 0.0) / wc) for c in shares]
+        lines.append("| %s | %s |" % (k, " | ".join(cells)))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
