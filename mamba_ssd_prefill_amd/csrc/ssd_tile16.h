@@ -112,18 +112,21 @@ __device__ inline void dma_rows(void* lds_tile, __amdgpu_buffer_rsrc_t rs_src, i
 // 4 rows down completes the 8 tokens of the MFMA k slots.  The swizzle of those rows does not
 // depend on k0 (a multiple of 32) nor on the +4, so the lane offset for k0 = 0 is computed once
 // per column block and each k step is a constant offset.
-template <int COLS> __device__ inline int tr_lane_off(int col0) {
+// tr_lane_offs: the lane offsets of column blocks 0, 16, .. 16 (NBK - 1); tr_lane_offs_p: those
+// of the x operand's p blocks 0 .. MBP - 1 in the interleaved column order of Geo16::pcol (the
+// four column quads of p block pb start at c0 + 4 MBP jj + 4 pb).  One read of the lane id
+// each, so the compiler shares the row part.
+template <int COLS, int NBK> __device__ inline void tr_lane_offs(int (&off)[NBK]) {
     const int lane = tid_here() & 63;
     const int q = lane >> 4, m = (lane & 15) >> 2, jj = lane & 3;
-    return sw_off<COLS>(8 * q + m, col0 + 4 * jj);
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb) off[nb] = sw_off<COLS>(8 * q + m, nb * 16 + 4 * jj);
 }
-
-// tr_lane_off for the x operand in the interleaved column order of Geo16::pcol: the four
-// column quads of p block pb start at c0 + 4 MBP jj + 4 pb.
-template <int COLS, int MBP> __device__ inline int tr_lane_off_p(int c0, int pb) {
+template <int COLS, int MBP> __device__ inline void tr_lane_offs_p(int c0, int (&off)[MBP]) {
     const int lane = tid_here() & 63;
     const int q = lane >> 4, m = (lane & 15) >> 2, jj = lane & 3;
-    return sw_off<COLS>(8 * q + m, c0 + 4 * MBP * jj + 4 * pb);
+#pragma unroll
+    for (int pb = 0; pb < MBP; ++pb) off[pb] = sw_off<COLS>(8 * q + m, c0 + 4 * MBP * jj + 4 * pb);
 }
 
 template <typename T, int COLS> __device__ inline typename TT<T>::frag tr_frag_at(const T* tile, int lane_off, int k0) {
@@ -399,10 +402,14 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
 
     // x operand, token-major: xf[kk][pb] holds x[kk*32 + 8q .. +7][ph*PW + pcol(pb, r16)]
     frag xf[KS][MBP];
+    {
+        int xo[MBP];
+        tr_lane_offs_p<P, MBP>(ph * PW, xo);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
+        for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int pb = 0; pb < MBP; ++pb) xf[kk][pb] = tr_frag_at<T, P>(sX + hs * Q * P, tr_lane_off_p<P, MBP>(ph * PW, pb), kk * 32);
+            for (int pb = 0; pb < MBP; ++pb) xf[kk][pb] = tr_frag_at<T, P>(sX + hs * Q * P, xo[pb], kk * 32);
+    }
 
     // S_c in accumulator layout, rounded to T: tile (nb, pb), lane -> S[p = ph*PW + pcol(pb, r16)][n = nb*16 + 4q + r]
     v4 scb[NB][MBP];
@@ -415,8 +422,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
 #pragma unroll
             for (int pb = 0; pb < MBP; ++pb) acc[nb][pb] = vzero<f32x4>();
         int boff[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) boff[nb] = tr_lane_off<N>(nb * 16);
+        tr_lane_offs<N, NB>(boff);
         if (hvalid) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
