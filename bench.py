@@ -59,18 +59,20 @@ def measured_traffic(workload, Q):
     return t.get("bytes_per_launch")
 
 
-def time_impl(ssd, torch, g, w, Q, impl, steps, warmup):
+def time_impl(ssd, torch, g, w, Q, impl, steps, warmup, state_dtype=None):
     """Warm up, then time `steps` calls; returns (ms per call, mean kernel ms)."""
+    sd_name = state_dtype or w.state_dtype
     prm = ssd.make_params(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, Q, w.dtype,
-                          w.state_dtype, True, impl)
+                          sd_name, True, impl)
     ws = ssd.alloc_workspace(prm, g.x.device)
     y = torch.empty_like(g.x)
-    sdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.state_dtype]
+    sdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[sd_name]
     fin = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=sdt, device=g.x.device)
+    h0 = g.h0.to(sdt) if g.h0 is not None else None
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
 
     def call(ev=None):
-        ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=Q, impl=impl,
+        ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, h0, chunk_size=Q, impl=impl,
                         state_dtype=sdt, workspace=ws, y=y, final_state=fin, kernel_events=ev)
 
     for _ in range(warmup):
@@ -87,6 +89,57 @@ def time_impl(ssd, torch, g, w, Q, impl, steps, warmup):
         raise RuntimeError("device status %d after %s Q=%d" % (status, impl, Q))
     del ws, y, fin
     return wall, kms
+
+
+def decode_bytes(w, batch):
+    """Algorithmic HBM bytes of one decode step: the state read and written once, x, dt, B, C
+    read and y written once, and the per-head parameters."""
+    e, es = ESZ[w.dtype], ESZ[w.state_dtype]
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    return 2 * batch * H * P * N * es + batch * (2 * H * P * e + H * e + 2 * G * N * e) + 3 * H * 4
+
+
+def time_decode(ssd, torch, w, batch, steps):
+    """`steps` consecutive ssd_decode_step calls (one token per batch row each, a new token per
+    step, the state updated in place) captured in one HIP graph and replayed, bracketed by HIP
+    events on the replay stream; returns microseconds per step.  The graph keeps the host out of
+    the timed region, as a decode loop on the device would."""
+    gen = torch.Generator().manual_seed(77)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    dev = "cuda:0"
+    x = torch.randn(steps, batch, H, P, generator=gen).to(tdt[w.dtype]).to(dev)
+    dt = torch.randn(steps, batch, H, generator=gen).to(tdt[w.dtype]).to(dev)
+    Bm = (torch.randn(steps, batch, G, N, generator=gen) / N ** 0.5).to(tdt[w.dtype]).to(dev)
+    Cm = (torch.randn(steps, batch, G, N, generator=gen) / N ** 0.5).to(tdt[w.dtype]).to(dev)
+    A = (-torch.exp(torch.rand(H, generator=gen) * 2.77)).to(dev)
+    D = torch.randn(H, generator=gen).to(dev)
+    bias = torch.full((H,), -4.0).to(dev)
+    state = (0.1 * torch.randn(batch, H, P, N, generator=gen)).to(tdt[w.state_dtype]).to(dev)
+    ys = torch.empty(steps, batch, H, P, dtype=tdt[w.dtype], device=dev)
+
+    def run():
+        for i in range(steps):
+            ssd.ssd_decode_step(x[i], dt[i], A, Bm[i], Cm[i], D, bias, state, y=ys[i])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * steps)
 
 
 def cpu_baseline(inp, w, seconds):
@@ -201,7 +254,29 @@ def main():
             fw, fk = time_impl(ssd, torch, g, w, q, "fused", max(5, args.steps // 2), 2)
             uw, uk = time_impl(ssd, torch, g, w, q, "unfused", max(5, args.steps // 2), 2)
             sweep[str(q)] = {"fused_ms": fw, "unfused_ms": uw, "fused_kernel_ms": fk}
+        for q, v in sweep.items():
+            # the roofline fraction of the fused kernel at this chunk size (its own algorithmic bytes)
+            c_q, x_q, _ = algorithmic(w, int(q), inp.h0 is not None)
+            v["frac"] = (c_q + x_q) / (v.get("fused_kernel_ms", f_kms) / 1e3) / 1e9 / HBM_PEAK_GBS
         out["chunk_sweep"] = sweep
+        if w.state_dtype == "f32" and w.dtype != "f32":
+            # the same call with the inter-chunk states (and h0 / final state) stored in fp16
+            log("fp16 state Q=%d" % Q)
+            hw, hk = time_impl(ssd, torch, g, w, Q, "fused", max(5, args.steps // 2), 2, state_dtype="f16")
+            c16, x16, _ = algorithmic(w.with_(state_dtype="f16"), Q, inp.h0 is not None)
+            out["state_f16"] = {"fused_ms": hw, "fused_kernel_ms": hk, "value": tokens / (hw / 1e3),
+                                "frac": (c16 + x16) / (hk / 1e3) / 1e9 / HBM_PEAK_GBS}
+        dec = {}
+        for bsz in (w.batch, 16 * w.batch):
+            log("decode step, batch %d" % bsz)
+            us = time_decode(ssd, torch, w, bsz, 100 if bsz == w.batch else 20)
+            nb = decode_bytes(w, bsz)
+            dec["batch%d" % bsz] = {"us_per_step": us, "tokens_per_s": bsz / (us / 1e6), "bytes": nb,
+                                    "achieved_gbs": nb / (us / 1e6) / 1e9,
+                                    "frac": nb / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
+        out["decode"] = {"kernel": "k_decode", "bound": "hbm", "peak_gbs": HBM_PEAK_GBS,
+                         "state_dtype": w.state_dtype, "timing": "HIP events around replays of a HIP graph of consecutive steps",
+                         **dec}
     del g
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -211,6 +211,45 @@ ssd_status_t ssd_step_chunk_scan(const ssd_params_t* p, const void* x, const voi
                                  const float* D, void* y, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Single-token decode step ("Mamba-2状态空间模型的编译器优化与实现", section 2.1: the
+ * cache holds the [B,H,P,N] SSM state and each generated token applies the recurrence
+ * once; section 3.2: the step is bound by memory bandwidth and runs as one pass over
+ * HBM).  It is exactly one token of the recurrence at the top of this header, started
+ * from state_in and ending in state_out:
+ *
+ *     dt = softplus(dt_raw[b,h] + dt_bias[h])   (dt_softplus = 1)
+ *     S  = exp(dt * A[h]) * state_in[b,h] + dt * x[b,h,:] (outer) B[b,g,:]
+ *     y[b,h,:] = S . C[b,g,:] + D[h] * x[b,h,:],   state_out[b,h] = S   (g = h / (H / G))
+ *
+ * so ssd_prefill of L tokens followed by ssd_decode_step on the next tokens, each
+ * taking the previous final state, equals ssd_prefill of the longer sequence.
+ *
+ * Parameters: *p as for ssd_prefill except that p->seqlen must be 1 (one token per
+ * batch row; SSD_ERR_INVALID_SHAPE otherwise), p->headdim may be any P >= 1, p->dstate
+ * must be one of 16, 32, 64, 128, 256 (SSD_ERR_UNSUPPORTED otherwise), and chunk_size
+ * and impl are ignored.
+ *
+ * Tensor arguments (device pointers; the layouts are ssd_prefill's with L = 1):
+ *   x          [B, H, P]     in_dtype     required, 16-byte aligned
+ *   dt         [B, H]        in_dtype     required (raw step, before bias / softplus)
+ *   A          [H]           fp32         required (A <= 0, not checked)
+ *   B, C       [B, G, N]     in_dtype     required, 16-byte aligned
+ *   D, dt_bias [H]           fp32         NULL means 0
+ *   state_in   [B, H, P, N]  state_dtype  NULL means 0; 16-byte aligned
+ *   state_out  [B, H, P, N]  state_dtype  required, 16-byte aligned; may be the same
+ *                                         buffer as state_in (in-place update); any other
+ *                                         overlap with state_in is undefined
+ *   y          [B, H, P]     in_dtype     required output, 16-byte aligned
+ * The update runs in fp32 and rounds the state to state_dtype once.  No workspace, no
+ * allocation, no synchronisation; one kernel on `stream`.  Errors as for ssd_prefill
+ * (validated on the host before the launch). */
+ssd_status_t ssd_decode_step(const ssd_params_t* p,
+                             const void* x, const void* dt, const float* A,
+                             const void* B, const void* C,
+                             const float* D, const float* dt_bias,
+                             const void* state_in, void* state_out, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,7 +13,7 @@ import os
 
 __all__ = ["ssd_prefill", "workspace_size", "workspace_layout", "Params", "SSDError", "library_path",
            "load_library", "step_chunk_cumsum", "step_bmm", "step_chunk_state", "step_state_passing",
-           "step_chunk_scan", "check_device_status", "make_params", "EXPORTED_SYMBOLS"]
+           "step_chunk_scan", "check_device_status", "make_params", "ssd_decode_step", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.environ.get("MAMBA_SSD_LIB", os.path.join(_HERE, "libmamba_ssd.so"))
@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_INVALID_SHAP
 EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill", "ssd_prefill_timed",
                     "ssd_check_device_status",
                     "ssd_status_string", "ssd_workspace_layout", "ssd_step_chunk_cumsum", "ssd_step_bmm",
-                    "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan"]
+                    "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan", "ssd_decode_step"]
 
 
 class SSDError(RuntimeError):
@@ -94,8 +94,9 @@ def load_library():
     lib.ssd_step_chunk_state.argtypes = [P, vp, vp, vp, sz, vp]
     lib.ssd_step_state_passing.argtypes = [P, vp, vp, vp, sz, vp]
     lib.ssd_step_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in ("ssd_step_chunk_cumsum", "ssd_step_bmm", "ssd_step_chunk_state", "ssd_step_state_passing",
-              "ssd_step_chunk_scan"):
+              "ssd_step_chunk_scan", "ssd_decode_step"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -252,3 +253,51 @@ def step_chunk_scan(params, x, C, D, y, workspace):
     _check(load_library().ssd_step_chunk_scan(ctypes.byref(params), _ptr(x), _ptr(C), _ptr(D), _ptr(y),
                                               _ptr(workspace), workspace.numel(), _stream(x.device)),
            "ssd_step_chunk_scan")
+
+
+# ---- single-token decode step ----------------------------------------------------------------
+def ssd_decode_step(x, dt, A, B, C, D=None, dt_bias=None, state=None, state_dtype=None, dt_softplus=True,
+                    out_state=None, y=None):
+    """One token of the recurrence per batch row on a cached state (ssd_decode_step in the C
+    ABI); returns (y[B,H,P], new_state[B,H,P,N]).
+
+    x [B,H,P], dt [B,H], B and C [B,G,N] (x's dtype); A, D, dt_bias [H] float32; ``state``
+    [B,H,P,N] (None: zeros) in ``state_dtype`` (default: state's dtype, else float32).
+    ``out_state`` receives the new state (default: ``state`` itself, updated in place, or a
+    new tensor when ``state`` is None)."""
+    import torch
+    Bt, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_decode_step needs device tensors (got %s)" % dev)
+    if state_dtype is None:
+        state_dtype = state.dtype if state is not None else torch.float32
+    want = {"dt": (dt, (Bt, H)), "B": (B, (Bt, G, N)), "C": (C, (Bt, G, N)), "A": (A, (H,)), "D": (D, (H,)),
+            "dt_bias": (dt_bias, (H,)), "state": (state, (Bt, H, P, N)), "out_state": (out_state, (Bt, H, P, N)),
+            "y": (y, (Bt, H, P))}
+    for name, (t, shape) in want.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous tensor on %s" % (name, dev))
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("y", y)):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("%s must have x's dtype %s" % (name, x.dtype))
+    for name, t in (("state", state), ("out_state", out_state)):
+        if t is not None and t.dtype != state_dtype:
+            raise ValueError("%s dtype %s != state_dtype %s" % (name, t.dtype, state_dtype))
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    sd = {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[state_dtype]
+    prm = make_params(Bt, 1, H, P, N, G, 128, _dtype_code(x), sd, dt_softplus, "fused")
+    if out_state is None:
+        out_state = state if state is not None else torch.empty((Bt, H, P, N), dtype=state_dtype, device=dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(load_library().ssd_decode_step(ctypes.byref(prm), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                          _ptr(dt_bias), _ptr(state), _ptr(out_state), _ptr(y), _stream(dev)),
+           "ssd_decode_step")
+    return y, out_state

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmamba_ssd.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["ssd_api.cpp", "ssd_common.hip", "ssd_kernels_f32.hip", "ssd_kernels_f16.hip", "ssd_kernels_bf16.hip",
+SOURCES = ["ssd_api.cpp", "ssd_common.hip", "ssd_decode.hip", "ssd_kernels_f32.hip", "ssd_kernels_f16.hip", "ssd_kernels_bf16.hip",
            "ssd_kernels_f16_q64.hip", "ssd_kernels_f16_q128.hip", "ssd_kernels_f16_q256.hip",
            "ssd_kernels_bf16_q64.hip", "ssd_kernels_bf16_q128.hip", "ssd_kernels_bf16_q256.hip"]
 

@@ -520,3 +520,57 @@ SSD_EXPORT ssd_status_t ssd_check_device_status(const ssd_params_t* p, const voi
         return SSD_ERR_HIP;
     return word == 0 ? SSD_OK : (ssd_status_t)word;
 }
+
+// ---- the single-token decode step -----------------------------------------------------------
+
+namespace {
+
+ssd_status_t validate_decode(const ssd_params_t* p) {
+    if (!p) return SSD_ERR_NULL_POINTER;
+    if (p->struct_size < sizeof(ssd_params_t)) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->in_dtype < SSD_F32 || p->in_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->state_dtype < SSD_F32 || p->state_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->dt_softplus != 0 && p->dt_softplus != 1) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->batch < 1 || p->seqlen != 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1 || p->ngroups < 1)
+        return SSD_ERR_INVALID_SHAPE;
+    if (p->nheads % p->ngroups) return SSD_ERR_INVALID_SHAPE;
+    const int N = p->dstate;
+    if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return SSD_ERR_UNSUPPORTED;
+    const int64_t rb = ssd::decode_rows_per_block(N);
+    const int64_t blocks = (int64_t)p->batch * p->nheads * ((p->headdim + rb - 1) / rb);
+    if (blocks >= (int64_t)1 << 31) return SSD_ERR_INVALID_SHAPE;
+    return SSD_OK;
+}
+
+}  // namespace
+
+SSD_EXPORT ssd_status_t ssd_decode_step(const ssd_params_t* p, const void* x, const void* dt, const float* A,
+                                        const void* B, const void* C, const float* D, const float* dt_bias,
+                                        const void* state_in, void* state_out, void* y, void* stream) {
+    const ssd_status_t s = validate_decode(p);
+    if (s != SSD_OK) return s;
+    if (!x || !dt || !A || !B || !C || !state_out || !y) return SSD_ERR_NULL_POINTER;
+    const size_t es = elem_size(p->in_dtype);
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(state_out, 16) ||
+        !aligned(state_in, 16) || !aligned(dt, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4))
+        return SSD_ERR_MISALIGNED;
+    ssd::DecodeArgs a{};
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.dt_bias = dt_bias;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.y = y;
+    a.batch = p->batch;
+    a.nheads = p->nheads;
+    a.headdim = p->headdim;
+    a.dstate = p->dstate;
+    a.ngroups = p->ngroups;
+    a.state_dtype = p->state_dtype;
+    a.softplus = p->dt_softplus;
+    return hip_status(ssd::launch_decode(a, p->in_dtype, (hipStream_t)stream));
+}

@@ -91,6 +91,28 @@ hipError_t launch_step_bf16_q64(int step, int P, int N, SsdArgs& a, hipStream_t 
 hipError_t launch_step_bf16_q128(int step, int P, int N, SsdArgs& a, hipStream_t st);
 hipError_t launch_step_bf16_q256(int step, int P, int N, SsdArgs& a, hipStream_t st);
 
+// Argument block of the single-token decode step (ssd_decode.hip); layouts in mamba_ssd.h.
+struct DecodeArgs {
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* dt_bias;
+    const void* state_in;  // nullptr: zero state
+    void* state_out;       // may equal state_in
+    void* y;
+    int batch, nheads, headdim, dstate, ngroups, state_dtype, softplus;
+};
+
+// State rows of P one decode workgroup covers (kDecodeIter loads per lane, 256 / N rows each).
+constexpr int kDecodeIter = 4;
+inline int decode_rows_per_block(int N) { return 4 * kDecodeIter * (256 / N); }
+
+// The decode step for dstate N in {16, 32, 64, 128, 256}; hipErrorNotSupported otherwise.
+hipError_t launch_decode(DecodeArgs& a, int in_dtype, hipStream_t st);
+
 // Non-templated kernels (ssd_common.hip).
 hipError_t launch_state_passing(SsdArgs& a, int PN, hipStream_t st);
 hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int PW, int N, int K,

@@ -7,6 +7,7 @@ imports, links or calls it, and it shares no code with the HIP library.
 * ``recurrence``  -- the definition: the sequential per-token recurrence (C, fp64).
 * ``chunked``     -- the five-step chunked algorithm with its intermediates (C, fp64).
 * ``quadratic``   -- the brute-force masked-matrix form (numpy, fp64, tiny inputs).
+* ``decode_step`` -- one token of the recurrence on a cached state (the decode step).
 
 Inputs may be torch CPU tensors or numpy arrays; 16-bit tensors are passed to C
 as their raw bits and widened exactly there.
@@ -190,6 +191,18 @@ def chunked(x, dt, A, B, C, D=None, dt_bias=None, h0=None, dt_softplus=True, chu
     if rc != 0:
         raise ValueError("ssd_oracle_chunked rejected its arguments")
     return out
+
+
+def decode_step(x, dt, A, B, C, D=None, dt_bias=None, state=None, dt_softplus=True):
+    """One autoregressive step: the recurrence over a single token per batch row, started from
+    ``state`` ("Mamba-2状态空间模型的编译器优化与实现", section 2.1: the cached [B,H,P,N] state is
+    updated once per generated token).  x [B,H,P], dt [B,H], B/C [B,G,N], state [B,H,P,N] or
+    None (zeros).  Returns ``(y[B,H,P], new_state[B,H,P,N])`` in fp64."""
+    Bt, H, P = (int(s) for s in x.shape)
+    G, N = int(B.shape[1]), int(B.shape[2])
+    y, fin = recurrence_full(x.reshape(Bt, 1, H, P), dt.reshape(Bt, 1, H), A, B.reshape(Bt, 1, G, N),
+                             C.reshape(Bt, 1, G, N), D, dt_bias, state, dt_softplus)
+    return y.reshape(Bt, H, P), fin
 
 
 def widen(t):

@@ -210,3 +210,47 @@ def test_python_binding_refuses_cpu_tensors():
     B = torch.zeros(1, 64, 1, 16)
     with pytest.raises(ValueError):
         ssd.ssd_prefill(x, torch.zeros(1, 64, 4), torch.zeros(4), B, B.clone())
+
+
+# ---- the decode step: host validation only (every call fails one check, nothing launches) -----
+def dec_params(**kw):
+    p = dict(batch=2, seqlen=1, nheads=8, headdim=64, dstate=128, ngroups=2, chunk_size=128,
+             in_dtype="bf16", state_dtype="f32", dt_softplus=True, impl="fused")
+    p.update(kw)
+    return ssd.make_params(**p)
+
+
+DEC_FIELDS = ["x", "dt", "A", "B", "C", "D", "dt_bias", "state_in", "state_out", "y"]
+
+
+def dec_call(lib, prm, **override):
+    ptrs = {f: 0x10000 * (i + 1) for i, f in enumerate(DEC_FIELDS)}
+    ptrs.update(override)
+    return lib.ssd_decode_step(ctypes.byref(prm), *[ptrs[f] for f in DEC_FIELDS], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seqlen=2), SHAPE), (dict(seqlen=0), SHAPE), (dict(batch=0), SHAPE), (dict(nheads=0), SHAPE),
+    (dict(headdim=0), SHAPE), (dict(ngroups=3), SHAPE), (dict(dstate=48), UNSUP), (dict(dstate=512), UNSUP),
+    (dict(dstate=8), UNSUP), (dict(in_dtype=3), BADARG), (dict(state_dtype=5), BADARG),
+])
+def test_decode_rejects_bad_params(lib, kw, code):
+    assert dec_call(lib, dec_params(**kw)) == code
+
+
+@pytest.mark.parametrize("field", ["x", "dt", "A", "B", "C", "state_out", "y"])
+def test_decode_null_pointers(lib, field):
+    assert dec_call(lib, dec_params(), **{field: None}) == NULLP
+
+
+@pytest.mark.parametrize("field,off", [("x", 8), ("B", 4), ("C", 2), ("y", 8), ("state_in", 8), ("state_out", 4),
+                                       ("A", 2), ("D", 1), ("dt_bias", 2), ("dt", 1)])
+def test_decode_misaligned(lib, field, off):
+    assert dec_call(lib, dec_params(), **{field: 0x10000 * (DEC_FIELDS.index(field) + 1) + off}) == MISAL
+
+
+def test_decode_short_struct(lib):
+    p = dec_params()
+    p.struct_size = 8
+    assert dec_call(lib, p) == BADARG
+    assert lib.ssd_decode_step(None, *([0x10000] * 10), None) == NULLP

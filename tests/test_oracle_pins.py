@@ -304,3 +304,39 @@ def test_golden_hand_example(oracle_mod):
                                         dt_softplus=False)
     assert np.allclose(y, np.array(g["y"]), rtol=0, atol=1e-12)
     assert np.allclose(fin, np.array(g["final"]), rtol=0, atol=1e-12)
+
+
+def test_decode_steps_continue_a_prefill(oracle_mod):
+    """The decode step ("Mamba-2状态空间模型的编译器优化与实现", section 2.1): k single-token
+    steps from a prefix's final state reproduce the last k tokens of one long run."""
+    inp = small(seed=20, Bt=2, L=29, H=4, G=2, dt_scale=2.0)
+    y, fin = oracle_mod.recurrence_full(**inp.args())
+    L0 = 25
+    pre = dict(inp.args())
+    for k in ("x", "dt", "B", "C"):
+        pre[k] = pre[k][:, :L0].contiguous()
+    _, state = oracle_mod.recurrence_full(**pre)
+    for t in range(L0, 29):
+        # the state enters as fp32 (its storage dtype): 2^-24 relative per step
+        yt, state = oracle_mod.decode_step(inp.x[:, t].contiguous(), inp.dt[:, t].contiguous(), inp.A,
+                                           inp.B[:, t].contiguous(), inp.C[:, t].contiguous(), inp.D, inp.dt_bias,
+                                           torch.from_numpy(state).float(), inp.dt_softplus)
+        assert yt.shape == (2, 4, 3)
+        assert rel_err(yt, y[:, t]) < 1e-6
+    assert rel_err(state, fin) < 1e-6
+
+
+def test_decode_step_by_hand(oracle_mod):
+    """One decode step for one (b, h), written out: S' = exp(dt A) S + dt x (outer) B,
+    y = S' C + D x, with dt = softplus(dt_raw + dt_bias) and group g = h / (H / G)."""
+    inp = small(seed=21, Bt=2, L=1, H=4, G=2, dt_scale=3.0)
+    x, dt, Bm, Cm = inp.x[:, 0], inp.dt[:, 0], inp.B[:, 0], inp.C[:, 0]
+    y, S = oracle_mod.decode_step(x, dt, inp.A, Bm, Cm, inp.D, inp.dt_bias, inp.h0, True)
+    b, h = 1, 3
+    g = h // 2
+    d = math.log1p(math.exp(float(dt[b, h]) + float(inp.dt_bias[h])))
+    a = math.exp(d * float(inp.A[h]))
+    Sref = a * f64(inp.h0)[b, h] + d * np.outer(f64(x)[b, h], f64(Bm)[b, g])
+    yref = Sref @ f64(Cm)[b, g] + float(inp.D[h]) * f64(x)[b, h]
+    assert rel_err(S[b, h], Sref) < REL
+    assert rel_err(y[b, h], yref) < REL
