@@ -142,6 +142,67 @@ def time_decode(ssd, torch, w, batch, steps):
     return e0.elapsed_time(e1) * 1e3 / (reps * steps)
 
 
+def time_varlen(ssd, torch, steps):
+    """The many-short-sequences workload (32 sequences of 1024 tokens, H=128, G=8, bf16, Q=128)
+    two ways: as a batch of 32 rows, and packed into one row of 32768 tokens told apart by
+    seq_idx (ssd_prefill_varlen).  Same tokens, same work; returns ms per call of each, fused."""
+    from mamba_ssd_prefill_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["short_g8_bf16"]
+    inp = workload_inputs(w)
+    g = inp.to("cuda:0")
+    Bt, L = w.batch, w.seqlen
+    packed = [t.reshape(1, Bt * L, *t.shape[2:]) for t in (g.x, g.dt, g.B, g.C)]
+    seq = torch.arange(Bt, dtype=torch.int32, device="cuda:0").repeat_interleave(L).reshape(1, Bt * L).contiguous()
+    res = {}
+    for name, args, kw in (("batched", (g.x, g.dt, g.A, g.B, g.C), {}),
+                           ("packed", (packed[0], packed[1], g.A, packed[2], packed[3]), {"seq_idx": seq})):
+        x = args[0]
+        prm = ssd.make_params(x.shape[0], x.shape[1], w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size,
+                              w.dtype, "f32", True, "fused")
+        ws = ssd.alloc_workspace(prm, x.device)
+        y = torch.empty_like(x)
+        fin = torch.empty(x.shape[0], w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=x.device)
+
+        def call():
+            ssd.ssd_prefill(*args, g.D, g.dt_bias, None, chunk_size=w.chunk_size, impl="fused", workspace=ws,
+                            y=y, final_state=fin, **kw)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        if ssd.check_device_status(prm, ws) != 0:
+            raise RuntimeError("device status after the %s short-sequence run" % name)
+        res[name] = e0.elapsed_time(e1) / steps
+    tokens = Bt * L
+    return {"workload": "32 sequences x 1024 tokens, H=128, P=64, N=128, G=8, bf16, Q=128",
+            "batched_ms": res["batched"], "packed_ms": res["packed"],
+            "batched_tokens_per_s": tokens / (res["batched"] / 1e3),
+            "packed_tokens_per_s": tokens / (res["packed"] / 1e3)}
+
+
+def copy_bandwidth(torch):
+    """Bytes read plus written per second of a 512 MiB device-to-device copy (torch's copy
+    kernel): what a plain streaming kernel reaches on this device, for context."""
+    src = torch.empty(1 << 27, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9
+
+
 def cpu_baseline(inp, w, seconds):
     """The fp64 oracle (as it stands) on whole (batch, head) chains of the same inputs,
     `threads` chains per call, until ~`seconds` have passed (whole passes repeat)."""
@@ -274,7 +335,10 @@ def main():
             dec["batch%d" % bsz] = {"us_per_step": us, "tokens_per_s": bsz / (us / 1e6), "bytes": nb,
                                     "achieved_gbs": nb / (us / 1e6) / 1e9,
                                     "frac": nb / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
+        log("packed variable-length input")
+        out["varlen"] = time_varlen(ssd, torch, 10)
         out["decode"] = {"kernel": "k_decode", "bound": "hbm", "peak_gbs": HBM_PEAK_GBS,
+                         "copy_gbs": copy_bandwidth(torch),
                          "state_dtype": w.state_dtype, "timing": "HIP events around replays of a HIP graph of consecutive steps",
                          **dec}
     del g

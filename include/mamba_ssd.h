@@ -123,6 +123,26 @@ ssd_status_t ssd_prefill_timed(const ssd_params_t* p,
                                void* workspace, size_t workspace_bytes, void* stream,
                                void* kernel_begin, void* kernel_end);
 
+/* Packed variable-length input ("Mamba-2炸裂升级！…", section "与vLLM的深度融合":
+ * several sequences share a batch row without padding and are told apart by a per-token
+ * sequence index, handled by masking).  Same as ssd_prefill, plus
+ *   seq_idx  [B, L]  int32  required, 4-byte aligned: a new sequence starts at every t > 0
+ *                           with seq_idx[b,t] != seq_idx[b,t-1]; the recurrence restarts
+ *                           there from S = 0.
+ * Each batch row's initial_state is the state entering its first sequence, and
+ * final_state[b] is the state after token L-1 (of its last sequence); sequences in the
+ * middle of a row start from zero and their end states are not written out.  The decay
+ * into a sequence start is exp(-128) = 0 in fp32 (the chunk_cumsum step adds -128 to that
+ * token's log-decay), so nothing crosses the boundary in any of the five steps. */
+ssd_status_t ssd_prefill_varlen(const ssd_params_t* p,
+                                const void* x, const void* dt, const float* A,
+                                const void* B, const void* C,
+                                const float* D, const float* dt_bias,
+                                const int32_t* seq_idx,
+                                const void* initial_state,
+                                void* y, void* final_state,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then reads the device status word the last fused
  * ssd_prefill on `workspace` left: SSD_OK, SSD_ERR_SYNC_TIMEOUT when one of its waits
  * gave up, or SSD_ERR_SCHEDULE when one of its work partitions was never served (in

@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_INVALID_SHAP
 EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill", "ssd_prefill_timed",
                     "ssd_check_device_status",
                     "ssd_status_string", "ssd_workspace_layout", "ssd_step_chunk_cumsum", "ssd_step_bmm",
-                    "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan", "ssd_decode_step"]
+                    "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan", "ssd_decode_step",
+                    "ssd_prefill_varlen"]
 
 
 class SSDError(RuntimeError):
@@ -82,6 +83,8 @@ def load_library():
     lib.ssd_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_prefill.restype = ctypes.c_int
     lib.ssd_prefill_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.ssd_prefill_varlen.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_prefill_varlen.restype = ctypes.c_int
     lib.ssd_prefill_timed.restype = ctypes.c_int
     lib.ssd_check_device_status.argtypes = [P, vp, vp]
     lib.ssd_check_device_status.restype = ctypes.c_int
@@ -184,15 +187,24 @@ def _check_tensors(x, dt, A, B, C, D, dt_bias, h0):
 
 
 def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_size=128, state_dtype=None,
-                impl="fused", dt_softplus=True, workspace=None, y=None, final_state=None, kernel_events=None):
+                impl="fused", dt_softplus=True, workspace=None, y=None, final_state=None, kernel_events=None,
+                seq_idx=None):
     """Run one SSD prefill on the GPU; returns (y[B,L,H,P], final_state[B,H,P,N]).
 
     ``state_dtype`` defaults to initial_state's dtype, else float32.  ``workspace``
     (uint8 device tensor), ``y`` and ``final_state`` may be passed to avoid allocation.
     ``kernel_events`` = (begin, end) torch.cuda.Event(enable_timing=True) pair, recorded
-    by the library around the SSD compute kernel(s) (ssd_prefill_timed)."""
+    by the library around the SSD compute kernel(s) (ssd_prefill_timed).  ``seq_idx``
+    (int32 [B, L]) packs several sequences per batch row: the recurrence restarts wherever
+    it changes (ssd_prefill_varlen)."""
     import torch
     _check_tensors(x, dt, A, B, C, D, dt_bias, initial_state)
+    if seq_idx is not None:
+        if (tuple(seq_idx.shape) != tuple(x.shape[:2]) or seq_idx.dtype != torch.int32 or seq_idx.device != x.device
+                or not seq_idx.is_contiguous()):
+            raise ValueError("seq_idx must be a contiguous int32 [B, L] tensor on %s" % x.device)
+        if kernel_events is not None:
+            raise ValueError("kernel_events are not recorded for packed variable-length input")
     if state_dtype is None:
         state_dtype = initial_state.dtype if initial_state is not None else torch.float32
     sd = {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[state_dtype]
@@ -209,7 +221,9 @@ def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_
         workspace = alloc_workspace(prm, x.device)
     args = (ctypes.byref(prm), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
             _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(x.device))
-    if kernel_events is None:
+    if seq_idx is not None:
+        _check(load_library().ssd_prefill_varlen(*args[:8], _ptr(seq_idx), *args[8:]), "ssd_prefill_varlen")
+    elif kernel_events is None:
         _check(load_library().ssd_prefill(*args), "ssd_prefill")
     else:
         ev0, ev1 = kernel_events

@@ -434,10 +434,11 @@ SSD_EXPORT ssd_status_t ssd_step_chunk_scan(const ssd_params_t* p, const void* x
 static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt, const float* A, const void* B,
                             const void* C, const float* D, const float* dt_bias, const void* initial_state, void* y,
                             void* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                            hipEvent_t ev_begin, hipEvent_t ev_end) {
+                            hipEvent_t ev_begin, hipEvent_t ev_end, const int32_t* seq_idx) {
     Layout l;
     ssd_status_t s = check_ws(p, workspace, workspace_bytes, &l);
     if (s != SSD_OK) return s;
+    if (!aligned(seq_idx, 4)) return SSD_ERR_MISALIGNED;
     if (!x || !dt || !A || !B || !C || !y || !final_state) return SSD_ERR_NULL_POINTER;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(final_state, 16) ||
         !aligned(initial_state, 16) || !aligned(dt, elem_size(p->in_dtype)) || !aligned(A, 4) || !aligned(D, 4) ||
@@ -452,6 +453,7 @@ static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt
     a.C = C;
     a.D = D;
     a.dt_bias = dt_bias;
+    a.seq_idx = seq_idx;
     a.y = y;
     a.has_h0 = initial_state != nullptr;
     hipError_t e;
@@ -495,7 +497,16 @@ SSD_EXPORT ssd_status_t ssd_prefill(const ssd_params_t* p, const void* x, const 
                                    const void* initial_state, void* y, void* final_state, void* workspace,
                                    size_t workspace_bytes, void* stream) {
     return prefill(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes, stream,
-                   nullptr, nullptr);
+                   nullptr, nullptr, nullptr);
+}
+
+SSD_EXPORT ssd_status_t ssd_prefill_varlen(const ssd_params_t* p, const void* x, const void* dt, const float* A,
+                                          const void* B, const void* C, const float* D, const float* dt_bias,
+                                          const int32_t* seq_idx, const void* initial_state, void* y,
+                                          void* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!seq_idx) return SSD_ERR_NULL_POINTER;
+    return prefill(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes, stream,
+                   nullptr, nullptr, seq_idx);
 }
 
 SSD_EXPORT ssd_status_t ssd_prefill_timed(const ssd_params_t* p, const void* x, const void* dt, const float* A,
@@ -505,7 +516,7 @@ SSD_EXPORT ssd_status_t ssd_prefill_timed(const ssd_params_t* p, const void* x, 
                                          void* kernel_end) {
     if (!kernel_begin || !kernel_end) return SSD_ERR_NULL_POINTER;
     return prefill(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes, stream,
-                   (hipEvent_t)kernel_begin, (hipEvent_t)kernel_end);
+                   (hipEvent_t)kernel_begin, (hipEvent_t)kernel_end, nullptr);
 }
 
 SSD_EXPORT ssd_status_t ssd_check_device_status(const ssd_params_t* p, const void* workspace, void* stream) {

@@ -634,6 +634,13 @@ __device__ inline bool relay_handoff(const SsdArgs& a, int b, int c, int h, int 
 // inclusive in-chunk running sum of dt * A, both fp32, into dtf / acs [B][nc][H][Q].  One
 // wave per head; each lane owns Q/64 consecutive tokens, then a wave-wide exclusive scan of
 // the lane totals.
+// Packed variable-length input ([KF] "与vLLM的深度融合": sequences told apart by a per-token
+// sequence index and masked, not offset): a token t > 0 whose seq_idx differs from token
+// t - 1's starts a new sequence, and its log-decay gets kSeqStartLogDecay added.  Every later
+// step only ever uses exp of acs differences and of acs itself, so the decay across a sequence
+// start -- into the chunk state, through the state passing, in the C . S term and in L --
+// underflows to exactly 0, while inside a sequence the offsets cancel.  The state entering a
+// batch row (the initial state) belongs to its first sequence.
 template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c, int h0, int h1) {
     const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int Q = a.chunk, L = a.seqlen, H = a.nheads, nc = a.nchunks;
@@ -649,11 +656,14 @@ template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c
             d[k] = 0.f;
             if (k < V) {
                 const int t = c * Q + lane * V + k;
+                float start = 0.f;
                 if (t < L) {
                     const float z = f32of(dtr[((size_t)b * L + t) * H + h]) + bias;
                     d[k] = a.softplus ? softplus_f(z) : z;
+                    if (a.seq_idx && t > 0 && a.seq_idx[(size_t)b * L + t] != a.seq_idx[(size_t)b * L + t - 1])
+                        start = kSeqStartLogDecay;
                 }
-                tot += d[k] * Ah;
+                tot += d[k] * Ah + start;
             }
             run[k] = tot;
         }

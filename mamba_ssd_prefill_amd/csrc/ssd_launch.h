@@ -8,6 +8,10 @@
 
 namespace ssd {
 
+// Log-decay added at every token that starts a new sequence of packed variable-length input:
+// exp(-128) underflows to 0 in fp32, so every decay across the sequence start vanishes.
+constexpr float kSeqStartLogDecay = -128.f;
+
 // Largest number of XCDs (L2 domains) the fused form partitions its work over.
 constexpr int kMaxXcc = 8;
 
@@ -20,6 +24,7 @@ struct SsdArgs {
     const void* C;
     const float* D;
     const float* dt_bias;
+    const int* seq_idx;  // [B][L] sequence ids of packed variable-length input, or nullptr
     void* y;
     float* dtf;          // [B][nc][H][Q]
     float* acs;          // [B][nc][H][Q]
@@ -107,6 +112,7 @@ struct DecodeArgs {
 };
 
 // State rows of P one decode workgroup covers (kDecodeIter loads per lane, 256 / N rows each).
+// (4 measured fastest on MI355X: 8 or 16 loads per lane were slower)
 constexpr int kDecodeIter = 4;
 inline int decode_rows_per_block(int N) { return 4 * kDecodeIter * (256 / N); }
 

@@ -8,6 +8,8 @@ imports, links or calls it, and it shares no code with the HIP library.
 * ``chunked``     -- the five-step chunked algorithm with its intermediates (C, fp64).
 * ``quadratic``   -- the brute-force masked-matrix form (numpy, fp64, tiny inputs).
 * ``decode_step`` -- one token of the recurrence on a cached state (the decode step).
+* ``recurrence_varlen`` -- packed variable-length input: the recurrence restarted at every
+  sequence start.
 
 Inputs may be torch CPU tensors or numpy arrays; 16-bit tensors are passed to C
 as their raw bits and widened exactly there.
@@ -203,6 +205,29 @@ def decode_step(x, dt, A, B, C, D=None, dt_bias=None, state=None, dt_softplus=Tr
     y, fin = recurrence_full(x.reshape(Bt, 1, H, P), dt.reshape(Bt, 1, H), A, B.reshape(Bt, 1, G, N),
                              C.reshape(Bt, 1, G, N), D, dt_bias, state, dt_softplus)
     return y.reshape(Bt, H, P), fin
+
+
+def recurrence_varlen(x, dt, A, B, C, D=None, dt_bias=None, h0=None, dt_softplus=True, seq_idx=None):
+    """Several sequences packed in each batch row ("Mamba-2炸裂升级！…", section "与vLLM的深度融合"):
+    a new sequence starts at every t > 0 where seq_idx[b, t] != seq_idx[b, t-1], and the
+    recurrence runs over each sequence on its own -- the first sequence of row b from h0[b],
+    every later one from zero.  Returns y[B, L, H, P] and the state after the last token of
+    each row, [B, H, P, N], in fp64."""
+    Bt, L, H, P = (int(s) for s in x.shape)
+    N = int(B.shape[3])
+    sidx = np.asarray(seq_idx.cpu() if hasattr(seq_idx, "cpu") else seq_idx)
+    y = np.empty((Bt, L, H, P))
+    fin = np.empty((Bt, H, P, N))
+    for b in range(Bt):
+        starts = [0] + [t for t in range(1, L) if sidx[b, t] != sidx[b, t - 1]] + [L]
+        for k in range(len(starts) - 1):
+            t0, t1 = starts[k], starts[k + 1]
+            part = lambda t: None if t is None else t[b:b + 1, t0:t1].contiguous()  # noqa: E731
+            init = h0[b:b + 1] if (h0 is not None and k == 0) else None
+            yk, fk = recurrence_full(part(x), part(dt), A, part(B), part(C), D, dt_bias, init, dt_softplus)
+            y[b, t0:t1] = yk[0]
+            fin[b] = fk[0]
+    return y, fin
 
 
 def widen(t):

@@ -254,3 +254,25 @@ def test_decode_short_struct(lib):
     p.struct_size = 8
     assert dec_call(lib, p) == BADARG
     assert lib.ssd_decode_step(None, *([0x10000] * 10), None) == NULLP
+
+
+# ---- packed variable-length prefill: host validation only ------------------------------------
+def call_varlen(lib, p, a, seq):
+    vp = ctypes.c_void_p
+    return lib.ssd_prefill_varlen(ctypes.byref(p), vp(a["x"]), vp(a["dt"]), vp(a["A"]), vp(a["B"]), vp(a["C"]),
+                                  vp(a["D"]), vp(a["dt_bias"]), vp(seq), vp(a["h0"]), vp(a["y"]), vp(a["fin"]),
+                                  vp(a["ws"]), a["ws_bytes"], a["stream"])
+
+
+def test_varlen_requires_aligned_seq_idx(lib):
+    p = base()
+    assert call_varlen(lib, p, prefill_args(p), None) == NULLP
+    assert call_varlen(lib, p, prefill_args(p), FAKE + 2) == MISAL
+
+
+@pytest.mark.parametrize("field", ["x", "C", "fin", "ws"])
+def test_varlen_validates_like_prefill(lib, field):
+    p = base()
+    assert call_varlen(lib, p, prefill_args(p, **{field: None}), FAKE) == NULLP
+    assert call_varlen(lib, base(headdim=48), prefill_args(p, ws_bytes=1 << 30), FAKE) == UNSUP
+    assert call_varlen(lib, p, prefill_args(p, ws_bytes=ssd.workspace_size(p) - 1), FAKE) == WS_SMALL

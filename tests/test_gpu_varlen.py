@@ -1,0 +1,135 @@
+"""GPU parity of packed variable-length prefill (ssd_prefill_varlen through the C ABI).
+
+Several sequences share a batch row, told apart by a per-token sequence index and masked
+("Mamba-2炸裂升级！…", section "与vLLM的深度融合").  The oracle runs the fp64 recurrence over
+each sequence on its own (oracle.recurrence_varlen); every comparison goes through the
+parity gate.  Layouts put sequence starts on chunk starts, in the middle of chunks, several
+in one chunk, at the last token, and include sequences of length 1.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mamba_ssd_prefill_amd as ssd
+import oracle
+from gpu_common import DT_NAME, f64, fused_form, require_gpu, say
+from mamba_ssd_prefill_amd.inputs import make_inputs
+from parity import gate
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def dev():
+    return require_gpu()
+
+
+def seq_index(lengths_per_row, L):
+    """int32 [B, L]: row b holds sequences of the given lengths (the last one takes the rest)."""
+    out = np.zeros((len(lengths_per_row), L), dtype=np.int32)
+    for b, lens in enumerate(lengths_per_row):
+        t, sid = 0, 0
+        for n in lens:
+            out[b, t:t + n] = sid
+            t += n
+            sid += 1
+        out[b, t:] = sid
+        assert t <= L
+    return torch.from_numpy(out)
+
+
+def layouts(Q, L):
+    # row 0: starts at chunk starts, mid-chunk, several per chunk, length-1 sequences, a start at
+    # the last token; row 1: one sequence (no start inside the row)
+    r0 = [1, Q - 1, Q, 3, 1, 2, 2 * Q + 5, 17, Q // 2]
+    used = sum(r0)
+    assert used < L - 1
+    r0 += [L - 1 - used]  # then one more sequence of length 1 at token L - 1
+    return [r0, []]
+
+
+def run_varlen(inp, seq, Q, impl, state_dtype=None):
+    with fused_form(impl) as name:
+        g = inp.to("cuda:0")
+        sd = state_dtype or (g.h0.dtype if g.h0 is not None else torch.float32)
+        Bt, L, H, P = g.x.shape
+        G, N = g.B.shape[2], g.B.shape[3]
+        prm = ssd.make_params(Bt, L, H, P, N, G, Q, DT_NAME[g.x.dtype], DT_NAME[sd], inp.dt_softplus, name)
+        ws = ssd.alloc_workspace(prm, g.x.device)
+        y, fin = ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=Q, impl=name,
+                                 state_dtype=sd, workspace=ws, seq_idx=seq.to("cuda:0"))
+        torch.cuda.synchronize()
+        assert ssd.check_device_status(prm, ws) == 0
+        return y, fin
+
+
+def check(inp, seq, y, fin, name):
+    yr, fr = oracle.recurrence_varlen(**inp.args(), seq_idx=seq)
+    in_dt = DT_NAME[inp.x.dtype]
+    skip = f64(inp.D)[None, None, :, None] * f64(inp.x) if inp.D is not None else None
+    gate(f64(y), yr, in_dt, in_dt, skip=skip, name=name + " y")
+    gate(f64(fin), fr, DT_NAME[fin.dtype], in_dt, name=name + " final")
+
+
+IMPLS = ["unfused", "fused_hop", "fused_relay2", "fused_relay4"]
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("Q", [64, 128, 256])
+def test_varlen_bf16(Q, impl):
+    L = 5 * Q + 37
+    inp = make_inputs(2, L, 8, 64, 128, 2, dtype="bf16", state_dtype="f32", has_h0=True, seed=8000 + Q)
+    seq = seq_index(layouts(Q, L), L)
+    say("varlen bf16 Q", Q, impl)
+    y, fin = run_varlen(inp, seq, Q, impl)
+    check(inp, seq, y, fin, "varlen bf16 Q%d %s" % (Q, impl))
+
+
+@pytest.mark.parametrize("impl", ["unfused", "fused_hop", "fused_relay2"])
+def test_varlen_f16_with_f16_state(impl):
+    Q, L = 128, 700
+    inp = make_inputs(1, L, 16, 64, 128, 1, dtype="f16", state_dtype="f16", has_h0=True, seed=8101)
+    seq = seq_index([[200, 1, 70, 128, 5]], L)
+    say("varlen f16 state", impl)
+    y, fin = run_varlen(inp, seq, Q, impl)
+    check(inp, seq, y, fin, "varlen f16/f16 %s" % impl)
+
+
+@pytest.mark.parametrize("impl", ["unfused", "fused_hop", "fused_relay2"])
+def test_varlen_f32(impl):
+    Q, L = 64, 300
+    inp = make_inputs(2, L, 4, 16, 16, 1, dtype="f32", state_dtype="f32", has_h0=True, seed=8102)
+    seq = seq_index([[64, 90, 1, 40], [150]], L)
+    say("varlen f32", impl)
+    y, fin = run_varlen(inp, seq, Q, impl)
+    check(inp, seq, y, fin, "varlen f32 %s" % impl)
+
+
+@pytest.mark.parametrize("impl", ["unfused", "fused_hop", "fused_relay2"])
+def test_varlen_grouped_many_short_sequences(impl):
+    # grouped B/C (4 heads per group), 24 sequences of 1..80 tokens in one row, no initial state
+    Q, L = 128, 1000
+    rng = np.random.default_rng(5)
+    lens = []
+    for n in rng.integers(1, 81, size=64):
+        if sum(lens) + int(n) >= L - 1 or len(lens) == 23:
+            break
+        lens.append(int(n))
+    inp = make_inputs(1, L, 16, 64, 128, 4, dtype="bf16", state_dtype="f32", has_h0=False, seed=8103)
+    seq = seq_index([lens], L)
+    say("varlen grouped", impl)
+    y, fin = run_varlen(inp, seq, Q, impl)
+    check(inp, seq, y, fin, "varlen grouped %s" % impl)
+
+
+@pytest.mark.parametrize("impl", ["unfused", "fused"])
+def test_one_sequence_per_row_is_bitwise_the_plain_prefill(impl):
+    Q, L = 128, 600
+    inp = make_inputs(2, L, 8, 64, 128, 2, dtype="bf16", state_dtype="f32", has_h0=True, seed=8104)
+    seq = torch.full((2, L), 7, dtype=torch.int32)
+    y1, f1 = run_varlen(inp, seq, Q, impl)
+    g = inp.to("cuda:0")
+    with fused_form(impl) as name:
+        y2, f2 = ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=Q, impl=name)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)

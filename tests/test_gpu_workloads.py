@@ -75,3 +75,18 @@ def test_long_context_sampled(name, impl):
     check_sampled(inp, y, fin, [(0, 0), (0, 33), (0, 79), (0, 50)], name + " " + impl)
     del y, fin
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("impl", ["fused", "unfused"])
+def test_mamba2_2p7b_fp16_state_sampled(impl):
+    """The 2.7B layer with fp16 state storage (the initial state, every inter-chunk state and
+    the final state): the relaxed-state point bench.py reports beside the fp32-state headline."""
+    import copy
+    w = WORKLOADS["mamba2_2p7b_bf16"]
+    inp = copy.copy(inputs_for(w.name))
+    inp.h0 = inp.h0.to(torch.float16)
+    say(w.name, "fp16 state", impl)
+    y, fin = run_gpu(inp, w.chunk_size, impl, state_dtype=torch.float16)
+    check_sampled(inp, y, fin, PAIRS_2P7B, "%s fp16 state %s" % (w.name, impl))
+    del y, fin
+    torch.cuda.empty_cache()

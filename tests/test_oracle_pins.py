@@ -340,3 +340,60 @@ def test_decode_step_by_hand(oracle_mod):
     yref = Sref @ f64(Cm)[b, g] + float(inp.D[h]) * f64(x)[b, h]
     assert rel_err(S[b, h], Sref) < REL
     assert rel_err(y[b, h], yref) < REL
+
+
+def _masked_quadratic(inp, seq):
+    """Packed sequences in the SSD "attention" form ("Mamba 硬件感知算法", section
+    "结构化状态空间对偶性"), with the mask of "Mamba-2炸裂升级！…", section "与vLLM的深度融合":
+    y_i = sum_{j <= i, same sequence} (C_i . B_j) exp(sum_{j < k <= i} dA_k) dt_j x_j + D x_i
+          + [i in the row's first sequence] exp(sum_{k <= i} dA_k) (h0 C_i);
+    the final state is the same sum over the last sequence (plus the decayed h0 when the row
+    holds one sequence).  Plain numpy, O(L^2) per (b, h)."""
+    x, dtr, A, Bm, Cm, D, bias, h0 = (f64(t) for t in (inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.dt_bias, inp.h0))
+    Bt, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    y = np.zeros((Bt, L, H, P))
+    fin = np.zeros((Bt, H, P, N))
+    for b in range(Bt):
+        first = seq[b] == seq[b, 0]
+        for h in range(H):
+            g = h // (H // G)
+            d = np.logaddexp(0.0, dtr[b, :, h] + bias[h])
+            cum = np.concatenate([[0.0], np.cumsum(d * A[h])])  # cum[t + 1] = sum_{k <= t} dA_k
+            for i in range(L):
+                acc = D[h] * x[b, i, h]
+                for j in range(i + 1):
+                    if seq[b, j] == seq[b, i] and np.all(seq[b, j:i + 1] == seq[b, i]):
+                        acc = acc + (Cm[b, i, g] @ Bm[b, j, g]) * np.exp(cum[i + 1] - cum[j + 1]) * d[j] * x[b, j, h]
+                if first[i] and np.all(seq[b, :i + 1] == seq[b, 0]):
+                    acc = acc + np.exp(cum[i + 1]) * (h0[b, h] @ Cm[b, i, g])
+                y[b, i, h] = acc
+            last = L - 1
+            for j in range(L):
+                if np.all(seq[b, j:] == seq[b, last]):
+                    fin[b, h] += np.exp(cum[L] - cum[j + 1]) * d[j] * np.outer(x[b, j, h], Bm[b, j, g])
+            if np.all(seq[b] == seq[b, 0]):
+                fin[b, h] += np.exp(cum[L]) * h0[b, h]
+    return y, fin
+
+
+def test_varlen_matches_masked_quadratic_form(oracle_mod):
+    inp = small(seed=22, Bt=2, L=30, H=4, P=3, N=5, G=2, dt_scale=2.0)
+    seq = np.array([[0] * 7 + [1] * 1 + [2] * 12 + [3] * 10,
+                    [5] * 30], dtype=np.int32)
+    y, fin = oracle_mod.recurrence_varlen(**inp.args(), seq_idx=seq)
+    yq, fq = _masked_quadratic(inp, seq)
+    assert rel_err(y, yq) < REL
+    assert rel_err(fin, fq) < REL
+    # a row holding one sequence is the plain recurrence
+    y1, f1 = oracle_mod.recurrence_full(**inp.args())
+    assert np.array_equal(y[1], y1[1]) and np.array_equal(fin[1], f1[1])
+
+
+def test_varlen_ids_only_matter_where_they_change(oracle_mod):
+    inp = small(seed=23, Bt=1, L=24, H=2, G=1)
+    a = np.array([[3] * 5 + [9] * 11 + [3] * 8], dtype=np.int32)
+    b = np.array([[0] * 5 + [1] * 11 + [2] * 8], dtype=np.int32)
+    ya, fa = oracle_mod.recurrence_varlen(**inp.args(), seq_idx=a)
+    yb, fb = oracle_mod.recurrence_varlen(**inp.args(), seq_idx=b)
+    assert np.array_equal(ya, yb) and np.array_equal(fa, fb)
