@@ -142,6 +142,21 @@ def time_decode(ssd, torch, w, batch, steps):
     return e0.elapsed_time(e1) * 1e3 / (reps * steps)
 
 
+def decode_legs(ssd, torch, w, only_batch=0):
+    """The decode step at the workload's layer shape, at its batch and at 16 times it (or at
+    `only_batch` alone)."""
+    dec = {}
+    for bsz in ((only_batch,) if only_batch else (w.batch, 16 * w.batch)):
+        log("decode step, batch %d" % bsz)
+        us = time_decode(ssd, torch, w, bsz, 100 if bsz <= w.batch else 20)
+        nb = decode_bytes(w, bsz)
+        dec["batch%d" % bsz] = {"us_per_step": us, "tokens_per_s": bsz / (us / 1e6), "bytes": nb,
+                                "achieved_gbs": nb / (us / 1e6) / 1e9, "frac": nb / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
+    return {"kernel": "k_decode", "bound": "hbm", "peak_gbs": HBM_PEAK_GBS, "copy_gbs": copy_bandwidth(torch),
+            "state_dtype": w.state_dtype, "timing": "HIP events around replays of a HIP graph of consecutive steps",
+            **dec}
+
+
 def time_varlen(ssd, torch, steps):
     """The many-short-sequences workload (32 sequences of 1024 tokens, H=128, G=8, bf16, Q=128)
     two ways: as a batch of 32 rows, and packed into one row of 32768 tokens told apart by
@@ -233,6 +248,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode-step legs (for a kernel trace of k_decode); prints their JSON")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="with --decode-only: this batch size only (default: the workload's and 16 times it)")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 1 GiB device copy (counter calibration), "
                          "then --steps fused calls; prints nothing")
@@ -254,6 +273,9 @@ def main():
     ssd.load_library()
     w = WORKLOADS[args.workload]
     Q = args.chunk or w.chunk_size
+    if args.decode_only:
+        print(json.dumps(decode_legs(ssd, torch, w, args.decode_batch)), flush=True)
+        return
     log("generating %s inputs" % w.name)
     inp = workload_inputs(w)
     g = inp.to("cuda:0")
@@ -327,20 +349,9 @@ def main():
             c16, x16, _ = algorithmic(w.with_(state_dtype="f16"), Q, inp.h0 is not None)
             out["state_f16"] = {"fused_ms": hw, "fused_kernel_ms": hk, "value": tokens / (hw / 1e3),
                                 "frac": (c16 + x16) / (hk / 1e3) / 1e9 / HBM_PEAK_GBS}
-        dec = {}
-        for bsz in (w.batch, 16 * w.batch):
-            log("decode step, batch %d" % bsz)
-            us = time_decode(ssd, torch, w, bsz, 100 if bsz == w.batch else 20)
-            nb = decode_bytes(w, bsz)
-            dec["batch%d" % bsz] = {"us_per_step": us, "tokens_per_s": bsz / (us / 1e6), "bytes": nb,
-                                    "achieved_gbs": nb / (us / 1e6) / 1e9,
-                                    "frac": nb / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
         log("packed variable-length input")
         out["varlen"] = time_varlen(ssd, torch, 10)
-        out["decode"] = {"kernel": "k_decode", "bound": "hbm", "peak_gbs": HBM_PEAK_GBS,
-                         "copy_gbs": copy_bandwidth(torch),
-                         "state_dtype": w.state_dtype, "timing": "HIP events around replays of a HIP graph of consecutive steps",
-                         **dec}
+        out["decode"] = decode_legs(ssd, torch, w)
     del g
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -67,8 +67,15 @@ def _demangle_ssd(name):
     return out
 
 
+# rocprofv3 prints some names already demangled, and its demangler reads the __bf16 template
+# argument followed by float (mangled "DF16bf") as "bool _Accum"
+_GARBLED = {"ssd::k_decode<bool _Accum, ": "ssd::k_decode<bf16, float, "}
+
+
 def short(name):
     """Demangled kernel name without its argument list."""
+    for bad, good in _GARBLED.items():
+        name = name.replace(bad, good)
     d = _demangle_ssd(name)
     if d:
         return d
