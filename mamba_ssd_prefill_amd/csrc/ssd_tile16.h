@@ -16,6 +16,7 @@
 
 #include "ssd_device.h"
 
+
 namespace ssd {
 
 constexpr float LOG2E = 1.4426950408889634f;
@@ -700,20 +701,50 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 yo[ib][pb] = cvt4<T>(yv);
             }
         }
-        // The stores go out together after the loop: a store's registers stay reserved until it
-        // completes, so reusing them block after block would make every block wait for the
-        // previous block's store.  (yo takes the registers the D x operand frees.)
+        // y leaves in whole token rows: the tile's HPT heads of one token are adjacent in y
+        // (HPT * P * 2 = 256 bytes for P >= 32), but each wave holds only its 32 p columns of a
+        // head, so stored directly every row would go out as 64-byte pieces of 128-byte lines.
+        // With every head of the tile valid (a tile-wide condition: the waves of a head past the
+        // group's end have left already) the waves first put their pieces into LDS (R1: the L
+        // bands, x and CB are no longer read), then each wave stores four whole token rows per
+        // instruction.  16-byte pieces are XOR-swizzled by the token so neither pass conflicts.
+        constexpr int ROWB = HPT * P * 2, PPR = ROWB / 16;
+        const int nvh_y = hpg - tig * HPT < HPT ? hpg - tig * HPT : HPT;
+        if (MBP == 2 && PPR == 16 && HPT * Q * P * 2 <= G_::SZ_R1 && nvh_y == HPT) {
+            char* sY = smem;
+            lds_barrier();  // every wave is done with R1
 #pragma unroll
-        for (int ib = 0; ib < QB; ++ib) {
-            const int i = ib * 16 + r16;
-            if (i < valid) {
-                const uint32_t yoff = (uint32_t)i * xrs + (uint32_t)(ph * PW + 4 * MBP * q) * 2;
-                if constexpr (MBP == 2)
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(u32x4, __builtin_shufflevector(yo[ib][0], yo[ib][1], 0, 1, 2, 3, 4, 5, 6, 7)),
-                        yr, yoff, 0, 2);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yo[ib][0]), yr, yoff, 0, 2);
+            for (int ib = 0; ib < QB; ++ib) {
+                const int i = ib * 16 + r16;
+                const int pc = (hs * P + ph * PW + 4 * MBP * q) >> 3;
+                *(u32x4*)(sY + i * ROWB + ((pc ^ (i & (PPR - 1))) << 4)) =
+                    __builtin_bit_cast(u32x4, __builtin_shufflevector(yo[ib][0], yo[ib][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            lds_barrier();
+            const __amdgpu_buffer_rsrc_t yrow =
+                make_rsrc((T*)a.y + (((size_t)b * L + tok0) * H + head0) * P, (uint32_t)(valid - 1) * xrs + ROWB);
+#pragma unroll
+            for (int k = 0; k < Q * PPR / 256; ++k) {
+                const int f = (k * 4 + wave) * 64 + lane, t = f / PPR, pc = f % PPR;
+                const u32x4 v = *(const u32x4*)(sY + t * ROWB + ((pc ^ (t & (PPR - 1))) << 4));
+                if (t < valid) __builtin_amdgcn_raw_buffer_store_b128(v, yrow, (uint32_t)t * xrs + (uint32_t)pc * 16, 0, 2);
+            }
+        } else {
+            // The stores go out together after the loop: a store's registers stay reserved until
+            // it completes, so reusing them block after block would make every block wait for the
+            // previous block's store.  (yo takes the registers the D x operand frees.)
+#pragma unroll
+            for (int ib = 0; ib < QB; ++ib) {
+                const int i = ib * 16 + r16;
+                if (i < valid) {
+                    const uint32_t yoff = (uint32_t)i * xrs + (uint32_t)(ph * PW + 4 * MBP * q) * 2;
+                    if constexpr (MBP == 2)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(u32x4, __builtin_shufflevector(yo[ib][0], yo[ib][1], 0, 1, 2, 3, 4, 5, 6, 7)),
+                            yr, yoff, 0, 2);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yo[ib][0]), yr, yoff, 0, 2);
+                }
             }
         }
         asm volatile("" ::"v"(touched.x), "v"(touched.y));  // the touch loads are long complete
