@@ -8,10 +8,9 @@
 
 namespace ssd {
 
-// No-op cross-tile prefetch hooks (see PrefetchHook) for the unfused kernels.
+// No-op hooks (see ClaimHook) for the unfused kernels.
 struct NoHook {
     __device__ inline void claim() const {}
-    __device__ inline u32x2 touch() const { return u32x2{0u, 0u}; }
 };
 
 // ---- unfused form: one kernel per step -------------------------------------------------
@@ -134,41 +133,17 @@ __device__ inline ChunkItem chunk_item(const SsdArgs& a, const FusedPart& f, uin
     return it;
 }
 
-// Cross-tile prefetch of the fused form.  A chunk tile calls claim() once its round-2 reads are
-// issued (thread 0 takes the workgroup's next ticket, so the atomic overlaps the state hop) and
-// touch() once its L bands are built (every thread loads one word of each 128-byte line of the
-// next chunk tile's x rows, which are then in the L2 when that tile copies them).  The next
-// ticket is larger than the current one and runs only after it, so the claim order keeps
-// every wait finite.  touch() returns the loaded words unused, to be consumed (asm sink) at
-// the end of the tile: a use any earlier would wait for the loads.
-template <int HPT, int P> struct PrefetchHook {
+// Ticket claimed ahead in the fused form: a chunk tile calls claim() once its round-2 reads
+// are issued, so thread 0's atomic on the partition's ticket overlaps the state hop.  The next
+// ticket is larger than the current one and runs only after it, so the claim order keeps every
+// wait finite.  (Touching the next tile's x rows into the L2 from here was measured slower once
+// y left in whole lines: the touched lines pushed state slots out of the L2.)
+struct ClaimHook {
     const SsdArgs& a;
-    const FusedPart& f;
     int part;
     uint32_t* s_next;  // LDS
     __device__ inline void claim() const {
         if (threadIdx.x == 0) *s_next = atomicAdd(a.ticket + part * kTicketStride, 1u);
-    }
-    __device__ inline u32x2 touch() const {
-        const uint32_t tn = __builtin_amdgcn_readfirstlane(*s_next);
-        if (tn < f.first_chunk || tn >= f.n_total) return u32x2{0u, 0u};
-        const ChunkItem it = chunk_item(a, f, tn);
-        const int L = a.seqlen, H = a.nheads, Q = a.chunk, hpg = a.hpg;
-        const int tok0 = it.c * Q, valid = L - tok0 < Q ? L - tok0 : Q;
-        const int nvh = hpg - it.tig * HPT < HPT ? hpg - it.tig * HPT : HPT;
-        const uint32_t xrs = (uint32_t)H * P * 2;
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(
-            (const char*)a.x + ((((size_t)it.b * L + tok0) * H + it.g * hpg + it.tig * HPT) * P) * 2,
-            (uint32_t)(valid - 1) * xrs + (uint32_t)nvh * P * 2);
-        constexpr int LPR = (HPT * P * 2 + 127) / 128;  // 128-byte lines per row (at most 2)
-        static_assert(LPR <= 2, "a tile row spans at most two lines");
-        const int k0 = tid_here(), k1 = k0 + 256;  // Q * LPR <= 512 lines
-        u32x2 v = {0u, 0u};
-        if (k0 < Q * LPR)
-            v.x = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(k0 / LPR) * xrs + (uint32_t)(k0 % LPR) * 128, 0, 0);
-        if (k1 < Q * LPR)
-            v.y = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(k1 / LPR) * xrs + (uint32_t)(k1 % LPR) * 128, 0, 0);
-        return v;
     }
 };
 
@@ -238,7 +213,7 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
             if (tid_here() < 64)  // wave 0: both flags with one poll
                 wait_pair(a.cs_done, (uint32_t)it.slot, (uint32_t)(a.bmm_done - a.cs_done + it.slot), a);
             lds_barrier();  // every wave starts after the flags were seen
-            const PrefetchHook<HPT, P> hook{a, f, x, &s_next};
+            const ClaimHook hook{a, x, &s_next};
             chunk(a, it.b, it.c, it.g, it.tig, a.cb + it.slot * Q * Q, hook);
             lds_barrier();  // s_next holds the ticket claimed ahead
             pending = __builtin_amdgcn_readfirstlane(s_next);

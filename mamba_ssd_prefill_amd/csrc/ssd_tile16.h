@@ -311,8 +311,7 @@ template <typename T, typename G_, int AUX> struct LBuild {
     }
 };
 
-// `hook` (fused form): claim() after the round-2 reads are issued, touch() once the L bands
-// are built; see PrefetchHook.
+// `hook` (fused form): claim() after the round-2 reads are issued; see ClaimHook.
 template <typename T, int P, int N, int Q, int MODE, typename Hook>
 __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbp,
                              const Hook& hook) {
@@ -384,22 +383,6 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     __syncthreads();
 
     const float* a2_h = sA2 + hs * Q;
-
-    // Touch this wave's state-slot lines (one lane per 128-byte line, sc1 so nothing stale
-    // stays in the L1) so they are resident in the L2 when the state hop reads them after its
-    // wait: under load they are otherwise evicted between chunks and the hop -- the serial
-    // chain from chunk to chunk -- would pay a memory round trip.  The values read here are
-    // not used (the state may not be written yet).
-    uint32_t pf0 = 0, pf1 = 0;
-    if constexpr (MODE == MODE_FUSED) {
-        if (hvalid && !a.relay) {
-            const int K = a.slots;
-            const __amdgpu_buffer_rsrc_t rpf =
-                ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
-            pf0 = __builtin_amdgcn_raw_buffer_load_b32(rpf, (uint32_t)lane * 128, 0, AUX_L2);
-            pf1 = __builtin_amdgcn_raw_buffer_load_b32(rpf, 8192 + (uint32_t)lane * 128, 0, AUX_L2);
-        }
-    }
 
     // x operand, token-major: xf[kk][pb] holds x[kk*32 + 8q .. +7][ph*PW + pcol(pb, r16)]
     frag xf[KS][MBP];
@@ -478,7 +461,6 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c, in place in the chain's slot
                 uint32_t* fl = chain_counter(a, b, h, ph, WPH);
                 wait_flag(fl, a, (uint32_t)c + 1);
-                asm volatile("" ::"v"(pf0), "v"(pf1));  // the touch loads are complete (long ago)
                 const int K = a.slots;
                 const __amdgpu_buffer_rsrc_t rin =
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
@@ -571,11 +553,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             lb.store((T*)smem, sA2, sF, sE, nvh, tid);  // over x (already in registers)
             lds_barrier();                              // L is complete
         }
-        const u32x2 touched = hook.touch();
-        if (!hvalid) {
-            asm volatile("" ::"v"(touched.x), "v"(touched.y));
-            return;
-        }
+        if (!hvalid) return;
         // S_c as the A operand of C . S^T; k slots of step ks: n = 32ks + 4q + {0..3} and
         // 32ks + 16 + 4q + {0..3} (the accumulator layout), matched by the C reads below.
         frag sop[N / 32][MBP];
@@ -747,7 +725,6 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 }
             }
         }
-        asm volatile("" ::"v"(touched.x), "v"(touched.y));  // the touch loads are long complete
     }
 }
 
