@@ -133,3 +133,33 @@ def test_one_sequence_per_row_is_bitwise_the_plain_prefill(impl):
         y2, f2 = ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=Q, impl=name)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("impl", ["fused", "unfused"])
+def test_packed_short_sequences_full_size(impl):
+    """The bench's packed workload at full size: the 32 x 1024-token short-sequence batch (H=128,
+    G=8, bf16, Q=128) packed into one row of 32768 tokens with seq_idx.  Sampled heads, every
+    token, against the oracle run on each sampled head alone (a head reads only its own x, dt,
+    A, D, dt_bias and its group's B and C)."""
+    from mamba_ssd_prefill_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["short_g8_bf16"]
+    inp = workload_inputs(w)
+    Bt, L, H = w.batch, w.seqlen, w.nheads
+    hpg = H // w.ngroups
+    packed = make_inputs(1, 1, H, w.headdim, w.dstate, w.ngroups, dtype=w.dtype, seed=0)
+    packed.x, packed.dt = inp.x.reshape(1, Bt * L, H, -1), inp.dt.reshape(1, Bt * L, H)
+    packed.B, packed.C = inp.B.reshape(1, Bt * L, w.ngroups, -1), inp.C.reshape(1, Bt * L, w.ngroups, -1)
+    packed.A, packed.D, packed.dt_bias, packed.h0 = inp.A, inp.D, inp.dt_bias, None
+    seq = torch.arange(Bt, dtype=torch.int32).repeat_interleave(L).reshape(1, Bt * L).contiguous()
+    say("packed short sequences", impl)
+    y, fin = run_varlen(packed, seq, w.chunk_size, impl)
+    for h in (0, 17, 64, 127):
+        g = h // hpg
+        one = make_inputs(1, 1, 1, w.headdim, w.dstate, 1, dtype=w.dtype, seed=0)
+        one.x, one.dt = packed.x[:, :, h:h + 1].contiguous(), packed.dt[:, :, h:h + 1].contiguous()
+        one.B, one.C = packed.B[:, :, g:g + 1].contiguous(), packed.C[:, :, g:g + 1].contiguous()
+        one.A, one.D, one.dt_bias, one.h0 = packed.A[h:h + 1], packed.D[h:h + 1], packed.dt_bias[h:h + 1], None
+        yr, fr = oracle.recurrence_varlen(**one.args(), seq_idx=seq)
+        skip = f64(one.D)[None, None, :, None] * f64(one.x)
+        gate(f64(y[:, :, h:h + 1]), yr, "bf16", "bf16", skip=skip, name="packed %s head %d y" % (impl, h))
+        gate(f64(fin[:, h:h + 1]), fr, "f32", "bf16", name="packed %s head %d final" % (impl, h))
