@@ -162,8 +162,8 @@ const char* ssd_status_string(ssd_status_t s);
  *           fused: [B*G + 7][nc][Q][Q], one [nc] run per (work partition, (b, g) pair)
  *   s       fp32 [B][nc][H][P][N]    chunk-end state from a zero start            chunk_state
  *           unfused: as shown; fused: 0 bytes, or with the relay form's buffers (below) a
- *           ring of 32 chunk states per chain ([B][H][P][N] x 32 fp32) followed by a ring of
- *           min(16, nc + 1) states in in_dtype ([B][H][P][N] x min(16, nc + 1)), both in the
+ *           ring of 10 chunk states per chain ([B][H][P][N] x 10 fp32) followed by a ring of
+ *           min(6, nc + 1) states in in_dtype ([B][H][P][N] x min(6, nc + 1)), both in the
  *           fused kernel's own order
  *   states  state_dtype, K slots     state entering chunk c lives in slot c % K; slot 0
  *                                    holds the initial state, slot nc % K the final one

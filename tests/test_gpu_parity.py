@@ -52,7 +52,7 @@ CASES = [
     ("f16", "f32", True, 3, 200, 12, 64, 64, 12, 64),   # G = H
     ("bf16", "bf16", True, 1, 260, 4, 64, 128, 1, 128),
     ("f32", "f32", False, 1, 256, 4, 16, 16, 1, 64),
-    # 41 chunks: wraps the relay form's 32-slot chunk-state ring and 16-slot operand ring
+    # 41 chunks: wraps the relay form's 10-slot chunk-state ring and 6-slot operand ring several times
     ("bf16", "f32", True, 1, 40 * 128 + 7, 4, 64, 128, 1, 128),
     ("f16", "f16", True, 1, 40 * 64 + 33, 2, 64, 64, 1, 64),
 ]
