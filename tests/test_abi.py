@@ -276,3 +276,20 @@ def test_varlen_validates_like_prefill(lib, field):
     assert call_varlen(lib, p, prefill_args(p, **{field: None}), FAKE) == NULLP
     assert call_varlen(lib, base(headdim=48), prefill_args(p, ws_bytes=1 << 30), FAKE) == UNSUP
     assert call_varlen(lib, p, prefill_args(p, ws_bytes=ssd.workspace_size(p) - 1), FAKE) == WS_SMALL
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    """include/mamba_ssd.h is a C header: a C11 translation unit that takes the address of every
+    declared function compiles with gcc (no HIP or C++ needed by callers)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use_header.c"
+    refs = "\n".join("    (void)&%s;" % f for f in header_functions())
+    src.write_text('#include "mamba_ssd.h"\nint main(void) {\n    ssd_params_t p = {0};\n    (void)p;\n%s\n'
+                   "    return 0;\n}\n" % refs)
+    r = subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
+                        str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
