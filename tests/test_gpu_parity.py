@@ -52,6 +52,11 @@ CASES = [
     ("f16", "f32", True, 3, 200, 12, 64, 64, 12, 64),   # G = H
     ("bf16", "bf16", True, 1, 260, 4, 64, 128, 1, 128),
     ("f32", "f32", False, 1, 256, 4, 16, 16, 1, 64),
+    # y leaves through LDS in whole token rows when every head of a tile is valid: four heads
+    # per tile at P = 32; and 3 heads per group at P = 64, where one tile of each group holds a
+    # single head and stores y directly, in the same launch
+    ("bf16", "f32", True, 1, 300, 8, 32, 128, 1, 128),
+    ("bf16", "f32", True, 2, 300, 6, 64, 128, 2, 128),
     # 41 chunks: wraps the relay form's 10-slot chunk-state ring and 6-slot operand ring several times
     ("bf16", "f32", True, 1, 40 * 128 + 7, 4, 64, 128, 1, 128),
     ("f16", "f16", True, 1, 40 * 64 + 33, 2, 64, 64, 1, 64),
