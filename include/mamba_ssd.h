@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 /* Element types.  x, dt, B, C and y share `in_dtype`; initial_state, final_state
  * and the inter-chunk states use `state_dtype`; A, D and dt_bias are always fp32. */
@@ -82,6 +82,12 @@ typedef struct {
  *   dt            [B, L, H]     in_dtype     required (raw step, before bias / softplus)
  *   A             [H]           fp32         required; A <= 0 is a precondition (not checked;
  *                                            A = 0 gives causal linear attention)
+ *   (dt)                                     with dt_softplus = 0 the step dt_raw + dt_bias may
+ *                                            have either sign (a negative step grows the state,
+ *                                            as the recurrence says); every decay is evaluated as
+ *                                            exp of a difference of fp32 in-chunk sums of dt * A,
+ *                                            so those sums must stay within about +-87 over any
+ *                                            chunk when some dt * A > 0 (fp32 exp range)
  *   B, C          [B, L, G, N]  in_dtype     required, 16-byte aligned
  *   D             [H]           fp32         NULL means 0
  *   dt_bias       [H]           fp32         NULL means 0
@@ -131,9 +137,13 @@ ssd_status_t ssd_prefill_timed(const ssd_params_t* p,
  *                           there from S = 0.
  * Each batch row's initial_state is the state entering its first sequence, and
  * final_state[b] is the state after token L-1 (of its last sequence); sequences in the
- * middle of a row start from zero and their end states are not written out.  The decay
- * into a sequence start is exp(-128) = 0 in fp32 (the chunk_cumsum step adds -128 to that
- * token's log-decay), so nothing crosses the boundary in any of the five steps. */
+ * middle of a row start from zero and their end states are not written out.  The
+ * chunk_cumsum step counts the sequence starts inside each chunk (workspace `seg`) and every
+ * later step masks with those counts: a decay between two tokens is used only when both lie
+ * in one sequence, the state entering a chunk only reaches the tokens before the chunk's
+ * first sequence start, and a chunk with a start inside passes on only its last sequence's
+ * state.  The in-chunk log-decay sums are those of the unpacked input, so packing costs no
+ * precision. */
 ssd_status_t ssd_prefill_varlen(const ssd_params_t* p,
                                 const void* x, const void* dt, const float* A,
                                 const void* B, const void* C,
@@ -172,6 +182,8 @@ const char* ssd_status_string(ssd_status_t s);
  *                    K = 2, the initial state in slot 0 and the final one in slot 1), in an
  *                    internal lane-major order (the fused kernel's own layout); without an
  *                    initial state slot 0 is not filled (the kernel takes S_0 = 0)
+ *   seg     int32 [B][nc][Q]         packed input (ssd_prefill_varlen) only: the number of
+ *                                    sequence starts among chunk tokens 0 .. i   chunk_cumsum
  *   sync    uint32 words: per-chain words (three 128-byte lines each: progress counter,
  *           relay slot words), cumsum / bmm completion flags, one
  *           work counter and one owner word per partition, the exit counter and the
@@ -193,6 +205,7 @@ typedef struct {
     size_t dt_bytes, acs_bytes, cb_bytes, s_bytes, states_bytes, sync_bytes;
     int nchunks;
     int state_slots;  /* K */
+    size_t seg_offset, seg_bytes;
 } ssd_workspace_layout_t;
 
 ssd_status_t ssd_workspace_layout(const ssd_params_t* p, ssd_workspace_layout_t* out);

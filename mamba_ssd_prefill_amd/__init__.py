@@ -23,7 +23,7 @@ DTYPE_CODES = {"f32": SSD_F32, "f16": SSD_F16, "bf16": SSD_BF16}
 IMPL_CODES = {"unfused": 0, "fused": 1}
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_INVALID_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
                 4: "SSD_ERR_MISALIGNED", 5: "SSD_ERR_WORKSPACE_TOO_SMALL", 6: "SSD_ERR_HIP",
-                7: "SSD_ERR_SYNC_TIMEOUT", 8: "SSD_ERR_INVALID_ARGUMENT"}
+                7: "SSD_ERR_SYNC_TIMEOUT", 8: "SSD_ERR_INVALID_ARGUMENT", 9: "SSD_ERR_SCHEDULE"}
 EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill", "ssd_prefill_timed",
                     "ssd_check_device_status",
                     "ssd_status_string", "ssd_workspace_layout", "ssd_step_chunk_cumsum", "ssd_step_bmm",
@@ -55,7 +55,7 @@ class Layout(ctypes.Structure):
                 ("sync_offset", ctypes.c_size_t), ("status_offset", ctypes.c_size_t), ("dt_bytes", ctypes.c_size_t),
                 ("acs_bytes", ctypes.c_size_t), ("cb_bytes", ctypes.c_size_t), ("s_bytes", ctypes.c_size_t),
                 ("states_bytes", ctypes.c_size_t), ("sync_bytes", ctypes.c_size_t), ("nchunks", ctypes.c_int),
-                ("state_slots", ctypes.c_int)]
+                ("state_slots", ctypes.c_int), ("seg_offset", ctypes.c_size_t), ("seg_bytes", ctypes.c_size_t)]
 
 
 _lib = None

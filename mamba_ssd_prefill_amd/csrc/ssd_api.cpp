@@ -130,6 +130,7 @@ Layout layout(const ssd_params_t* p) {
     w.s_bytes = fused ? (relay ? l.agg_bytes + B * H * P * N * elem_size(p->in_dtype) * l.op_slots : 0)
                       : B * nc * H * P * N * 4;
     w.states_bytes = B * K * H * P * N * elem_size(p->state_dtype);
+    w.seg_bytes = B * nc * Q * 4;
     l.nflags = fused ? B * H * (size_t)l.wph * ssd::kChainStride : 0;
     l.flags_w = 0;
     l.cs_w = l.nflags;
@@ -152,6 +153,8 @@ Layout layout(const ssd_params_t* p) {
     off = align_up(off + w.s_bytes);
     w.states_offset = off;
     off = align_up(off + w.states_bytes);
+    w.seg_offset = off;
+    off = align_up(off + w.seg_bytes);
     w.sync_offset = off;
     w.status_offset = off + 4 * l.status_w;
     off = align_up(off + w.sync_bytes);
@@ -185,6 +188,7 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.opnd = base + l.w.s_offset + l.agg_bytes;
     a.op_slots = l.op_slots;
     a.states = base + l.w.states_offset;
+    a.seg = (int*)(base + l.w.seg_offset);
     uint32_t* sync = (uint32_t*)(base + l.w.sync_offset);
     a.flags = sync + l.flags_w;
     a.cs_done = sync + l.cs_w;

@@ -7,7 +7,8 @@ namespace ssd {
 // state_passing ("Mamba-2炸裂升级！…", section "Mamba-2核心操作与融合的必要性", item 6):
 // one thread per 4 consecutive state elements of one (b, h), sequential over the chunks:
 // S_{c+1} = exp(acs_c[Q-1]) S_c + s_c, carried in fp32 and stored to slot c + 1 in the
-// state dtype.  Slot 0 holds the initial state (written by the boundary copy).
+// state dtype (the decay is 0 when a packed sequence starts inside chunk c).  Slot 0 holds
+// the initial state (written by the boundary copy).
 __global__ __launch_bounds__(256) void k_state_passing(SsdArgs a, int PN) {
     const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= PN) return;
@@ -16,7 +17,9 @@ __global__ __launch_bounds__(256) void k_state_passing(SsdArgs a, int PN) {
     f32x4 S = load_state4(a.states, a.state_dtype, ((size_t)b * K * H + h) * PN + e);
 #pragma unroll 4
     for (int c = 0; c < nc; ++c) {
-        const float dec = __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
+        // packed input: a sequence that starts inside chunk c passes no state on
+        const bool start = a.seq_idx && a.seg[((size_t)b * nc + c) * Q + Q - 1] != 0;
+        const float dec = start ? 0.f : __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
         const f32x4 sl = *(const f32x4*)(a.s + (((size_t)b * nc + c) * H + h) * PN + e);
         S = dec * S + sl;
         store_state4(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);

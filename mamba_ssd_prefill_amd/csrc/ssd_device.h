@@ -107,7 +107,7 @@ template <typename T, int P, int N> struct Geo {
     static constexpr int SZ_PHASE_S = SZ_BT + SZ_XW;
     static constexpr int SZ_PHASE_Y = SZ_C + SZ_L + SZ_XT;
     static constexpr int SZ_MAIN = SZ_PHASE_S > SZ_PHASE_Y ? SZ_PHASE_S : SZ_PHASE_Y;
-    static constexpr int SZ_VEC = 3 * HPT * QMAX * 4;  // dt, acs, chunk-state weights
+    static constexpr int SZ_VEC = (3 * HPT + 1) * QMAX * 4;  // dt, acs, chunk-state weights; seg
     static constexpr int SMEM = SZ_MAIN + SZ_VEC;
     static_assert(P % 16 == 0 && N % 16 == 0, "P and N must be multiples of 16");
     static_assert(KPL == 1 || N % 32 == 0, "16-bit inputs need N % 32 == 0");
@@ -486,6 +486,7 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     const uint32_t t0 = (uint32_t)(w * TPW);
     f32x4 S[TPW], B0[TPW], B1[TPW];
     float d0 = 0.f, d1 = 0.f;
+    uint32_t g0 = 0u, g1 = 0u;
     {
         const __amdgpu_buffer_rsrc_t r = ring_rsrc(a.states, sdt, ring_chain(b, 0, h, ph, K, H, WPH, NT), NT);
 #pragma unroll
@@ -499,13 +500,18 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     }
     int agg_hi = 0;  // chunk states 0 .. agg_hi - 1 are known to be in their slots
     int wr_hi = 0;   // states 0 .. wr_hi - 1 are known to be free to write
-    // L(c): TPW loads of s_c and one of acs_c[Q-1], into buf / d
-    auto issue_load = [&](int c, f32x4 (&buf)[TPW], float& d) {
+    // L(c): TPW loads of s_c, one of acs_c[Q-1] and one of seg_c[Q-1] (packed input: nonzero
+    // when a sequence starts inside chunk c, which then passes no state on; without packed
+    // input the descriptor covers 0 bytes and the load reads 0), into buf / d / sg
+    auto issue_load = [&](int c, f32x4 (&buf)[TPW], float& d, uint32_t& sg) {
         const __amdgpu_buffer_rsrc_t r = agg_rsrc<NT>(a, b, h, ph, WPH, c % kAggSlots);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) buf[t] = bload_f32x4<AUX_L2>(r, ((t0 + t) * 64 + lane) * 16);
         d = bload_f32<AUX_L2>(make_rsrc(a.acs + (((size_t)b * nc + c) * H + h) * Q, (uint32_t)Q * 4),
                               (uint32_t)(Q - 1) * 4);
+        sg = __builtin_amdgcn_raw_buffer_load_b32(
+            make_rsrc(a.seg + ((size_t)b * nc + c) * Q, a.seq_idx ? (uint32_t)Q * 4 : 0u), (uint32_t)(Q - 1) * 4, 0,
+            AUX_L2);
     };
     // Step c: issue L(c + 1) if s_{c+1} is known to be ready, wait for L(c), publish S_{c-1},
     // else wait for s_{c+1} and issue L(c + 1) now; fold s_c in; store S_{c+1} (St(c + 1),
@@ -513,11 +519,12 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     // |St(c)| + |L(c + 1)| operations are pending (|St(c)| alone if L(c + 1) is not issued yet),
     // L(c) and everything before it (St(c - 1) too) are complete.  Any extra operation in
     // between (a poll, a flag) only makes the count wait for more.
-    constexpr int NST = TPW / TPU, NLD = TPW + 1;
-    auto step = [&](int c, f32x4 (&cur)[TPW], float dcur, f32x4 (&nxt)[TPW], float& dnxt) -> bool {
+    constexpr int NST = TPW / TPU, NLD = TPW + 2;
+    auto step = [&](int c, f32x4 (&cur)[TPW], float dcur, uint32_t gcur, f32x4 (&nxt)[TPW], float& dnxt,
+                    uint32_t& gnxt) -> bool {
         const bool has_next = c + 1 < nc;
         const bool early = has_next && c + 1 < agg_hi;
-        if (early) issue_load(c + 1, nxt, dnxt);
+        if (early) issue_load(c + 1, nxt, dnxt, gnxt);
         asm volatile("" ::: "memory");
         if (early) {
             if (c >= 1)
@@ -543,10 +550,10 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
             if (n == 0) return false;
             agg_hi = c + 1 + n;
             asm volatile("" ::: "memory");
-            issue_load(c + 1, nxt, dnxt);
+            issue_load(c + 1, nxt, dnxt, gnxt);
             asm volatile("" ::: "memory");
         }
-        const float dec = __expf(dcur);
+        const float dec = gcur ? 0.f : __expf(dcur);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) S[t] = dec * S[t] + cur[t];
         const int m = c + 1;  // the state written now
@@ -571,10 +578,10 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
         ok = n > 0;
         agg_hi = n;
     }
-    if (ok) issue_load(0, B0, d0);
+    if (ok) issue_load(0, B0, d0, g0);
     for (int c = 0; ok && c < nc; c += 2) {
-        ok = step(c, B0, d0, B1, d1);
-        if (ok && c + 1 < nc) ok = step(c + 1, B1, d1, B0, d0);
+        ok = step(c, B0, d0, g0, B1, d1, g1);
+        if (ok && c + 1 < nc) ok = step(c + 1, B1, d1, g1, B0, d0, g0);
     }
     // the final state, in the state dtype, for the boundary copy
     const __amdgpu_buffer_rsrc_t rf = ring_rsrc(a.states, sdt, ring_chain(b, 1, h, ph, K, H, WPH, NT), NT);
@@ -636,11 +643,12 @@ __device__ inline bool relay_handoff(const SsdArgs& a, int b, int c, int h, int 
 // the lane totals.
 // Packed variable-length input ([KF] "与vLLM的深度融合": sequences told apart by a per-token
 // sequence index and masked, not offset): a token t > 0 whose seq_idx differs from token
-// t - 1's starts a new sequence, and its log-decay gets kSeqStartLogDecay added.  Every later
-// step only ever uses exp of acs differences and of acs itself, so the decay across a sequence
-// start -- into the chunk state, through the state passing, in the C . S term and in L --
-// underflows to exactly 0, while inside a sequence the offsets cancel.  The state entering a
-// batch row (the initial state) belongs to its first sequence.
+// t - 1's starts a new sequence.  acs stays the plain in-chunk sum; wave 0 also writes
+// seg[b][c][i] = the number of sequence starts among chunk tokens 0 .. i (tokens past L add
+// none).  Two tokens i >= j of a chunk belong to one sequence exactly when seg[i] == seg[j]
+// (sequences are contiguous), and the state entering the chunk reaches token i exactly when
+// seg[i] == 0; every later step masks its decays with these tests, so nothing crosses a
+// sequence start and the in-chunk sums lose no precision to the masking.
 template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c, int h0, int h1) {
     const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int Q = a.chunk, L = a.seqlen, H = a.nheads, nc = a.nchunks;
@@ -656,14 +664,11 @@ template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c
             d[k] = 0.f;
             if (k < V) {
                 const int t = c * Q + lane * V + k;
-                float start = 0.f;
                 if (t < L) {
                     const float z = f32of(dtr[((size_t)b * L + t) * H + h]) + bias;
                     d[k] = a.softplus ? softplus_f(z) : z;
-                    if (a.seq_idx && t > 0 && a.seq_idx[(size_t)b * L + t] != a.seq_idx[(size_t)b * L + t - 1])
-                        start = kSeqStartLogDecay;
                 }
-                tot += d[k] * Ah + start;
+                tot += d[k] * Ah;
             }
             run[k] = tot;
         }
@@ -681,6 +686,28 @@ template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c
                 a.dtf[base + k] = d[k];
                 a.acs[base + k] = excl + run[k];
             }
+    }
+    if (a.seq_idx && wave == 0) {
+        const int* sq = a.seq_idx + (size_t)b * L;
+        int run[4], tot = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (k < V) {
+                const int t = c * Q + lane * V + k;
+                tot += (t > 0 && t < L && sq[t] != sq[t - 1]) ? 1 : 0;
+            }
+            run[k] = tot;
+        }
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const size_t base = ((size_t)b * nc + c) * Q + (size_t)lane * V;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (k < V) a.seg[base + k] = incl - tot + run[k];
     }
 }
 
@@ -813,6 +840,8 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
     float* sDt = (float*)(smem + G_::SZ_MAIN);  // [HPT][QMAX]
     float* sAcs = sDt + HPT * QMAX;             // [HPT][QMAX]
     float* sW = sAcs + HPT * QMAX;              // [HPT][QMAX] chunk-state weights
+    int* sSeg = (int*)(sW + HPT * QMAX);        // [QMAX] packed input: sequence starts up to token i
+    const bool varlen = a.seq_idx != nullptr;
 
     {
         // heads of the tile past the group read as zeros
@@ -825,13 +854,21 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
             sDt[hh * QMAX + i] = bload_f32<AUX>(rdt, (uint32_t)e * 4);
             sAcs[hh * QMAX + i] = bload_f32<AUX>(ra, (uint32_t)e * 4);
         }
+        if (varlen) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.seg + ((size_t)b * nc + c) * Q, (uint32_t)Q * 4);
+            for (int e = tid; e < Q; e += 256) sSeg[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, e * 4, 0, AUX);
+        }
     }
     __syncthreads();
+    // chunk-state weights; with packed input only the chunk's last sequence reaches its end
     for (int e = tid; e < HPT * Q; e += 256) {
         const int hh = e / Q, i = e - hh * Q;
-        sW[hh * QMAX + i] = __expf(sAcs[hh * QMAX + Q - 1] - sAcs[hh * QMAX + i]) * sDt[hh * QMAX + i];
+        const float w = __expf(sAcs[hh * QMAX + Q - 1] - sAcs[hh * QMAX + i]) * sDt[hh * QMAX + i];
+        sW[hh * QMAX + i] = (varlen && sSeg[i] != sSeg[Q - 1]) ? 0.f : w;
     }
     const float acs_last = sAcs[hs * QMAX + Q - 1];
+    // the state entering the chunk survives to its end unless a sequence starts inside it
+    const bool carry = !varlen || sSeg[Q - 1] == 0;
 
     // S_c in accumulator layout: tile (nb, pb), lane -> S[p = ph*PW + pb*16 + r16][n = nb*16 + 4q + r]
     f32x4 sc[NB][MBP];
@@ -895,7 +932,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const __amdgpu_buffer_rsrc_t rout =
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
-                const float dec = __expf(acs_last);
+                const float dec = carry ? __expf(acs_last) : 0.f;
                 const bool zero0 = c == 0 && !a.has_h0;  // S_0 = 0: nothing to read
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
@@ -975,7 +1012,8 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                 }
 #pragma unroll
                 for (int ib = 0; ib < WB; ++ib) {
-                    const float e = __expf(sAcs[hs * QMAX + i0 + ib * 16 + r16]);
+                    const int i = i0 + ib * 16 + r16;  // S_c reaches row i only inside the chunk's first sequence
+                    const float e = (varlen && sSeg[i] != 0) ? 0.f : __expf(sAcs[hs * QMAX + i]);
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) accY[pb][ib] *= e;
                 }
@@ -988,8 +1026,8 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                                                    ok ? xg + ((size_t)b * L * H + head0 + hh) * P : nullptr,
                                                    (size_t)H * P, tok0 + j0, L, nullptr, tid, 256);
                 }
-                // L[i][j] = CB[i][j] exp(acs_i - acs_j) dt_j for j <= i, else 0 (log-space
-                // decay differences in fp32, [HW] segsum section, [XLA] 2.2)
+                // L[i][j] = CB[i][j] exp(acs_i - acs_j) dt_j for j <= i in i's sequence, else 0
+                // (log-space decay differences in fp32, [HW] segsum section, [XLA] 2.2)
                 for (int it = tid; it < W * (W / 4); it += 256) {
                     const int jq = it % (W / 4), ii = it / (W / 4);
                     const int i = i0 + ii, j = j0 + 4 * jq;
@@ -1001,7 +1039,8 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float v = cbv[e] * __expf(ai - sAcs[hh * QMAX + j + e]) * sDt[hh * QMAX + j + e];
-                            lv[e] = (j + e <= i) ? v : 0.f;
+                            const bool same = !varlen || sSeg[i] == sSeg[j + e];
+                            lv[e] = (j + e <= i && same) ? v : 0.f;
                         }
                         *(v4*)(sL + (hh * W + ii) * LDW + 4 * jq) = cvt4<T>(lv);
                     }

@@ -8,10 +8,6 @@
 
 namespace ssd {
 
-// Log-decay added at every token that starts a new sequence of packed variable-length input:
-// exp(-128) underflows to 0 in fp32, so every decay across the sequence start vanishes.
-constexpr float kSeqStartLogDecay = -128.f;
-
 // Largest number of XCDs (L2 domains) the fused form partitions its work over.
 constexpr int kMaxXcc = 8;
 
@@ -25,6 +21,7 @@ struct SsdArgs {
     const float* D;
     const float* dt_bias;
     const int* seq_idx;  // [B][L] sequence ids of packed variable-length input, or nullptr
+    int* seg;            // [B][nc][Q] with seq_idx: sequence starts among chunk tokens 0..i
     void* y;
     float* dtf;          // [B][nc][H][Q]
     float* acs;          // [B][nc][H][Q]

@@ -39,7 +39,7 @@ template <typename T, int P, int N, int Q> struct Geo16 {
     static constexpr int QB = Q / 16;  // 16-token row blocks
     static constexpr int SZ_X = HPT * Q * P * 2;
     static constexpr int SZ_BC = Q * N * 2;
-    static constexpr int SZ_V = 3 * HPT * Q * 4;  // dt, acs, chunk-state weights
+    static constexpr int SZ_V = (3 * HPT + 1) * Q * 4;  // dt, acs, chunk-state weights; seg
     // CB (fp32) staged in LDS as 32-row bands holding only the columns the diagonal block
     // reads: band r (rows 32r .. 32r+31) keeps columns [0, 32(r+1)) in rows of 8(r+1)+1
     // 16-byte pieces (the odd pitch spreads 16 consecutive rows over all bank groups), each
@@ -66,6 +66,10 @@ template <typename T, int P, int N, int Q> struct Geo16 {
     // for three
     static constexpr int OCC = Q == 64 ? 3 : 2;
     static_assert(Q % 32 == 0 && Q <= 256, "Q must be a multiple of 32, at most 256");
+    // OCC is the register budget's hint; the LDS decides the real count (hipOccupancy at launch).
+    // They agree for P >= 64 at Q <= 128; Q = 256 and the 4-head tiles at N = 128, Q = 128 hold
+    // one workgroup per CU by their LDS.
+    static_assert(!(P >= 64 && Q <= 128) || OCC * SMEM <= 160 * 1024, "OCC workgroups must fit in 160 KB of LDS");
     static_assert(N % 32 == 0, "N % 32 == 0");
 };
 
@@ -187,10 +191,14 @@ template <typename G_> __device__ inline int lband_off(int i, int jp) {
 //   factored: j's 16-token block ends before row i (all of a 32-block left of the diagonal,
 //             and the lower-left 16x16 of a diagonal 32-block): L = CB * exp(acs_i - acs_m) *
 //             sF[j], with m = the last token of j's 16-block and sF[j] = exp(acs_m - acs_j) dt_j.
-//             Both factors are at most 1 (acs does not increase along the chunk), so nothing
-//             overflows; a factor underflows only when the exact product is below e^-87.
-//   diagonal: i and j in the same 16-token block: L = CB * exp2(acs_i log2 e - sE[j]) with
-//             sE[j] = acs_j log2 e - log2 dt_j, masked to j <= i;
+//             Both factors are at most 1 when dt A <= 0 (acs does not increase along the chunk),
+//             so nothing overflows; a factor underflows only when the exact product is below
+//             e^-87.  Packed input: i and j are in one sequence exactly when j and m are and m
+//             and i are (sequences are contiguous), so sF[j] carries the first test and the row
+//             factor the second;
+//   diagonal: i and j in the same 16-token block: L = CB * exp(acs_i - acs_j) * dt_j, masked to
+//             j <= i (and, packed, to seg[j] == seg[i]) -- a product with dt_j, so any sign of dt
+//             is handled;
 //   zero:     the upper-right 16x16 of a diagonal 32-block.
 // load() reads this thread's CB pieces from HBM/L2 into registers (issued early, so the reads
 // overlap other work); store() writes the L pieces of every valid head into LDS.
@@ -258,17 +266,20 @@ template <typename T, typename G_, int AUX> struct LBuild {
         }
     }
 
-    __device__ inline void store(T* sL, const float* sA2, const float* sF, const float* sE, int nvh, int tid) {
+    __device__ inline void store(T* sL, const float* sA2, const float* sF, const float* sDt, const int* sSeg,
+                                 bool varlen, int nvh, int tid) {
 #pragma unroll
         for (int it = 0; it < FI; ++it) {
             const int k = tid + it * 256;
             if (k < NF) {
                 const int i = fi[it], jp = fj[it], j0 = 8 * jp;
                 const int o = lband_off<G_>(i, jp) * 8;
+                const bool row_same = !varlen || sSeg[i] == sSeg[j0 | 15];
 #pragma unroll
                 for (int hh = 0; hh < HPT; ++hh) {
                     if (hh < nvh) {
-                        const float g = __builtin_amdgcn_exp2f(sA2[hh * Q + i] - sA2[hh * Q + (j0 | 15)]);
+                        const float gx = __builtin_amdgcn_exp2f(sA2[hh * Q + i] - sA2[hh * Q + (j0 | 15)]);
+                        const float g = row_same ? gx : 0.f;
                         const f32x4 f0 = *(const f32x4*)(sF + hh * Q + j0) * g;
                         const f32x4 f1 = *(const f32x4*)(sF + hh * Q + j0 + 4) * g;
                         *(frag*)(sL + (size_t)hh * (G_::SZ_LH / sizeof(T)) + o) = pack8<T>(cf[it][0] * f0, cf[it][1] * f1);
@@ -284,17 +295,22 @@ template <typename T, typename G_, int AUX> struct LBuild {
                 d_item(k, i, jp);
                 const int j0 = 8 * jp;
                 const int o = lband_off<G_>(i, jp) * 8;
+                bool keep[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) keep[e] = j0 + e <= i && (!varlen || sSeg[j0 + e] == sSeg[i]);
 #pragma unroll
                 for (int hh = 0; hh < HPT; ++hh) {
                     if (hh < nvh) {
                         const float ai = sA2[hh * Q + i];
-                        const f32x4 e0 = *(const f32x4*)(sE + hh * Q + j0);
-                        const f32x4 e1 = *(const f32x4*)(sE + hh * Q + j0 + 4);
+                        const f32x4 a0 = *(const f32x4*)(sA2 + hh * Q + j0);
+                        const f32x4 a1 = *(const f32x4*)(sA2 + hh * Q + j0 + 4);
+                        const f32x4 d0 = *(const f32x4*)(sDt + hh * Q + j0);
+                        const f32x4 d1 = *(const f32x4*)(sDt + hh * Q + j0 + 4);
                         f32x4 l0, l1;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            l0[e] = j0 + e <= i ? cd[it][0][e] * __builtin_amdgcn_exp2f(ai - e0[e]) : 0.f;
-                            l1[e] = j0 + 4 + e <= i ? cd[it][1][e] * __builtin_amdgcn_exp2f(ai - e1[e]) : 0.f;
+                            l0[e] = keep[e] ? cd[it][0][e] * __builtin_amdgcn_exp2f(ai - a0[e]) * d0[e] : 0.f;
+                            l1[e] = keep[e + 4] ? cd[it][1][e] * __builtin_amdgcn_exp2f(ai - a1[e]) * d1[e] : 0.f;
                         }
                         *(frag*)(sL + (size_t)hh * (G_::SZ_LH / sizeof(T)) + o) = pack8<T>(l0, l1);
                     }
@@ -338,12 +354,14 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     float* sCB = (float*)smem;
     T* sBC = (T*)(smem + G_::SZ_R1);                      // R2: [Q][N] B, later C
     // per-token vectors, [HPT][Q] each: sA2 = acs * log2(e); sW = chunk-state weights
-    // exp(acs[Q-1] - acs_j) dt_j, later replaced by sF; sDt = dt, later replaced by sE (see below)
+    // exp(acs[Q-1] - acs_j) dt_j, later replaced by sF (see below); sDt = dt; then [Q] sSeg =
+    // the sequence starts among chunk tokens 0 .. i (packed input only, shared by the heads)
     float* sA2 = (float*)(smem + G_::SZ_R1 + G_::SZ_BC);
     float* sW = sA2 + HPT * Q;
     float* sDt = sW + HPT * Q;
     float* sF = sW;
-    float* sE = sDt;
+    int* sSeg = (int*)(sDt + HPT * Q);
+    const bool varlen = a.seq_idx != nullptr;
 
     // read now: a load issued just before its use in the y loop would make every row block wait
     // for all of the tile's outstanding memory operations
@@ -373,16 +391,24 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             sDt[e] = bload_f32<AUX>(rdt, (uint32_t)e * 4);
             sA2[e] = bload_f32<AUX>(ra, (uint32_t)e * 4) * LOG2E;
         }
+        if (varlen) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.seg + ((size_t)b * nc + c) * Q, (uint32_t)Q * 4);
+            for (int e = tid; e < Q; e += 256) sSeg[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, e * 4, 0, AUX);
+        }
     }
-    lds_barrier();  // dt, acs in LDS (the x / B copies may still be in flight)
+    lds_barrier();  // dt, acs (seg) in LDS (the x / B copies may still be in flight)
+    // chunk-state weights; with packed input only the chunk's last sequence reaches its end
     for (int e = tid; e < HPT * Q; e += 256) {
         const int hh = e / Q;
-        sW[e] = __builtin_amdgcn_exp2f(sA2[hh * Q + Q - 1] - sA2[e]) * sDt[e];
+        const float w = __builtin_amdgcn_exp2f(sA2[hh * Q + Q - 1] - sA2[e]) * sDt[e];
+        sW[e] = (varlen && sSeg[e - hh * Q] != sSeg[Q - 1]) ? 0.f : w;
     }
     wait_vm_all();
     __syncthreads();
 
     const float* a2_h = sA2 + hs * Q;
+    // the state entering the chunk reaches its end unless a packed sequence starts inside it
+    const bool carry = !varlen || sSeg[Q - 1] == 0;
 
     // x operand, token-major: xf[kk][pb] holds x[kk*32 + 8q .. +7][ph*PW + pcol(pb, r16)]
     frag xf[KS][MBP];
@@ -466,7 +492,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const __amdgpu_buffer_rsrc_t rout =
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
-                const float dec = __builtin_amdgcn_exp2f(a2_h[Q - 1]);
+                const float dec = carry ? __builtin_amdgcn_exp2f(a2_h[Q - 1]) : 0.f;
                 const bool zero0 = c == 0 && !a.has_h0;  // S_0 = 0: nothing to read
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
@@ -506,16 +532,15 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
 
     if constexpr (MODE != MODE_STATE) {
         // ---- chunk_scan, 16 rows of y at a time ----
-        // Per-token factors for the diagonal block, replacing sW and sDt in place (each element
-        // is rewritten by the thread that reads it):
-        //   sF[j] = exp(acs_r - acs_j) dt_j, r = the last token of j's 32-token block (<= dt_j);
-        //   sE[j] = acs_j log2(e) - log2(dt_j)  (+inf when dt_j = 0).
-        // Off the diagonal (all of a 32-column block left of the 16 rows) L[i][j] is split as
-        // exp(acs_i - acs_r) * exp(acs_r - acs_j) dt_j: both factors are at most 1 because acs does
-        // not increase along the chunk, so nothing overflows, and a factor only underflows when
-        // the exact product is below e^-87.  The column factor scales x once per tile; the row
-        // factor is one exp per lane per block.  On the diagonal, each element takes its own
-        // exp2(acs_i log2(e) - sE[j]) = exp(acs_i - acs_j) dt_j.
+        // Per-token column factors, replacing sW in place (each element is rewritten by the
+        // thread that reads it): sF[j] = exp(acs_r - acs_j) dt_j, r = the last token of j's
+        // 32-token block (<= dt_j when dt A <= 0); packed input: 0 unless j and r are in one
+        // sequence.  Off the diagonal (all of a 32-column block left of the 16 rows) L[i][j] is
+        // split as exp(acs_i - acs_r) * exp(acs_r - acs_j) dt_j: both factors are at most 1 when
+        // acs does not increase along the chunk, so nothing overflows, and a factor only
+        // underflows when the exact product is below e^-87.  The column factor scales x once per
+        // tile; the row factor is one exp per lane per block (packed: 0 unless r and i are in
+        // one sequence).  On the diagonal, each element takes its own exp(acs_i - acs_j) * dt_j.
         // (With the L bands, the column factors end at 16-token blocks instead: see LBuild.)
         //
         // x for the D x term in the y layout (x[ib*16 + r16][ph*PW + 4 MBP q + 4 pb .. +3]).  While the
@@ -542,16 +567,15 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         }
         for (int e = tid; e < HPT * Q; e += 256) {
             const int hh = e / Q, j = e - hh * Q;
-            const float dt = sDt[e];
-            const float ar = sA2[hh * Q + (G_::L_LDS ? (j | 15) : (j | 31))];
-            sF[e] = __builtin_amdgcn_exp2f(ar - sA2[e]) * dt;
-            sE[e] = sA2[e] - __log2f(dt);
+            const int r = G_::L_LDS ? (j | 15) : (j | 31);
+            const float f = __builtin_amdgcn_exp2f(sA2[hh * Q + r] - sA2[e]) * sDt[e];
+            sF[e] = (varlen && sSeg[j] != sSeg[r]) ? 0.f : f;
         }
         lds_barrier();
         if constexpr (G_::L_LDS) {
             const int nvh = hpg - tig * HPT < HPT ? hpg - tig * HPT : HPT;
-            lb.store((T*)smem, sA2, sF, sE, nvh, tid);  // over x (already in registers)
-            lds_barrier();                              // L is complete
+            lb.store((T*)smem, sA2, sF, sDt, sSeg, varlen, nvh, tid);  // over x (already in registers)
+            lds_barrier();                                             // L is complete
         }
         if (!hvalid) return;
         // S_c as the A operand of C . S^T; k slots of step ks: n = 32ks + 4q + {0..3} and
@@ -565,7 +589,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         // x scaled by the column factor, for the blocks left of the diagonal (without L bands)
         frag xs[KS][MBP];
         const float* f_h = sF + hs * Q;
-        const float* e_h = sE + hs * Q;
+        const float* dt_h = sDt + hs * Q;
         const T* sL_h = (const T*)smem + (size_t)hs * G_::SZ_LH / sizeof(T);
 #pragma unroll
         for (int kk = 0; kk + 1 < (G_::L_LDS ? 0 : KS); ++kk) {
@@ -611,7 +635,8 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 for (int pb = 0; pb < MBP; ++pb) accY[pb] = TT<T>::mma(sop[ks][pb], cf, accY[pb]);
             }
             const float ai2 = a2_h[i];
-            const float ei = __builtin_amdgcn_exp2f(ai2);
+            // S_c reaches row i only inside the chunk's first packed sequence
+            const float ei = (varlen && sSeg[i] != 0) ? 0.f : __builtin_amdgcn_exp2f(ai2);
 #pragma unroll
             for (int pb = 0; pb < MBP; ++pb) accY[pb] *= ei;
             const int kd = ib >> 1;  // the diagonal 32-column block of these 16 rows
@@ -636,19 +661,23 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0 + 4) * 4, 0, CB_AUX));
                 }
                 if (kk < kd) {
-                    const float gi = __builtin_amdgcn_exp2f(ai2 - a2_h[kk * 32 + 31]);
+                    const float gx = __builtin_amdgcn_exp2f(ai2 - a2_h[kk * 32 + 31]);
+                    const float gi = (varlen && sSeg[i] != sSeg[kk * 32 + 31]) ? 0.f : gx;
                     const frag lf = pack8<T>(c0 * gi, c1 * gi);
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) accY[pb] = TT<T>::mma(xs[kk][pb], lf, accY[pb]);
                 } else {
-                    const f32x4 e0 = *(const f32x4*)(e_h + j0), e1 = *(const f32x4*)(e_h + j0 + 4);
+                    const f32x4 a0 = *(const f32x4*)(a2_h + j0), a1 = *(const f32x4*)(a2_h + j0 + 4);
+                    const f32x4 d0 = *(const f32x4*)(dt_h + j0), d1 = *(const f32x4*)(dt_h + j0 + 4);
                     f32x4 l0, l1;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float v0 = c0[e] * __builtin_amdgcn_exp2f(ai2 - e0[e]);
-                        const float v1 = c1[e] * __builtin_amdgcn_exp2f(ai2 - e1[e]);
-                        l0[e] = j0 + e <= i ? v0 : 0.f;
-                        l1[e] = j0 + 4 + e <= i ? v1 : 0.f;
+                        const float v0 = c0[e] * __builtin_amdgcn_exp2f(ai2 - a0[e]) * d0[e];
+                        const float v1 = c1[e] * __builtin_amdgcn_exp2f(ai2 - a1[e]) * d1[e];
+                        const bool k0 = j0 + e <= i && (!varlen || sSeg[j0 + e] == sSeg[i]);
+                        const bool k1 = j0 + 4 + e <= i && (!varlen || sSeg[j0 + 4 + e] == sSeg[i]);
+                        l0[e] = k0 ? v0 : 0.f;
+                        l1[e] = k1 ? v1 : 0.f;
                     }
                     const frag lf = pack8<T>(l0, l1);
 #pragma unroll

@@ -8,7 +8,7 @@ import torch
 
 import mamba_ssd_prefill_amd as ssd
 import oracle
-from parity import gate
+from parity import StreamGate, gate
 
 DT_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 
@@ -98,3 +98,28 @@ def check_sampled(inp, y, fin, pairs, name=""):
     r1 = gate(ys, yr, in_dt, in_dt, skip=skip, name=name + " y")
     r2 = gate(fs, fr, st_dt, in_dt, name=name + " final")
     return r1, r2
+
+
+def check_all_chains(inp, y, fin, name="", heads_per_block=0):
+    """Every element of y and of the final state against the fp64 recurrence, one batch row
+    (or, with heads_per_block, one block of heads of a row) at a time, through StreamGate:
+    the whole-array gate without holding the whole fp64 reference.  y and fin may live on
+    the GPU; the inputs are the host tensors the GPU copy was made from."""
+    Bt, L, H, P = (int(s) for s in inp.x.shape)
+    hb = heads_per_block or H
+    in_dt = DT_NAME[inp.x.dtype]
+    gy = StreamGate(in_dt, in_dt, name + " y")
+    gf = StreamGate(DT_NAME[fin.dtype], in_dt, name + " final")
+    for b in range(Bt):
+        for h0 in range(0, H, hb):
+            h1 = min(H, h0 + hb)
+            yr, fr, _ = oracle.recurrence(**inp.args(), bh=[(b, h) for h in range(h0, h1)])  # [nh, L, P]
+            yg = y[b, :, h0:h1].permute(1, 0, 2).to(torch.float64).cpu()
+            skip = None
+            if inp.D is not None:
+                skip = inp.x[b, :, h0:h1].permute(1, 0, 2).to(torch.float64) * \
+                    inp.D[h0:h1].to(torch.float64)[:, None, None]
+            gy.add(yg, yr, skip)
+            gf.add(fin[b, h0:h1].to(torch.float64).cpu(), fr)
+            del yr, yg, skip
+    return gy.finish(), gf.finish()

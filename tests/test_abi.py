@@ -46,10 +46,31 @@ def test_library_exports_every_declared_function(lib):
         assert hasattr(lib, name), name
 
 
-def test_abi_struct_sizes_match_header():
-    # ssd_params_t: size_t + 11 ints -> 8 + 44 = 52, padded to 56 on LP64
-    assert ctypes.sizeof(ssd.Params) == 56
-    assert ctypes.sizeof(ssd.Layout) == 14 * 8 + 2 * 4
+def test_abi_struct_sizes_match_header(tmp_path):
+    """The binding's ctypes structs have the C header's sizes and field offsets (gcc, LP64)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    checks = [("ssd_params_t", ssd.Params), ("ssd_workspace_layout_t", ssd.Layout)]
+    lines = []
+    for cname, cls in checks:
+        lines.append('    printf("%%s %%zu\\n", "%s", sizeof(%s));' % (cname, cname))
+        for f, _ in cls._fields_:
+            lines.append('    printf("%%s.%%s %%zu\\n", "%s", "%s", offsetof(%s, %s));' % (cname, f, cname, f))
+    src = tmp_path / "sizes.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mamba_ssd.h"\nint main(void) {\n%s\n'
+                   "    return 0;\n}\n" % "\n".join(lines))
+    exe = tmp_path / "sizes"
+    r = subprocess.run([gcc, "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    for cname, cls in checks:
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(got["%s.%s" % (cname, f)]) == getattr(cls, f).offset, (cname, f)
 
 
 def test_status_strings(lib):
@@ -114,9 +135,10 @@ def test_workspace_layout_arithmetic(lib, impl, state, relay, monkeypatch):
     relay_bytes = Bt * H * P * N * (4 * 10 + 2 * min(6, nc + 1))
     assert lay.s_bytes == ((relay_bytes if relay_ws else 0) if fused else Bt * nc * H * P * N * 4)
     assert lay.states_bytes == Bt * K * H * P * N * es
+    assert lay.seg_bytes == Bt * nc * Q * 4
     regions = sorted([(lay.dt_offset, lay.dt_bytes), (lay.acs_offset, lay.acs_bytes), (lay.cb_offset, lay.cb_bytes),
                       (lay.s_offset, lay.s_bytes), (lay.states_offset, lay.states_bytes),
-                      (lay.sync_offset, lay.sync_bytes)])
+                      (lay.seg_offset, lay.seg_bytes), (lay.sync_offset, lay.sync_bytes)])
     for (o1, n1), (o2, _) in zip(regions, regions[1:]):
         assert o1 % 256 == 0 and o1 + n1 <= o2
     assert lay.sync_offset <= lay.status_offset < lay.sync_offset + lay.sync_bytes

@@ -95,6 +95,22 @@ def test_no_D_no_bias_no_softplus(impl):
 
 
 @pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_negative_steps(impl, dtype):
+    """dt_softplus = 0 with steps of either sign (dt = dt_raw, no bias): a negative step makes
+    dt * A > 0, so the in-chunk decay sums rise and fall; the recurrence (and the oracle) grow
+    the state there.  Every decay must stay finite and exact, the diagonal block included."""
+    say("negative steps", dtype, impl)
+    inp = make_inputs(2, 333, 4, 64, 128, 1, dtype=dtype, has_h0=True, seed=55)
+    inp.dt_bias = None
+    inp.dt = (0.02 * inp.dt.float()).to(inp.x.dtype)
+    inp.dt_softplus = False
+    assert bool((inp.dt.float() < 0).any()) and bool((inp.dt.float() > 0).any())
+    y, fin = run_gpu(inp, 64 if dtype == "f32" else 128, impl)
+    check_full(inp, y, fin, "negative dt %s" % dtype)
+
+
+@pytest.mark.parametrize("impl", IMPLS)
 def test_linear_attention_case(impl):
     """A = 0, dt = 1: causal linear attention (no decay)."""
     say("linear attention", impl)

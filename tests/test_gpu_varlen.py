@@ -105,6 +105,22 @@ def test_varlen_f32(impl):
     check(inp, seq, y, fin, "varlen f32 %s" % impl)
 
 
+@pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("shape", [(16, 16), (32, 64)], ids=["P16N16", "P32N64"])
+def test_varlen_f32_dozens_of_starts_per_chunk(impl, shape):
+    """fp32 inputs held to the fp32 contract (1e-5) with up to 31 sequence starts in one chunk:
+    30 sequences of one token, then longer ones, so later sequences of a chunk sit behind many
+    starts (the masked decays must lose nothing to them)."""
+    P, N = shape
+    Q, L = 64, 400
+    lens = [1] * 30 + [34, 2, 3, 1, 1, 5, 60, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 9, 100]
+    inp = make_inputs(2, L, 4, P, N, 1, dtype="f32", state_dtype="f32", has_h0=True, seed=8105 + P)
+    seq = seq_index([lens, [3] * 20 + [250]], L)
+    say("varlen f32 many starts", shape, impl)
+    y, fin = run_varlen(inp, seq, Q, impl)
+    check(inp, seq, y, fin, "varlen f32 many starts %s %s" % (shape, impl))
+
+
 @pytest.mark.parametrize("impl", ["unfused", "fused_hop", "fused_relay2"])
 def test_varlen_grouped_many_short_sequences(impl):
     # grouped B/C (4 heads per group), 24 sequences of 1..80 tokens in one row, no initial state
