@@ -185,19 +185,24 @@ const char* ssd_status_string(ssd_status_t s);
  *   seg     int32 [B][nc][Q]         packed input (ssd_prefill_varlen) only: the number of
  *                                    sequence starts among chunk tokens 0 .. i   chunk_cumsum
  *   sync    uint32 words: per-chain words (three 128-byte lines each: progress counter,
- *           relay slot words), cumsum / bmm completion flags, one
- *           work counter and one owner word per partition, the exit counter and the
- *           abort word (fused only)
+ *           relay slot words), cumsum / bmm completion flags, one work counter per
+ *           partition, then per partition an owner word, a count of the workgroups that
+ *           joined it and its relay decision, the exit counter and the abort word (fused only)
  *   status  uint32 device status word
  * The fused form splits its work into one partition per XCD of the device (at most 8);
  * the sizes above are bounds that hold for any such split.  Shapes with at most 128
  * chains (batch * ngroups * ceil(heads per group / heads per tile); 4 heads per tile
  * for headdim <= 32, 2 for 64, 1 for 128) get the buffers of the fused relay form, in which
  * dedicated work items (2 or 4 per chain) pass the state from chunk to chunk; it is used
- * when they take at most half of every partition's workgroups.  The environment variable
- * MAMBA_SSD_RELAY = 0 / 1 forces the buffers off / on (2 / 4: on, with that many items per
- * chain); it is read on every call, so workspace sizing and the call must see the same
- * value.
+ * when they take at most half of the workgroups a partition holds at once (the fused
+ * kernel's occupancy times the XCD's compute units), and each partition checks that rule
+ * again on the device against the workgroups that actually joined it, its chunk tiles
+ * passing the state themselves where it fails.  The environment variable MAMBA_SSD_RELAY =
+ * 0 / 1 forces the buffers off / on (2 / 4: on, with that many items per chain); it is read
+ * on every call, so workspace sizing and the call must see the same value.
+ * Test knobs, also read on every call: MAMBA_SSD_SPIN_LIMIT (polls before a wait gives up),
+ * MAMBA_SSD_RELAY_ADMIT=0 (every partition refuses its relay items) and
+ * MAMBA_SSD_GRID_LIMIT (caps the fused grid; unserved partitions give SSD_ERR_SCHEDULE).
  * ------------------------------------------------------------------------------------ */
 typedef struct {
     size_t total_bytes;

@@ -24,14 +24,23 @@ size_t elem_size(int dt) { return dt == SSD_F32 ? 4 : 2; }
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// MAMBA_SSD_SPIN_LIMIT: polls after which a fused-kernel wait gives up (read on every call, so
+// a test can make the kernel's own bounded waits give up and then run normally again).
 uint32_t spin_limit() {
-    static const uint32_t v = [] {
-        const char* e = getenv("MAMBA_SSD_SPIN_LIMIT");
-        if (!e || !*e) return kDefaultSpin;
-        const unsigned long x = strtoul(e, nullptr, 10);
-        return x ? (uint32_t)(x > 0xffffffffUL ? 0xffffffffUL : x) : kDefaultSpin;
-    }();
-    return v;
+    const char* e = getenv("MAMBA_SSD_SPIN_LIMIT");
+    if (!e || !*e) return kDefaultSpin;
+    const unsigned long x = strtoul(e, nullptr, 10);
+    return x ? (uint32_t)(x > 0xffffffffUL ? 0xffffffffUL : x) : kDefaultSpin;
+}
+
+// Test knobs of the fused form, read on every call: MAMBA_SSD_RELAY_ADMIT=0 makes every
+// partition of a relay-form launch decide that its chunk tiles pass the state themselves;
+// MAMBA_SSD_GRID_LIMIT=n caps the fused grid at n workgroups (partitions left without a
+// workgroup are then reported as SSD_ERR_SCHEDULE).
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    if (!e || !*e) return dflt;
+    return (int)strtol(e, nullptr, 10);
 }
 
 // MAMBA_SSD_CHAIN_GROUP: chains per claim group of the fused kernel (unset or 0: automatic).
@@ -137,7 +146,7 @@ Layout layout(const ssd_params_t* p) {
     l.bmm_w = l.cs_w + PS * nc;
     l.ticket_w = l.bmm_w + PS * nc;
     l.owner_w = l.ticket_w + (fused ? (size_t)ssd::kMaxXcc * ssd::kTicketStride : 0);
-    l.exit_w = l.owner_w + (fused ? ssd::kMaxXcc : 0);
+    l.exit_w = l.owner_w + (fused ? 3 * ssd::kMaxXcc : 0);  // owner, joined, relay_on words
     l.abort_w = l.exit_w + (fused ? 1 : 0);
     l.status_w = l.abort_w + 1;
     l.nsync = l.status_w + 1;
@@ -195,6 +204,8 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.bmm_done = sync + l.bmm_w;
     a.ticket = sync + l.ticket_w;
     a.owner = sync + l.owner_w;
+    a.joined = a.owner + ssd::kMaxXcc;
+    a.relay_on = a.owner + 2 * ssd::kMaxXcc;
     a.exit_count = sync + l.exit_w;
     a.abort_word = sync + l.abort_w;
     a.status = sync + l.status_w;
@@ -254,6 +265,7 @@ void set_partitions(const ssd_params_t* p, const Layout& l, const DevInfo& d, ss
     a.nparts = d.nparts;
     a.cu_count = d.cus;
     a.chain_group = chain_group_env();
+    a.relay_admit = env_int("MAMBA_SSD_RELAY_ADMIT", 1) != 0;
     int pb = 0, maxw = 0, maxu = 0;
     for (int x = 0; x <= d.nparts; ++x) {
         a.part_u0[x] = (int)(U * x / d.nparts);
@@ -268,12 +280,14 @@ void set_partitions(const ssd_params_t* p, const Layout& l, const DevInfo& d, ss
     }
     a.part_max_work = maxw;
     // The relay items (R per chain, R = relay waves per chain part) hold one workgroup each
-    // for the whole launch: use them only while they take at most half of a partition's
-    // workgroups (two per CU) and leave room for two chunks of the partition's chunk tiles.
+    // for the whole launch: use them only while they fit (relay_fits) in the workgroups a
+    // partition holds at once (its CUs times the fused kernel's real occupancy).  The kernel
+    // checks the same rule again against the workgroups that actually joined each partition,
+    // and falls back to the chunk tiles' own hop where it fails (see fused_loop).
     // R = 4 halves each relay wave's share of the state (faster hand-offs) and is used while
     // the chunk tiles still have 16 workgroups per chain; else R = 2 (more chunk tiles at once).
-    const int per_part = (d.cus / d.nparts > 0 ? d.cus / d.nparts : 1) * 2;
-    auto usable = [&](int R) { return 2 * R * maxu <= per_part && per_part - R * maxu >= 2 * maxu + 2; };
+    const int per_part = (d.cus / d.nparts > 0 ? d.cus / d.nparts : 1) * (a.fused_occ > 0 ? a.fused_occ : 1);
+    auto usable = [&](int R) { return ssd::relay_fits(R, maxu, per_part); };
     const int env = relay_env();
     a.relay = 0;
     if (relay_capable(p)) {
@@ -465,6 +479,7 @@ static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt
     if (p->impl == SSD_IMPL_FUSED) {
         DevInfo d;
         e = device_info(&d);
+        if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED_OCCUPANCY, p, a, st);
         if (e != hipSuccess) return hip_status(e);
         set_partitions(p, l, d, a);
         // initial state into the ring's slot 0; every sync word reset (chain counters to 1: the

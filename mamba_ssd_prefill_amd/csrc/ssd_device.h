@@ -815,8 +815,10 @@ enum : int { MODE_STATE = 0, MODE_SCAN = 1, MODE_FUSED = 2 };
 // MODE_FUSED  chunk_state, then the state_passing hop ([KF] item 6; fused schedule of
 //             [KF] "高效内核融合技术揭秘"): wait for S_c, write S_{c+1} = exp(acs[Q-1]) S_c
 //             + s_c to the next ring slot and release it, then chunk_scan with S_c.
+// relay_live (MODE_FUSED of a relay-form launch): the partition's relay items run.
 template <typename T, int P, int N, int MODE>
-__device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbase) {
+__device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbase,
+                           bool relay_live = false) {
     typedef Geo<T, P, N> G_;
     constexpr int W = G_::W, PW = G_::PW, WPH = G_::WPH, HPT = G_::HPT, MBP = G_::MBP;
     constexpr int NB = G_::NB, WB = G_::WB, KPL = G_::KPL, KI = G_::KI, LDW = G_::LDW, LDN = G_::LDN;
@@ -919,19 +921,22 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                     }
             }
             return;
-        } else if (a.relay) {
+        } else if (a.relay && relay_live) {
             // relay form: s_c to the chain's relay item, S_c back
             if (hvalid) relay_handoff<T, NB, MBP>(a, b, c, h, ph, WPH, acc, sc);
         } else {
-            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c
+            // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c (a relay-form launch whose
+            // partition runs no relay items: counter from 0, the state in the final-state slot 1)
             if (hvalid) {
                 uint32_t* fl = chain_counter(a, b, h, ph, WPH);
-                wait_flag(fl, a, (uint32_t)c + 1);
+                const uint32_t base = a.relay ? 0u : 1u;
+                wait_flag(fl, a, (uint32_t)c + base);
                 const int K = a.slots;
+                const int sin = a.relay ? (c > 0 ? 1 : 0) : c % K, sout = a.relay ? 1 : (c + 1) % K;
                 const __amdgpu_buffer_rsrc_t rin =
-                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
+                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, sin, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const __amdgpu_buffer_rsrc_t rout =
-                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
+                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, sout, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const float dec = carry ? __expf(acs_last) : 0.f;
                 const bool zero0 = c == 0 && !a.has_h0;  // S_0 = 0: nothing to read
 #pragma unroll
@@ -942,7 +947,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
                         sc[nb][pb] = zero0 ? vzero<f32x4>() : ring_load(rin, a.state_dtype, off);
                         ring_store(rout, a.state_dtype, off, dec * sc[nb][pb] + acc[nb][pb]);
                     }
-                publish_flag_wave(fl, (uint32_t)c + 2);
+                publish_flag_wave(fl, (uint32_t)c + 1 + base);
             }
         }
     } else {

@@ -3,6 +3,8 @@
 // the launchers for the supported (headdim, dstate) pairs.
 #pragma once
 
+#include <stdlib.h>
+
 #include "ssd_device.h"
 #include "ssd_tile16.h"
 
@@ -11,6 +13,7 @@ namespace ssd {
 // No-op hooks (see ClaimHook) for the unfused kernels.
 struct NoHook {
     __device__ inline void claim() const {}
+    __device__ inline bool relay_live() const { return false; }
 };
 
 // ---- unfused form: one kernel per step -------------------------------------------------
@@ -73,9 +76,11 @@ template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds_
 // one L2 (see the coherence notes in ssd_device.h).  A chunk tile waits only on work with
 // smaller tickets of its own queue (its cumsum and bmm tiles and the previous chunk's tile of
 // its chains, or its chain's relay item), claimed by workgroups that are running, so every
-// wait ends.  A relay item waits on chunk tiles with larger tickets: the relay form is used
-// only when a partition has far more workgroups than chains (set at launch), so those tiles
-// are claimed by other workgroups while the relay items run.
+// wait ends.  A relay item waits on chunk tiles with larger tickets, which other workgroups
+// must claim while it runs: so the relay items of a partition run only when the workgroups
+// that joined the partition leave room for them (relay_fits, decided once per partition by the
+// first relay ticket and read by every chunk tile); otherwise they leave at once and the chunk
+// tiles pass the state themselves, in place in the chain's final-state slot.
 struct FusedPart {
     int u0, nu, p0, np, pb;
     uint32_t n_cs, first_chunk, n_total;
@@ -142,9 +147,11 @@ struct ClaimHook {
     const SsdArgs& a;
     int part;
     uint32_t* s_next;  // LDS
+    bool live;         // the partition's relay items run
     __device__ inline void claim() const {
         if (threadIdx.x == 0) *s_next = atomicAdd(a.ticket + part * kTicketStride, 1u);
     }
+    __device__ inline bool relay_live() const { return live; }
 };
 
 // chunk(args, b, c, g, tig, cb, hook) runs one chunk tile after its cumsum and bmm tiles are done.
@@ -159,10 +166,12 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     if (threadIdx.x == 0) {
         const uint32_t prev = atomicCAS(a.owner + x, 0u, raw + 1);
         s_word = (prev == 0u || prev == raw + 1) ? 1u : 0u;
+        if (s_word) atomicAdd(a.joined + x, 1u);
     }
     __syncthreads();
     const bool mine = __builtin_amdgcn_readfirstlane(s_word) != 0u;
     uint32_t pending = 0xffffffffu;  // a ticket the previous chunk tile claimed ahead
+    int live = -1;                   // relay form: the partition's decision, once read
     while (mine) {
         lds_barrier();  // the previous tile is done with LDS and s_word (its stores may still fly)
         const SsdArgs& a = fresh_args(a0);
@@ -193,6 +202,21 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                 publish_flag_block(a.bmm_done + slot);
             }
         } else if (t < f.first_chunk) {
+            // The first relay ticket decides for the partition whether its relay items run: only
+            // when the workgroups that joined it (all launched workgroups that found room on the
+            // XCD by now; later ones may be waiting for a relay item to end) leave room for them.
+            if (threadIdx.x == 0) {
+                uint32_t d = __hip_atomic_load(a.relay_on + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (d == 0u) {
+                    const int j = (int)__hip_atomic_load(a.joined + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint32_t want = (a.relay_admit && relay_fits(a.relay, f.nu, j)) ? 1u : 2u;
+                    const uint32_t prev = atomicCAS(a.relay_on + x, 0u, want);
+                    d = prev == 0u ? want : prev;
+                }
+                s_word = d;
+            }
+            lds_barrier();
+            if (__builtin_amdgcn_readfirstlane(s_word) != 1u) continue;  // the chunk tiles hop
             // relay item k of chain u (its chunk tiles' 4 waves are 4 parts, (head hs, p-slice ph)):
             // parts k * PPI .. k * PPI + PPI - 1, R = a.relay waves each
             constexpr int PW = P < 32 ? P : 32, WPH = P / PW, NT = (N / 16) * (PW / 16);
@@ -210,10 +234,20 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
             }
         } else {
             const ChunkItem it = chunk_item(a, f, t);
+            if (a.relay && live < 0) {
+                // the partition's relay decision (made by its first relay ticket, which is smaller)
+                if (tid_here() < 64) {
+                    wait_flag(a.relay_on + x, a, 1u);
+                    if (tid_here() == 0)
+                        s_word = __hip_atomic_load(a.relay_on + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                lds_barrier();
+                live = __builtin_amdgcn_readfirstlane(s_word) == 1u ? 1 : 0;
+            }
             if (tid_here() < 64)  // wave 0: both flags with one poll
                 wait_pair(a.cs_done, (uint32_t)it.slot, (uint32_t)(a.bmm_done - a.cs_done + it.slot), a);
             lds_barrier();  // every wave starts after the flags were seen
-            const ClaimHook hook{a, x, &s_next};
+            const ClaimHook hook{a, x, &s_next, live == 1};
             chunk(a, it.b, it.c, it.g, it.tig, a.cb + it.slot * Q * Q, hook);
             lds_barrier();  // s_next holds the ticket claimed ahead
             pending = __builtin_amdgcn_readfirstlane(s_next);
@@ -237,7 +271,7 @@ template <typename T, int P, int N> __global__ __launch_bounds__(256) void k_fus
     fused_loop<Geo<T, P, N>::HPT, P, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig, const float* cbp,
                                                   const auto& hook) {
         hook.claim();
-        chunk_tile<T, P, N, MODE_FUSED>(ai, b, c, g, tig, smem, cbp);
+        chunk_tile<T, P, N, MODE_FUSED>(ai, b, c, g, tig, smem, cbp, hook.relay_live());
     });
 }
 
@@ -259,17 +293,27 @@ inline hipError_t launch(const void* fn, unsigned grid, void* arg0, hipStream_t 
 // Persistent fused launch: as many workgroups per partition as fit on its XCD at once (and no
 // more than its queue holds).  Workgroups are dealt to XCDs round robin, so partition x's
 // share arrives on one XCD; fused_loop does not rely on that for correctness.
-inline hipError_t launch_fused(const void* fn, SsdArgs& a, hipStream_t st) {
+inline hipError_t fused_occupancy(const void* fn, SsdArgs& a) {
     int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 256, 0);
-    if (e != hipSuccess) return e;
-    if (occ < 1) occ = 1;
-    const int per_xcd = (a.cu_count / a.nparts > 0 ? a.cu_count / a.nparts : 1) * occ;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 256, 0);
+    a.fused_occ = occ < 1 ? 1 : occ;
+    return e;
+}
+
+inline hipError_t launch_fused(const void* fn, SsdArgs& a, hipStream_t st) {
+    if (a.fused_occ < 1) {
+        const hipError_t e = fused_occupancy(fn, a);
+        if (e != hipSuccess) return e;
+    }
+    const int per_xcd = (a.cu_count / a.nparts > 0 ? a.cu_count / a.nparts : 1) * a.fused_occ;
     const int wgs = per_xcd < a.part_max_work ? per_xcd : a.part_max_work;
     // default: all of a partition's chains in one group (measured fastest: smaller groups keep
     // fewer state slots live but serialise on the chunk-to-chunk hand-off)
     if (a.chain_group <= 0) a.chain_group = 1 << 30;
-    return launch(fn, (unsigned)(a.nparts * (wgs > 0 ? wgs : 1)), &a, st);
+    unsigned grid = (unsigned)(a.nparts * (wgs > 0 ? wgs : 1));
+    const char* lim = getenv("MAMBA_SSD_GRID_LIMIT");  // test knob (see ssd_api.cpp)
+    if (lim && *lim && atoi(lim) > 0 && (unsigned)atoi(lim) < grid) grid = (unsigned)atoi(lim);
+    return launch(fn, grid, &a, st);
 }
 
 template <typename T, int P, int N> hipError_t launch_step_t(int step, SsdArgs& a, hipStream_t st) {
@@ -288,6 +332,8 @@ template <typename T, int P, int N> hipError_t launch_step_t(int step, SsdArgs& 
         return launch((const void*)&k_chunk<T, P, N, MODE_SCAN>, Bn * nc * Gn * tpg, &a, st);
     case STEP_FUSED:
         return launch_fused((const void*)&k_fused<T, P, N>, a, st);
+    case STEP_FUSED_OCCUPANCY:
+        return fused_occupancy((const void*)&k_fused<T, P, N>, a);
     default:
         return hipErrorInvalidValue;
     }
@@ -309,6 +355,8 @@ template <typename T, int P, int N, int Q> hipError_t launch_step16(int step, Ss
         return launch((const void*)&k_chunk16<T, P, N, Q, MODE_SCAN>, Bn * nc * Gn * tpg, &a, st);
     case STEP_FUSED:
         return launch_fused((const void*)&k_fused16<T, P, N, Q>, a, st);
+    case STEP_FUSED_OCCUPANCY:
+        return fused_occupancy((const void*)&k_fused16<T, P, N, Q>, a);
     default:
         return hipErrorInvalidValue;
     }

@@ -34,6 +34,8 @@ struct SsdArgs {
     uint32_t* bmm_done;  // fused: [pair slot][nc]
     uint32_t* ticket;    // fused: one work counter per partition, kTicketStride words apart
     uint32_t* owner;     // fused: [kMaxXcc] hardware XCC id (+1) that serves each partition
+    uint32_t* joined;    // fused: [kMaxXcc] workgroups that joined each partition
+    uint32_t* relay_on;  // fused relay form: [kMaxXcc] 0 undecided, 1 relay items run, 2 chunk tiles hop
     uint32_t* exit_count;
     uint32_t* abort_word;
     uint32_t* status;
@@ -50,8 +52,10 @@ struct SsdArgs {
     int part_pb[kMaxXcc + 1];
     int chain_group;    // chains whose chunk tiles are claimed together (0: set at launch)
     int relay;          // fused form: relay waves per chain part (2 or 4), 0 = no relay items
+    int relay_admit;    // fused relay form: 0 makes every partition decide "chunk tiles hop" (a test knob)
     int part_max_work;  // host only: the longest partition queue
     int cu_count;       // host only: compute units of the device
+    int fused_occ;      // host only: workgroups of the fused kernel one CU holds at once
 };
 
 constexpr int kTicketStride = 32;  // one 128-byte line per partition counter
@@ -76,7 +80,15 @@ enum : int {
     STEP_STATE_PASSING = 3,
     STEP_CHUNK_SCAN = 4,
     STEP_FUSED = 5,
+    STEP_FUSED_OCCUPANCY = 6,  // host only: sets SsdArgs::fused_occ for the fused kernel, launches nothing
 };
+
+// Relay admission, the same rule on the host (with the workgroups a partition can hold) and on
+// the device (with the workgroups that actually joined it): relay items, R per chain, may take at
+// most half of the partition's workgroups and must leave room for two chunks of its chunk tiles.
+__host__ __device__ inline bool relay_fits(int R, int nu, int workgroups) {
+    return 2 * R * nu <= workgroups && workgroups - R * nu >= 2 * nu + 2;
+}
 
 // Work split of a chunk tile for headdim P: PW columns of P per wave, WPH waves per
 // head, HPT = 4 / WPH heads per 256-thread workgroup.

@@ -480,18 +480,22 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             else if constexpr (CB_LDS)
                 dma_cb_bands<Q, CB_AUX>(sCB, cbp);
             hook.claim();
-            if (a.relay) {
+            if (a.relay && hook.relay_live()) {
                 // relay form: s_c to the chain's relay item, S_c back
                 if (hvalid) relay_handoff<T, NB, MBP>(a, b, c, h, ph, WPH, acc, scb);
             } else if (hvalid) {
-                // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c, in place in the chain's slot
+                // state_passing hop: S_{c+1} = exp(acs[Q-1]) S_c + s_c, in place in the chain's slot.
+                // In a relay-form launch whose partition runs no relay items, the chain's counter
+                // starts at 0 and the state lives in the final-state slot 1 (S_0 in slot 0).
                 uint32_t* fl = chain_counter(a, b, h, ph, WPH);
-                wait_flag(fl, a, (uint32_t)c + 1);
+                const uint32_t base = a.relay ? 0u : 1u;
+                wait_flag(fl, a, (uint32_t)c + base);
                 const int K = a.slots;
+                const int sin = a.relay ? (c > 0 ? 1 : 0) : c % K, sout = a.relay ? 1 : (c + 1) % K;
                 const __amdgpu_buffer_rsrc_t rin =
-                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, c % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
+                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, sin, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const __amdgpu_buffer_rsrc_t rout =
-                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, (c + 1) % K, h, ph, K, H, WPH, NB * MBP), NB * MBP);
+                    ring_rsrc(a.states, a.state_dtype, ring_chain(b, sout, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const float dec = carry ? __builtin_amdgcn_exp2f(a2_h[Q - 1]) : 0.f;
                 const bool zero0 = c == 0 && !a.has_h0;  // S_0 = 0: nothing to read
 #pragma unroll
@@ -503,7 +507,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                         ring_store(rout, a.state_dtype, off, dec * sv + acc[nb][pb]);
                         scb[nb][pb] = cvt4<T>(sv);
                     }
-                publish_flag_wave(fl, (uint32_t)c + 2);  // its wait covers the copies too
+                publish_flag_wave(fl, (uint32_t)c + 1 + base);  // its wait covers the copies too
             }
             wait_vm_all();
             __syncthreads();  // C (and CB) are in LDS

@@ -146,9 +146,9 @@ def test_workspace_layout_arithmetic(lib, impl, state, relay, monkeypatch):
     assert ssd.workspace_size(p) == lay.total_bytes
     if fused:
         # per-chain words [B][H][P/32] (three 128-byte lines each), cs_done and bmm_done
-        # [pair slots][nc], 8 partition tickets 32 words apart, 8 owner words, exit counter,
-        # abort, status
-        assert lay.sync_bytes == 4 * (Bt * H * 2 * 96 + 2 * pair_slots * nc + 8 * 32 + 8 + 3)
+        # [pair slots][nc], 8 partition tickets 32 words apart, 8 owner, 8 joined and 8 relay
+        # decision words, exit counter, abort, status
+        assert lay.sync_bytes == 4 * (Bt * H * 2 * 96 + 2 * pair_slots * nc + 8 * 32 + 24 + 3)
     else:
         assert lay.sync_bytes == 8  # abort and status words
 
