@@ -15,11 +15,20 @@ __global__ __launch_bounds__(256) void k_state_passing(SsdArgs a, int PN) {
     const int h = blockIdx.y, b = blockIdx.z;
     const int H = a.nheads, nc = a.nchunks, Q = a.chunk, K = a.slots;
     f32x4 S = load_state4(a.states, a.state_dtype, ((size_t)b * K * H + h) * PN + e);
+    if (a.seq_idx) {
+        // packed input: a sequence that starts inside chunk c passes no state on
+        for (int c = 0; c < nc; ++c) {
+            const bool start = a.seg[((size_t)b * nc + c) * Q + Q - 1] != 0;
+            const float dec = start ? 0.f : __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
+            const f32x4 sl = *(const f32x4*)(a.s + (((size_t)b * nc + c) * H + h) * PN + e);
+            S = dec * S + sl;
+            store_state4(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);
+        }
+        return;
+    }
 #pragma unroll 4
     for (int c = 0; c < nc; ++c) {
-        // packed input: a sequence that starts inside chunk c passes no state on
-        const bool start = a.seq_idx && a.seg[((size_t)b * nc + c) * Q + Q - 1] != 0;
-        const float dec = start ? 0.f : __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
+        const float dec = __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
         const f32x4 sl = *(const f32x4*)(a.s + (((size_t)b * nc + c) * H + h) * PN + e);
         S = dec * S + sl;
         store_state4(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);

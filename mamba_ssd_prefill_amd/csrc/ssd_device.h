@@ -212,10 +212,10 @@ __device__ inline void store_state4(void* base, int dtype, size_t off, f32x4 v) 
 // Waiters further back sleep longer between polls (s_sleep n is about 64 n cycles): a chain's
 // counter is polled by every waiting tile of the chain, and a tight loop from all of them
 // would saturate its L2 channel -- slowing the very stores it waits for.
-// Every 32nd poll of a wait: false once another wait gave up or this one has polled
-// spin_limit times (then it raises the abort and status words).
+// Every 32nd poll of a wait, and every poll past spin_limit: false once another wait gave up or
+// this one has polled more than spin_limit times (then it raises the abort and status words).
 __device__ inline bool spin_ok(uint32_t spins, const SsdArgs& a) {
-    if ((spins & 31u) != 0u) return true;
+    if ((spins & 31u) != 0u && spins <= a.spin_limit) return true;
     if (__hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
     if (spins > a.spin_limit) {
         __hip_atomic_store(a.abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -472,8 +472,8 @@ template <typename T> __device__ inline u32x4 pack_unit(const f32x4* v) {
 }
 
 // Relay wave w of chain (b, h, ph): the state passing of tiles [w * TPW, (w + 1) * TPW) of the
-// chain's NT accumulator tiles, over every chunk.
-template <typename T, int NT, int RWM>
+// chain's NT accumulator tiles, over every chunk.  VL: packed variable-length input.
+template <typename T, int NT, int RWM, bool VL>
 __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int w) {
     constexpr int TPU = tiles_per_unit<T>(), TPW = NT / relay_waves<T, NT, RWM>();
     static_assert(TPW % TPU == 0, "a relay wave holds whole operand units");
@@ -500,18 +500,19 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     }
     int agg_hi = 0;  // chunk states 0 .. agg_hi - 1 are known to be in their slots
     int wr_hi = 0;   // states 0 .. wr_hi - 1 are known to be free to write
-    // L(c): TPW loads of s_c, one of acs_c[Q-1] and one of seg_c[Q-1] (packed input: nonzero
-    // when a sequence starts inside chunk c, which then passes no state on; without packed
-    // input the descriptor covers 0 bytes and the load reads 0), into buf / d / sg
+    // L(c): TPW loads of s_c, one of acs_c[Q-1] and (packed input) one of seg_c[Q-1], nonzero
+    // when a sequence starts inside chunk c, which then passes no state on; into buf / d / sg
     auto issue_load = [&](int c, f32x4 (&buf)[TPW], float& d, uint32_t& sg) {
         const __amdgpu_buffer_rsrc_t r = agg_rsrc<NT>(a, b, h, ph, WPH, c % kAggSlots);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) buf[t] = bload_f32x4<AUX_L2>(r, ((t0 + t) * 64 + lane) * 16);
         d = bload_f32<AUX_L2>(make_rsrc(a.acs + (((size_t)b * nc + c) * H + h) * Q, (uint32_t)Q * 4),
                               (uint32_t)(Q - 1) * 4);
-        sg = __builtin_amdgcn_raw_buffer_load_b32(
-            make_rsrc(a.seg + ((size_t)b * nc + c) * Q, a.seq_idx ? (uint32_t)Q * 4 : 0u), (uint32_t)(Q - 1) * 4, 0,
-            AUX_L2);
+        if constexpr (VL)
+            sg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.seg + ((size_t)b * nc + c) * Q, (uint32_t)Q * 4),
+                                                      (uint32_t)(Q - 1) * 4, 0, AUX_L2);
+        else
+            sg = 0u;
     };
     // Step c: issue L(c + 1) if s_{c+1} is known to be ready, wait for L(c), publish S_{c-1},
     // else wait for s_{c+1} and issue L(c + 1) now; fold s_c in; store S_{c+1} (St(c + 1),
@@ -519,7 +520,7 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     // |St(c)| + |L(c + 1)| operations are pending (|St(c)| alone if L(c + 1) is not issued yet),
     // L(c) and everything before it (St(c - 1) too) are complete.  Any extra operation in
     // between (a poll, a flag) only makes the count wait for more.
-    constexpr int NST = TPW / TPU, NLD = TPW + 2;
+    constexpr int NST = TPW / TPU, NLD = TPW + (VL ? 2 : 1);
     auto step = [&](int c, f32x4 (&cur)[TPW], float dcur, uint32_t gcur, f32x4 (&nxt)[TPW], float& dnxt,
                     uint32_t& gnxt) -> bool {
         const bool has_next = c + 1 < nc;
@@ -815,8 +816,9 @@ enum : int { MODE_STATE = 0, MODE_SCAN = 1, MODE_FUSED = 2 };
 // MODE_FUSED  chunk_state, then the state_passing hop ([KF] item 6; fused schedule of
 //             [KF] "高效内核融合技术揭秘"): wait for S_c, write S_{c+1} = exp(acs[Q-1]) S_c
 //             + s_c to the next ring slot and release it, then chunk_scan with S_c.
-// relay_live (MODE_FUSED of a relay-form launch): the partition's relay items run.
-template <typename T, int P, int N, int MODE>
+// relay_live (MODE_FUSED of a relay-form launch): the partition's relay items run.  VL: packed
+// variable-length input (a.seq_idx set), a separate instantiation.
+template <typename T, int P, int N, int MODE, bool VL>
 __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbase,
                            bool relay_live = false) {
     typedef Geo<T, P, N> G_;
@@ -843,7 +845,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
     float* sAcs = sDt + HPT * QMAX;             // [HPT][QMAX]
     float* sW = sAcs + HPT * QMAX;              // [HPT][QMAX] chunk-state weights
     int* sSeg = (int*)(sW + HPT * QMAX);        // [QMAX] packed input: sequence starts up to token i
-    const bool varlen = a.seq_idx != nullptr;
+    constexpr bool varlen = VL;
 
     {
         // heads of the tile past the group read as zeros
@@ -856,7 +858,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
             sDt[hh * QMAX + i] = bload_f32<AUX>(rdt, (uint32_t)e * 4);
             sAcs[hh * QMAX + i] = bload_f32<AUX>(ra, (uint32_t)e * 4);
         }
-        if (varlen) {
+        if constexpr (varlen) {
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.seg + ((size_t)b * nc + c) * Q, (uint32_t)Q * 4);
             for (int e = tid; e < Q; e += 256) sSeg[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, e * 4, 0, AUX);
         }

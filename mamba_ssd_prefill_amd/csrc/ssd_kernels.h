@@ -33,8 +33,8 @@ template <typename T, int N> __global__ __launch_bounds__(256) void k_bmm(SsdArg
     bmm_tile<T, N>(a, b, c, g, cb_global(a, b, c, g));
 }
 
-// blockIdx.x -> (b, c, g, tile-in-group)
-template <typename T, int P, int N, int MODE> __global__ __launch_bounds__(256) void k_chunk(SsdArgs a) {
+// blockIdx.x -> (b, c, g, tile-in-group).  VL: packed variable-length input (a.seq_idx set).
+template <typename T, int P, int N, int MODE, bool VL> __global__ __launch_bounds__(256) void k_chunk(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo<T, P, N>::SMEM];
     int r = blockIdx.x;
     const int tig = r % a.tpg;
@@ -43,10 +43,11 @@ template <typename T, int P, int N, int MODE> __global__ __launch_bounds__(256) 
     r /= a.ngroups;
     const int c = r % a.nchunks;
     const int b = r / a.nchunks;
-    chunk_tile<T, P, N, MODE>(a, b, c, g, tig, smem, cb_global(a, b, c, g));
+    chunk_tile<T, P, N, MODE, VL>(a, b, c, g, tig, smem, cb_global(a, b, c, g));
 }
 
-template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds__(256) void k_chunk16(SsdArgs a) {
+template <typename T, int P, int N, int Q, int MODE, bool VL>
+__global__ __launch_bounds__(256) void k_chunk16(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
     int r = blockIdx.x;
     const int tig = r % a.tpg;
@@ -55,7 +56,7 @@ template <typename T, int P, int N, int Q, int MODE> __global__ __launch_bounds_
     r /= a.ngroups;
     const int c = r % a.nchunks;
     const int b = r / a.nchunks;
-    chunk_tile16<T, P, N, Q, MODE>(a, b, c, g, tig, smem, cb_global(a, b, c, g), NoHook{});
+    chunk_tile16<T, P, N, Q, MODE, VL>(a, b, c, g, tig, smem, cb_global(a, b, c, g), NoHook{});
 }
 
 // ---- fused form: a single launch ([KF] "高效内核融合技术揭秘") ------------------------------
@@ -155,7 +156,7 @@ struct ClaimHook {
 };
 
 // chunk(args, b, c, g, tig, cb, hook) runs one chunk tile after its cumsum and bmm tiles are done.
-template <int HPT, int P, typename T, int N, typename ChunkFn>
+template <int HPT, int P, typename T, int N, bool VL, typename ChunkFn>
 __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     __shared__ uint32_t s_word, s_next;
     const uint32_t raw = xcc_id();
@@ -228,9 +229,9 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
             const int b = pair / Gn, h = (pair % Gn) * hpg + tig * HPT + hs;
             if (tig * HPT + hs < hpg && rw < relay_waves_of<T, NT>(a)) {
                 if (R == 4)
-                    relay_chain<T, NT, 4>(a, b, h, ph, WPH, rw);
+                    relay_chain<T, NT, 4, VL>(a, b, h, ph, WPH, rw);
                 else
-                    relay_chain<T, NT, 2>(a, b, h, ph, WPH, rw);
+                    relay_chain<T, NT, 2, VL>(a, b, h, ph, WPH, rw);
             }
         } else {
             const ChunkItem it = chunk_item(a, f, t);
@@ -266,21 +267,21 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     }
 }
 
-template <typename T, int P, int N> __global__ __launch_bounds__(256) void k_fused(SsdArgs a) {
+template <typename T, int P, int N, bool VL> __global__ __launch_bounds__(256) void k_fused(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo<T, P, N>::SMEM];
-    fused_loop<Geo<T, P, N>::HPT, P, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig, const float* cbp,
-                                                  const auto& hook) {
+    fused_loop<Geo<T, P, N>::HPT, P, T, N, VL>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
+                                                      const float* cbp, const auto& hook) {
         hook.claim();
-        chunk_tile<T, P, N, MODE_FUSED>(ai, b, c, g, tig, smem, cbp, hook.relay_live());
+        chunk_tile<T, P, N, MODE_FUSED, VL>(ai, b, c, g, tig, smem, cbp, hook.relay_live());
     });
 }
 
-template <typename T, int P, int N, int Q>
+template <typename T, int P, int N, int Q, bool VL>
 __global__ __launch_bounds__(256, (Geo16<T, P, N, Q>::OCC)) void k_fused16(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
-    fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
-                                                       const float* cbp, const auto& hook) {
-        chunk_tile16<T, P, N, Q, MODE_FUSED>(ai, b, c, g, tig, smem, cbp, hook);
+    fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N, VL>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
+                                                           const float* cbp, const auto& hook) {
+        chunk_tile16<T, P, N, Q, MODE_FUSED, VL>(ai, b, c, g, tig, smem, cbp, hook);
     });
 }
 
@@ -316,7 +317,8 @@ inline hipError_t launch_fused(const void* fn, SsdArgs& a, hipStream_t st) {
     return launch(fn, grid, &a, st);
 }
 
-template <typename T, int P, int N> hipError_t launch_step_t(int step, SsdArgs& a, hipStream_t st) {
+// VL: the packed-input instantiation (the caller passes a.seq_idx != nullptr).
+template <typename T, int P, int N, bool VL> hipError_t launch_step_t(int step, SsdArgs& a, hipStream_t st) {
     typedef Geo<T, P, N> G_;
     const unsigned Bn = a.batch, nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
     switch (step) {
@@ -325,22 +327,22 @@ template <typename T, int P, int N> hipError_t launch_step_t(int step, SsdArgs& 
     case STEP_BMM:
         return launch((const void*)&k_bmm<T, N>, Bn * nc * Gn, &a, st);
     case STEP_CHUNK_STATE:
-        return launch((const void*)&k_chunk<T, P, N, MODE_STATE>, Bn * nc * Gn * tpg, &a, st);
+        return launch((const void*)&k_chunk<T, P, N, MODE_STATE, VL>, Bn * nc * Gn * tpg, &a, st);
     case STEP_STATE_PASSING:
         return launch_state_passing(a, P * N, st);
     case STEP_CHUNK_SCAN:
-        return launch((const void*)&k_chunk<T, P, N, MODE_SCAN>, Bn * nc * Gn * tpg, &a, st);
+        return launch((const void*)&k_chunk<T, P, N, MODE_SCAN, VL>, Bn * nc * Gn * tpg, &a, st);
     case STEP_FUSED:
-        return launch_fused((const void*)&k_fused<T, P, N>, a, st);
+        return launch_fused((const void*)&k_fused<T, P, N, VL>, a, st);
     case STEP_FUSED_OCCUPANCY:
-        return fused_occupancy((const void*)&k_fused<T, P, N>, a);
+        return fused_occupancy((const void*)&k_fused<T, P, N, VL>, a);
     default:
         return hipErrorInvalidValue;
     }
     (void)sizeof(G_);
 }
 
-template <typename T, int P, int N, int Q> hipError_t launch_step16(int step, SsdArgs& a, hipStream_t st) {
+template <typename T, int P, int N, int Q, bool VL> hipError_t launch_step16(int step, SsdArgs& a, hipStream_t st) {
     const unsigned Bn = a.batch, nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
     switch (step) {
     case STEP_CUMSUM:
@@ -348,18 +350,57 @@ template <typename T, int P, int N, int Q> hipError_t launch_step16(int step, Ss
     case STEP_BMM:
         return launch((const void*)&k_bmm<T, N>, Bn * nc * Gn, &a, st);
     case STEP_CHUNK_STATE:
-        return launch((const void*)&k_chunk16<T, P, N, Q, MODE_STATE>, Bn * nc * Gn * tpg, &a, st);
+        return launch((const void*)&k_chunk16<T, P, N, Q, MODE_STATE, VL>, Bn * nc * Gn * tpg, &a, st);
     case STEP_STATE_PASSING:
         return launch_state_passing(a, P * N, st);
     case STEP_CHUNK_SCAN:
-        return launch((const void*)&k_chunk16<T, P, N, Q, MODE_SCAN>, Bn * nc * Gn * tpg, &a, st);
+        return launch((const void*)&k_chunk16<T, P, N, Q, MODE_SCAN, VL>, Bn * nc * Gn * tpg, &a, st);
     case STEP_FUSED:
-        return launch_fused((const void*)&k_fused16<T, P, N, Q>, a, st);
+        return launch_fused((const void*)&k_fused16<T, P, N, Q, VL>, a, st);
     case STEP_FUSED_OCCUPANCY:
-        return fused_occupancy((const void*)&k_fused16<T, P, N, Q>, a);
+        return fused_occupancy((const void*)&k_fused16<T, P, N, Q, VL>, a);
     default:
         return hipErrorInvalidValue;
     }
+}
+
+// The (headdim, dstate) pairs each input type supports, dispatched to launch_step16 /
+// launch_step_t; hipErrorNotSupported otherwise.  One translation unit instantiates one
+// (type, chunk size, VL) combination.
+template <typename T, int Q, bool VL> hipError_t dispatch16(int step, int P, int N, SsdArgs& a, hipStream_t st) {
+    if (P == 16 && N == 32) return launch_step16<T, 16, 32, Q, VL>(step, a, st);
+    if (P == 16 && N == 64) return launch_step16<T, 16, 64, Q, VL>(step, a, st);
+    if (P == 16 && N == 128) return launch_step16<T, 16, 128, Q, VL>(step, a, st);
+    if (P == 32 && N == 32) return launch_step16<T, 32, 32, Q, VL>(step, a, st);
+    if (P == 32 && N == 64) return launch_step16<T, 32, 64, Q, VL>(step, a, st);
+    if (P == 32 && N == 128) return launch_step16<T, 32, 128, Q, VL>(step, a, st);
+    if (P == 64 && N == 32) return launch_step16<T, 64, 32, Q, VL>(step, a, st);
+    if (P == 64 && N == 64) return launch_step16<T, 64, 64, Q, VL>(step, a, st);
+    if (P == 64 && N == 128) return launch_step16<T, 64, 128, Q, VL>(step, a, st);
+    if (P == 128 && N == 32) return launch_step16<T, 128, 32, Q, VL>(step, a, st);
+    if (P == 128 && N == 64) return launch_step16<T, 128, 64, Q, VL>(step, a, st);
+    if (P == 128 && N == 128) return launch_step16<T, 128, 128, Q, VL>(step, a, st);
+    return hipErrorNotSupported;
+}
+
+template <bool VL> hipError_t dispatch32(int step, int P, int N, SsdArgs& a, hipStream_t st) {
+    if (P == 16 && N == 16) return launch_step_t<float, 16, 16, VL>(step, a, st);
+    if (P == 16 && N == 32) return launch_step_t<float, 16, 32, VL>(step, a, st);
+    if (P == 16 && N == 64) return launch_step_t<float, 16, 64, VL>(step, a, st);
+    if (P == 16 && N == 128) return launch_step_t<float, 16, 128, VL>(step, a, st);
+    if (P == 32 && N == 16) return launch_step_t<float, 32, 16, VL>(step, a, st);
+    if (P == 32 && N == 32) return launch_step_t<float, 32, 32, VL>(step, a, st);
+    if (P == 32 && N == 64) return launch_step_t<float, 32, 64, VL>(step, a, st);
+    if (P == 32 && N == 128) return launch_step_t<float, 32, 128, VL>(step, a, st);
+    if (P == 64 && N == 16) return launch_step_t<float, 64, 16, VL>(step, a, st);
+    if (P == 64 && N == 32) return launch_step_t<float, 64, 32, VL>(step, a, st);
+    if (P == 64 && N == 64) return launch_step_t<float, 64, 64, VL>(step, a, st);
+    if (P == 64 && N == 128) return launch_step_t<float, 64, 128, VL>(step, a, st);
+    if (P == 128 && N == 16) return launch_step_t<float, 128, 16, VL>(step, a, st);
+    if (P == 128 && N == 32) return launch_step_t<float, 128, 32, VL>(step, a, st);
+    if (P == 128 && N == 64) return launch_step_t<float, 128, 64, VL>(step, a, st);
+    if (P == 128 && N == 128) return launch_step_t<float, 128, 128, VL>(step, a, st);
+    return hipErrorNotSupported;
 }
 
 }  // namespace ssd

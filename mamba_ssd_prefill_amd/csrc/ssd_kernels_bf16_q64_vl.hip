@@ -1,0 +1,10 @@
+// ssd_kernels_bf16_q64_vl.hip -- kernel instantiations for bf16 inputs, chunk size 64, packed variable-length input.
+#include "ssd_kernels.h"
+
+namespace ssd {
+
+hipError_t launch_step_bf16_q64_vl1(int step, int P, int N, SsdArgs& a, hipStream_t st) {
+    return dispatch16<__bf16, 64, true>(step, P, N, a, st);
+}
+
+}  // namespace ssd

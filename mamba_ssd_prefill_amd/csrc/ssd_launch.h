@@ -100,13 +100,19 @@ inline int heads_per_tile(int P) { return 4 / waves_per_head(P); }
 hipError_t launch_step_f32(int step, int P, int N, SsdArgs& a, hipStream_t st);
 hipError_t launch_step_f16(int step, int P, int N, SsdArgs& a, hipStream_t st);
 hipError_t launch_step_bf16(int step, int P, int N, SsdArgs& a, hipStream_t st);
-// 16-bit inputs, one translation unit per (dtype, chunk size)
-hipError_t launch_step_f16_q64(int step, int P, int N, SsdArgs& a, hipStream_t st);
-hipError_t launch_step_f16_q128(int step, int P, int N, SsdArgs& a, hipStream_t st);
-hipError_t launch_step_f16_q256(int step, int P, int N, SsdArgs& a, hipStream_t st);
-hipError_t launch_step_bf16_q64(int step, int P, int N, SsdArgs& a, hipStream_t st);
-hipError_t launch_step_bf16_q128(int step, int P, int N, SsdArgs& a, hipStream_t st);
-hipError_t launch_step_bf16_q256(int step, int P, int N, SsdArgs& a, hipStream_t st);
+// One translation unit per (dtype, chunk size, packed input or not); vl1 = packed input
+hipError_t launch_step_f32_vl0(int step, int P, int N, SsdArgs& a, hipStream_t st);
+hipError_t launch_step_f32_vl1(int step, int P, int N, SsdArgs& a, hipStream_t st);
+#define SSD_DECLARE_16(dt)                                                                 \
+    hipError_t launch_step_##dt##_q64_vl0(int step, int P, int N, SsdArgs& a, hipStream_t st);  \
+    hipError_t launch_step_##dt##_q64_vl1(int step, int P, int N, SsdArgs& a, hipStream_t st);  \
+    hipError_t launch_step_##dt##_q128_vl0(int step, int P, int N, SsdArgs& a, hipStream_t st); \
+    hipError_t launch_step_##dt##_q128_vl1(int step, int P, int N, SsdArgs& a, hipStream_t st); \
+    hipError_t launch_step_##dt##_q256_vl0(int step, int P, int N, SsdArgs& a, hipStream_t st); \
+    hipError_t launch_step_##dt##_q256_vl1(int step, int P, int N, SsdArgs& a, hipStream_t st);
+SSD_DECLARE_16(f16)
+SSD_DECLARE_16(bf16)
+#undef SSD_DECLARE_16
 
 // Argument block of the single-token decode step (ssd_decode.hip); layouts in mamba_ssd.h.
 struct DecodeArgs {

@@ -328,7 +328,9 @@ template <typename T, typename G_, int AUX> struct LBuild {
 };
 
 // `hook` (fused form): claim() after the round-2 reads are issued; see ClaimHook.
-template <typename T, int P, int N, int Q, int MODE, typename Hook>
+// VL: packed variable-length input (a.seq_idx set): the decays are masked by sequence; a
+// separate instantiation, so the plain kernels carry none of the masking code.
+template <typename T, int P, int N, int Q, int MODE, bool VL, typename Hook>
 __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbp,
                              const Hook& hook) {
     typedef Geo16<T, P, N, Q> G_;
@@ -361,7 +363,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     float* sDt = sW + HPT * Q;
     float* sF = sW;
     int* sSeg = (int*)(sDt + HPT * Q);
-    const bool varlen = a.seq_idx != nullptr;
+    constexpr bool varlen = VL;
 
     // read now: a load issued just before its use in the y loop would make every row block wait
     // for all of the tile's outstanding memory operations
@@ -391,7 +393,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             sDt[e] = bload_f32<AUX>(rdt, (uint32_t)e * 4);
             sA2[e] = bload_f32<AUX>(ra, (uint32_t)e * 4) * LOG2E;
         }
-        if (varlen) {
+        if constexpr (varlen) {
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.seg + ((size_t)b * nc + c) * Q, (uint32_t)Q * 4);
             for (int e = tid; e < Q; e += 256) sSeg[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, e * 4, 0, AUX);
         }
