@@ -57,7 +57,8 @@ typedef enum {
     SSD_ERR_HIP = 6,                 /* a HIP runtime call or kernel launch failed */
     SSD_ERR_SYNC_TIMEOUT = 7,        /* fused kernel: a cross-workgroup wait hit its spin limit (results invalid) */
     SSD_ERR_INVALID_ARGUMENT = 8,    /* an enum field is out of range, or struct_size is too small */
-    SSD_ERR_SCHEDULE = 9             /* fused kernel: a work partition found no workgroup on its XCD (results invalid) */
+    SSD_ERR_SCHEDULE = 9,            /* fused kernel: a work partition found no workgroup on its XCD (results invalid) */
+    SSD_ERR_SCRATCH_TOO_SMALL = 10   /* ssd_prefill_noalloc: the problem's workspace exceeds the static scratch */
 } ssd_status_t;
 
 /* Problem description.  Set struct_size = sizeof(ssd_params_t). */
@@ -152,6 +153,28 @@ ssd_status_t ssd_prefill_varlen(const ssd_params_t* p,
                                 const void* initial_state,
                                 void* y, void* final_state,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssd_prefill without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a static device array inside the library, SSD_NOALLOC_SCRATCH_BYTES bytes on each
+ * GPU the library runs on, held until the process ends; its address on the current device is
+ * looked up once per device, on that device's first call.  The call allocates nothing and makes
+ * no allocating library call.  Arguments, layouts and errors are ssd_prefill's, plus
+ *   SSD_ERR_SCRATCH_TOO_SMALL  when ssd_prefill_workspace_size(p) > SSD_NOALLOC_SCRATCH_BYTES
+ *                              (nothing is enqueued);
+ *   SSD_ERR_HIP                when the scratch's address cannot be obtained.
+ * Every call on one GPU uses the same scratch, which keeps the previous call's contents (each
+ * call resets what must start at zero with a kernel): calls that overlap in time on one GPU
+ * (different streams, or different host threads) race and give wrong results; serialise them.
+ * The device status of such a call (SSD_ERR_SYNC_TIMEOUT / SSD_ERR_SCHEDULE) is not readable:
+ * ssd_check_device_status needs the workspace, so diagnose with ssd_prefill. */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)320 << 20)
+ssd_status_t ssd_prefill_noalloc(const ssd_params_t* p,
+                                 const void* x, const void* dt, const float* A,
+                                 const void* B, const void* C,
+                                 const float* D, const float* dt_bias,
+                                 const void* initial_state,
+                                 void* y, void* final_state, void* stream);
 
 /* Synchronises `stream`, then reads the device status word the last fused
  * ssd_prefill on `workspace` left: SSD_OK, SSD_ERR_SYNC_TIMEOUT when one of its waits

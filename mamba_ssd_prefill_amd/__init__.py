@@ -13,7 +13,8 @@ import os
 
 __all__ = ["ssd_prefill", "workspace_size", "workspace_layout", "Params", "SSDError", "library_path",
            "load_library", "step_chunk_cumsum", "step_bmm", "step_chunk_state", "step_state_passing",
-           "step_chunk_scan", "check_device_status", "make_params", "ssd_decode_step", "EXPORTED_SYMBOLS"]
+           "step_chunk_scan", "check_device_status", "make_params", "ssd_decode_step", "ssd_prefill_noalloc",
+           "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.environ.get("MAMBA_SSD_LIB", os.path.join(_HERE, "libmamba_ssd.so"))
@@ -23,12 +24,13 @@ DTYPE_CODES = {"f32": SSD_F32, "f16": SSD_F16, "bf16": SSD_BF16}
 IMPL_CODES = {"unfused": 0, "fused": 1}
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_INVALID_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
                 4: "SSD_ERR_MISALIGNED", 5: "SSD_ERR_WORKSPACE_TOO_SMALL", 6: "SSD_ERR_HIP",
-                7: "SSD_ERR_SYNC_TIMEOUT", 8: "SSD_ERR_INVALID_ARGUMENT", 9: "SSD_ERR_SCHEDULE"}
+                7: "SSD_ERR_SYNC_TIMEOUT", 8: "SSD_ERR_INVALID_ARGUMENT", 9: "SSD_ERR_SCHEDULE",
+                10: "SSD_ERR_SCRATCH_TOO_SMALL"}
 EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill", "ssd_prefill_timed",
                     "ssd_check_device_status",
                     "ssd_status_string", "ssd_workspace_layout", "ssd_step_chunk_cumsum", "ssd_step_bmm",
                     "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan", "ssd_decode_step",
-                    "ssd_prefill_varlen"]
+                    "ssd_prefill_varlen", "ssd_prefill_noalloc"]
 
 
 class SSDError(RuntimeError):
@@ -98,6 +100,8 @@ def load_library():
     lib.ssd_step_state_passing.argtypes = [P, vp, vp, vp, sz, vp]
     lib.ssd_step_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_prefill_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_prefill_noalloc.restype = ctypes.c_int
     for f in ("ssd_step_chunk_cumsum", "ssd_step_bmm", "ssd_step_chunk_state", "ssd_step_state_passing",
               "ssd_step_chunk_scan", "ssd_decode_step"):
         getattr(lib, f).restype = ctypes.c_int
@@ -232,6 +236,29 @@ def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_
                 ev.record()
         _check(load_library().ssd_prefill_timed(*args, ctypes.c_void_p(ev0.cuda_event), ctypes.c_void_p(ev1.cuda_event)),
                "ssd_prefill_timed")
+    return y, final_state
+
+
+def ssd_prefill_noalloc(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_size=128, state_dtype=None,
+                        impl="fused", dt_softplus=True, y=None, final_state=None):
+    """ssd_prefill through ssd_prefill_noalloc: the library's static scratch is the workspace, so
+    the call allocates no device memory when ``y`` and ``final_state`` are passed (this binding
+    allocates them with torch only when they are not).  Returns (y, final_state)."""
+    import torch
+    _check_tensors(x, dt, A, B, C, D, dt_bias, initial_state)
+    if state_dtype is None:
+        state_dtype = initial_state.dtype if initial_state is not None else torch.float32
+    sd = {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[state_dtype]
+    prm = _params_for(x, B, chunk_size, sd, dt_softplus, impl)
+    Bt, L, H, P = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None:
+        final_state = torch.empty((Bt, H, P, N), dtype=state_dtype, device=x.device)
+    _check(load_library().ssd_prefill_noalloc(ctypes.byref(prm), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                              _ptr(dt_bias), _ptr(initial_state), _ptr(y), _ptr(final_state),
+                                              _stream(x.device)), "ssd_prefill_noalloc")
     return y, final_state
 
 

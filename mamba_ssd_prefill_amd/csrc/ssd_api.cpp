@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "../../include/mamba_ssd.h"
+#include "ssd_api_internal.h"
 #include "ssd_launch.h"
 
 #define SSD_EXPORT extern "C" __attribute__((visibility("default")))
@@ -359,6 +360,8 @@ SSD_EXPORT const char* ssd_status_string(ssd_status_t s) {
     case SSD_ERR_SYNC_TIMEOUT: return "a cross-workgroup wait hit its spin limit; outputs are invalid";
     case SSD_ERR_INVALID_ARGUMENT: return "an enum field is out of range or struct_size is too small";
     case SSD_ERR_SCHEDULE: return "fused kernel: a work partition was not served by any workgroup; outputs are invalid";
+    case SSD_ERR_SCRATCH_TOO_SMALL:
+        return "ssd_prefill_noalloc: the problem needs more workspace than the library's static scratch holds";
     default: return "unknown status";
     }
 }
@@ -449,10 +452,10 @@ SSD_EXPORT ssd_status_t ssd_step_chunk_scan(const ssd_params_t* p, const void* x
 
 // ---- the whole prefill ----------------------------------------------------------------------
 
-static ssd_status_t prefill(const ssd_params_t* p, const void* x, const void* dt, const float* A, const void* B,
-                            const void* C, const float* D, const float* dt_bias, const void* initial_state, void* y,
-                            void* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                            hipEvent_t ev_begin, hipEvent_t ev_end, const int32_t* seq_idx) {
+ssd_status_t ssd::prefill_impl(const ssd_params_t* p, const void* x, const void* dt, const float* A, const void* B,
+                               const void* C, const float* D, const float* dt_bias, const void* initial_state,
+                               void* y, void* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                               hipEvent_t ev_begin, hipEvent_t ev_end, const int32_t* seq_idx) {
     Layout l;
     ssd_status_t s = check_ws(p, workspace, workspace_bytes, &l);
     if (s != SSD_OK) return s;
@@ -515,8 +518,8 @@ SSD_EXPORT ssd_status_t ssd_prefill(const ssd_params_t* p, const void* x, const 
                                    const void* B, const void* C, const float* D, const float* dt_bias,
                                    const void* initial_state, void* y, void* final_state, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-    return prefill(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes, stream,
-                   nullptr, nullptr, nullptr);
+    return ssd::prefill_impl(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes,
+                             stream, nullptr, nullptr, nullptr);
 }
 
 SSD_EXPORT ssd_status_t ssd_prefill_varlen(const ssd_params_t* p, const void* x, const void* dt, const float* A,
@@ -524,8 +527,8 @@ SSD_EXPORT ssd_status_t ssd_prefill_varlen(const ssd_params_t* p, const void* x,
                                           const int32_t* seq_idx, const void* initial_state, void* y,
                                           void* final_state, void* workspace, size_t workspace_bytes, void* stream) {
     if (!seq_idx) return SSD_ERR_NULL_POINTER;
-    return prefill(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes, stream,
-                   nullptr, nullptr, seq_idx);
+    return ssd::prefill_impl(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes,
+                             stream, nullptr, nullptr, seq_idx);
 }
 
 SSD_EXPORT ssd_status_t ssd_prefill_timed(const ssd_params_t* p, const void* x, const void* dt, const float* A,
@@ -534,8 +537,8 @@ SSD_EXPORT ssd_status_t ssd_prefill_timed(const ssd_params_t* p, const void* x, 
                                          size_t workspace_bytes, void* stream, void* kernel_begin,
                                          void* kernel_end) {
     if (!kernel_begin || !kernel_end) return SSD_ERR_NULL_POINTER;
-    return prefill(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes, stream,
-                   (hipEvent_t)kernel_begin, (hipEvent_t)kernel_end, nullptr);
+    return ssd::prefill_impl(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes,
+                             stream, (hipEvent_t)kernel_begin, (hipEvent_t)kernel_end, nullptr);
 }
 
 SSD_EXPORT ssd_status_t ssd_check_device_status(const ssd_params_t* p, const void* workspace, void* stream) {

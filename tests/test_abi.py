@@ -74,7 +74,7 @@ def test_abi_struct_sizes_match_header(tmp_path):
 
 
 def test_status_strings(lib):
-    for code in range(10):
+    for code in range(11):
         s = lib.ssd_status_string(code)
         assert s and len(s) > 3
     assert lib.ssd_status_string(1234) == b"unknown status"
@@ -315,3 +315,15 @@ def test_header_compiles_as_plain_c(tmp_path):
     r = subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
                         str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_noalloc_refuses_a_problem_larger_than_the_scratch(lib):
+    """ssd_prefill_noalloc checks the problem's workspace against its static scratch before any
+    HIP call (so this runs without a GPU): the 262K-token context needs more than it holds."""
+    prm = ssd.make_params(1, 262144, 80, 64, 128, 1, 128, "f16", "f16", True, "fused")
+    assert ssd.workspace_size(prm) > (320 << 20)
+    fake = ctypes.c_void_p(FAKE)
+    rc = lib.ssd_prefill_noalloc(ctypes.byref(prm), fake, fake, fake, fake, fake, None, None, None, fake, fake, None)
+    assert ssd.STATUS_NAMES[rc] == "SSD_ERR_SCRATCH_TOO_SMALL"
+    assert lib.ssd_prefill_noalloc(ctypes.byref(base(headdim=48)), fake, fake, fake, fake, fake, None, None, None,
+                                   fake, fake, None) == UNSUP
