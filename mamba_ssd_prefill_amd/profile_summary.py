@@ -2,6 +2,7 @@
 
     python -m mamba_ssd_prefill_amd.profile_summary trace    <rocprof dir> <out.md> "<command>"
     python -m mamba_ssd_prefill_amd.profile_summary counters <rocprof dir> <out.md> "<command>"
+    python -m mamba_ssd_prefill_amd.profile_summary metrics  <out.md> "<cmd1 ;; cmd2 ...>" <dir1> <dir2> ...
     python -m mamba_ssd_prefill_amd.profile_summary traffic <FETCH_SIZE dir> <WRITE_SIZE dir> \\
            <workload> <chunk> <out.json> "<fetch command>" "<write command>"
 
@@ -57,6 +58,9 @@ def _demangle_ssd(name):
             elif name[k] == "f":
                 args.append("float")
                 k += 1
+            elif name.startswith("Lb0E", k) or name.startswith("Lb1E", k):
+                args.append("packed" if name[k + 2] == "1" else "plain")
+                k += 4
             elif name.startswith("Li", k):
                 e = name.index("E", k)
                 args.append(name[k + 2:e])
@@ -174,11 +178,56 @@ def counters(d, out, command):
         f.write("\n".join(lines) + "\n")
 
 
+def metrics(out, command, dirs):
+    """Per-kernel averages of the counters of several --pmc runs (one directory each, same
+    program), with the derived figures the counters define on gfx950:
+      MFMA busy %   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs) * 100
+      occupancy %   = 4 * SQ_WAVE_CYCLES / (GRBM_GUI_ACTIVE * CUs * 32) * 100 (resident waves
+                      per CU against the 32 a CU holds; SQ_WAVE_CYCLES counts in units of 4)
+      L2 hit %      = TCC_HIT / (TCC_HIT + TCC_MISS) * 100
+      LDS conflict  = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (conflict cycles per LDS cycle)
+    GRBM_GUI_ACTIVE as collected here is the sum of the 8 XCDs' counters (each close to the
+    kernel's duration in cycles), so it is divided by 8 first (rocprofv3's own derived metrics
+    take the largest XCD's value instead)."""
+    acc = {}
+    for d in dirs:
+        for r in _rows(d, "*counter_collection.csv"):
+            k = short(r["Kernel_Name"])
+            if not k.startswith("ssd::"):
+                continue
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    cus, simds = 256, 1024
+    names = sorted({c for v in acc.values() for c in v})
+    lines = ["# Counters: %s" % os.path.basename(out).rsplit(".", 1)[0], "",
+             "Commands (from the repository root, on one MI355X), one --pmc pass each:", ""]
+    lines += ["    " + c for c in command.split(" ;; ")]
+    lines += ["", "Average per dispatch.", "",
+              "| kernel | " + " | ".join(names) + " | MFMA busy % | occupancy % | L2 hit % | LDS conflict / LDS cycle |",
+              "|---|" + "---:|" * (len(names) + 4)]
+    for k, v in sorted(acc.items()):
+        a = {c: sum(x) / len(x) for c, x in v.items()}
+        g = a.get("GRBM_GUI_ACTIVE")
+        g = g / 8.0 if g else g
+        mf = 100 * a["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds) if g and "SQ_VALU_MFMA_BUSY_CYCLES" in a else None
+        oc = 100 * 4 * a["SQ_WAVE_CYCLES"] / (g * cus * 32) if g and "SQ_WAVE_CYCLES" in a else None
+        hm = a.get("TCC_HIT_sum", 0.0) + a.get("TCC_MISS_sum", 0.0)
+        l2 = 100 * a["TCC_HIT_sum"] / hm if hm else None
+        lc = (a["SQ_LDS_BANK_CONFLICT"] / a["SQ_LDS_IDX_ACTIVE"]) if a.get("SQ_LDS_IDX_ACTIVE") else None
+        f = lambda x, fmt: "-" if x is None else fmt % x  # noqa: E731
+        cells = ["%.4g" % a[c] if c in a else "-" for c in names]
+        cells += [f(mf, "%.1f"), f(oc, "%.1f"), f(l2, "%.1f"), f(lc, "%.3f")]
+        lines.append("| %s | %s |" % (k, " | ".join(cells)))
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "trace":
         trace(argv[1], argv[2], argv[3])
     elif len(argv) >= 4 and argv[0] == "counters":
         counters(argv[1], argv[2], argv[3])
+    elif len(argv) >= 4 and argv[0] == "metrics":
+        metrics(argv[1], argv[2], argv[3:])
     elif len(argv) >= 8 and argv[0] == "traffic":
         traffic(*argv[1:8])
     else:
