@@ -76,6 +76,10 @@ bool relay_capable(const ssd_params_t* p) {
     return env >= 0 ? env != 0 : chain_count(p) <= kRelayMaxChains;
 }
 
+// Relay form with fp16 state storage (16-bit inputs): the chunk states handed to the relay
+// items are stored as fp16 too, like every other inter-chunk state of that storage mode.
+bool agg16(const ssd_params_t* p) { return p->state_dtype == SSD_F16 && p->in_dtype != SSD_F32; }
+
 struct Layout {
     ssd_workspace_layout_t w;
     // sync words: [flags | cs_done | bmm_done | tickets | owners | exit | abort | status]
@@ -136,7 +140,7 @@ Layout layout(const ssd_params_t* p) {
     w.cb_bytes = (fused ? PS : B * G) * nc * Q * Q * 4;
     // relay form: the chunk-state ring (fp32) and then the operand ring (input dtype)
     l.op_slots = (int)(nc + 1 < (size_t)ssd::kRelaySlots ? nc + 1 : (size_t)ssd::kRelaySlots);
-    l.agg_bytes = B * H * P * N * 4 * ssd::kAggSlots;
+    l.agg_bytes = B * H * P * N * (agg16(p) ? 2 : 4) * ssd::kAggSlots;
     w.s_bytes = fused ? (relay ? l.agg_bytes + B * H * P * N * elem_size(p->in_dtype) * l.op_slots : 0)
                       : B * nc * H * P * N * 4;
     w.states_bytes = B * K * H * P * N * elem_size(p->state_dtype);
@@ -221,6 +225,7 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.slots = l.w.state_slots;
     a.state_dtype = p->state_dtype;
     a.softplus = p->dt_softplus;
+    a.agg16 = agg16(p);
     a.spin_limit = spin_limit();
     return a;
 }

@@ -416,7 +416,8 @@ __device__ inline void ring_store(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t 
 // nanoseconds, so moving a wave's 16 KB of state costs microseconds.  The relay form gives every
 // chain (b, h, p-slice) a dedicated state-passing item whose relay waves each keep a share of S
 // (whole accumulator tiles) in fp32 registers and stream the chunk states through:
-//   chunk tile c:  s_c -> chunk-state ring slot c % kAggSlots (fp32), slot word = c + 1; wait
+//   chunk tile c:  s_c -> chunk-state ring slot c % kAggSlots (fp32; fp16 with fp16 state
+//                  storage), slot word = c + 1; wait
 //                  until every relay wave's counter >= c + 1, read S_c (operand type) from
 //                  operand slot c % op_slots, read word = c + 1
 //   relay wave:    for c = 0, 1, ...: S_{c+1} = exp(acs_c[Q-1]) S_c + s_c (its tiles) -> operand
@@ -446,11 +447,14 @@ __device__ inline size_t chain_index(const SsdArgs& a, int b, int h, int ph, int
     return ((size_t)b * a.nheads + h) * WPH + ph;
 }
 
-// The chunk-state ring slot of chain (b, h, ph): NT accumulator tiles of 64 lanes x 4 floats.
+// The chunk-state ring slot of chain (b, h, ph): NT accumulator tiles of 64 lanes x 4 floats,
+// lane after lane as in ring_chain.  a.agg16: 4 fp16 instead, tiles 2u and 2u + 1 of a lane
+// side by side in its 16-byte unit u (unit u of lane l at byte (u * 64 + l) * 16).
 template <int NT> __device__ inline __amdgpu_buffer_rsrc_t agg_rsrc(const SsdArgs& a, int b, int h, int ph, int WPH,
                                                                      int slot) {
     const size_t chain = chain_index(a, b, h, ph, WPH) * kAggSlots + slot;
-    return make_rsrc(a.s + chain * NT * 256, NT * 256 * 4);
+    const int es = a.agg16 ? 2 : 4;
+    return make_rsrc((const char*)a.s + chain * NT * 256 * es, NT * 256 * es);
 }
 
 // The operand ring slot of chain (b, h, ph): NT tiles of 64 lanes x 4 elements of T.
@@ -472,11 +476,17 @@ template <typename T> __device__ inline u32x4 pack_unit(const f32x4* v) {
 }
 
 // Relay wave w of chain (b, h, ph): the state passing of tiles [w * TPW, (w + 1) * TPW) of the
-// chain's NT accumulator tiles, over every chunk.  VL: packed variable-length input.
+// chain's NT accumulator tiles, over every chunk.  VL: packed variable-length input.  With
+// a.agg16 the chunk-state ring holds fp16: the wave's TPW tiles arrive in TPW / 2 16-byte loads,
+// and the other TPW / 2 loads go to an empty buffer range (no memory access, zeros), so the
+// number of memory operations per chunk -- which the waits below count -- stays the same.  (A
+// run-time choice rather than another instantiation: four relay instantiations in the fused
+// kernel pushed its registers into spills.)
 template <typename T, int NT, int RWM, bool VL>
 __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int w) {
     constexpr int TPU = tiles_per_unit<T>(), TPW = NT / relay_waves<T, NT, RWM>();
     static_assert(TPW % TPU == 0, "a relay wave holds whole operand units");
+    constexpr int NAL = TPW;  // chunk-state loads per chunk (one per tile)
     const uint32_t lane = (uint32_t)tid_here() & 63u;
     const int H = a.nheads, nc = a.nchunks, Q = a.chunk, K = a.slots, KO = a.op_slots, sdt = a.state_dtype;
     uint32_t* cnt = chain_counter(a, b, h, ph, WPH);
@@ -484,7 +494,11 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     const uint32_t* agg_words = cnt + kChainAggWords;
     const uint32_t* read_words = cnt + kChainReadWords;
     const uint32_t t0 = (uint32_t)(w * TPW);
-    f32x4 S[TPW], B0[TPW], B1[TPW];
+    f32x4 S[TPW];
+    typedef u32x4 aggv;  // one lane's 4 fp32 elements of a tile, or (fp16) of two tiles
+    aggv B0[NAL], B1[NAL];
+    const bool a16 = a.agg16;
+    static_assert(TPW % 2 == 0 || sizeof(T) == 4, "16-bit tiles come in pairs");
     float d0 = 0.f, d1 = 0.f;
     uint32_t g0 = 0u, g1 = 0u;
     {
@@ -502,10 +516,15 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     int wr_hi = 0;   // states 0 .. wr_hi - 1 are known to be free to write
     // L(c): TPW loads of s_c, one of acs_c[Q-1] and (packed input) one of seg_c[Q-1], nonzero
     // when a sequence starts inside chunk c, which then passes no state on; into buf / d / sg
-    auto issue_load = [&](int c, f32x4 (&buf)[TPW], float& d, uint32_t& sg) {
+    auto issue_load = [&](int c, aggv (&buf)[NAL], float& d, uint32_t& sg) {
         const __amdgpu_buffer_rsrc_t r = agg_rsrc<NT>(a, b, h, ph, WPH, c % kAggSlots);
+        const __amdgpu_buffer_rsrc_t rnone = make_rsrc(a.s, 0u);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) buf[t] = bload_f32x4<AUX_L2>(r, ((t0 + t) * 64 + lane) * 16);
+        for (int t = 0; t < NAL; ++t) {
+            const bool real = !a16 || 2 * t < TPW;
+            const uint32_t unit = a16 ? t0 / 2 + t : t0 + t;
+            buf[t] = __builtin_amdgcn_raw_buffer_load_b128(real ? r : rnone, (unit * 64 + lane) * 16, 0, AUX_L2);
+        }
         d = bload_f32<AUX_L2>(make_rsrc(a.acs + (((size_t)b * nc + c) * H + h) * Q, (uint32_t)Q * 4),
                               (uint32_t)(Q - 1) * 4);
         if constexpr (VL)
@@ -520,8 +539,8 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     // |St(c)| + |L(c + 1)| operations are pending (|St(c)| alone if L(c + 1) is not issued yet),
     // L(c) and everything before it (St(c - 1) too) are complete.  Any extra operation in
     // between (a poll, a flag) only makes the count wait for more.
-    constexpr int NST = TPW / TPU, NLD = TPW + (VL ? 2 : 1);
-    auto step = [&](int c, f32x4 (&cur)[TPW], float dcur, uint32_t gcur, f32x4 (&nxt)[TPW], float& dnxt,
+    constexpr int NST = TPW / TPU, NLD = NAL + (VL ? 2 : 1);
+    auto step = [&](int c, aggv (&cur)[NAL], float dcur, uint32_t gcur, aggv (&nxt)[NAL], float& dnxt,
                     uint32_t& gnxt) -> bool {
         const bool has_next = c + 1 < nc;
         const bool early = has_next && c + 1 < agg_hi;
@@ -555,8 +574,17 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
             asm volatile("" ::: "memory");
         }
         const float dec = gcur ? 0.f : __expf(dcur);
+        if (a16) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) S[t] = dec * S[t] + cur[t];
+            for (int u = 0; u < TPW / 2; ++u) {
+                const f16x8 hv = __builtin_bit_cast(f16x8, cur[u]);
+                S[2 * u] = dec * S[2 * u] + f32x4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
+                S[2 * u + 1] = dec * S[2 * u + 1] + f32x4{(float)hv[4], (float)hv[5], (float)hv[6], (float)hv[7]};
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) S[t] = dec * S[t] + __builtin_bit_cast(f32x4, cur[t]);
+        }
         const int m = c + 1;  // the state written now
         if (m >= wr_hi) {
             // slot m % KO last held S_{m-KO}: its reader must be done (bias KO: always true for m < KO)
@@ -605,12 +633,26 @@ __device__ inline bool relay_handoff(const SsdArgs& a, int b, int c, int h, int 
     // the slot's previous chunk state (chunk c - kAggSlots) has been folded in
     bool ok = c < kAggSlots || wait_words(cnt, RW, a, (uint32_t)(c - kAggSlots) + 2u);
     const __amdgpu_buffer_rsrc_t ra = agg_rsrc<NT>(a, b, h, ph, WPH, c % kAggSlots);
+    if (a.agg16) {
+        // tile t of this lane: 8 bytes at ((t / 2) * 64 + lane) * 16 + (t % 2) * 8
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int pb = 0; pb < MBP; ++pb)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[nb][pb]), ra,
-                                                   ((uint32_t)(nb * MBP + pb) * 64 + lane) * 16, 0, 0);
+            for (int pb = 0; pb < MBP; ++pb) {
+                const uint32_t t = (uint32_t)(nb * MBP + pb);
+                const f32x4 v = acc[nb][pb];
+                const f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), ra,
+                                                      ((t >> 1) * 64 + lane) * 16 + (t & 1) * 8, 0, 0);
+            }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int pb = 0; pb < MBP; ++pb)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[nb][pb]), ra,
+                                                       ((uint32_t)(nb * MBP + pb) * 64 + lane) * 16, 0, 0);
+    }
     publish_flag_wave(cnt + kChainAggWords + c % kAggSlots, (uint32_t)c + 1);
     ok = wait_words(cnt, RW, a, (uint32_t)c + 1) && ok;
     const int KO = a.op_slots;

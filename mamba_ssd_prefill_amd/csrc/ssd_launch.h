@@ -53,6 +53,7 @@ struct SsdArgs {
     int chain_group;    // chains whose chunk tiles are claimed together (0: set at launch)
     int relay;          // fused form: relay waves per chain part (2 or 4), 0 = no relay items
     int relay_admit;    // fused relay form: 0 makes every partition decide "chunk tiles hop" (a test knob)
+    int agg16;          // fused relay form: the chunk-state ring holds fp16 (fp16 state storage), else fp32
     int part_max_work;  // host only: the longest partition queue
     int cu_count;       // host only: compute units of the device
     int fused_occ;      // host only: workgroups of the fused kernel one CU holds at once

@@ -130,9 +130,9 @@ def test_workspace_layout_arithmetic(lib, impl, state, relay, monkeypatch):
     # fused: one CB run per (partition, (b, g) pair); at most B*G + 7 with up to 8 partitions
     pair_slots = Bt * G + 7
     assert lay.cb_bytes == (pair_slots if fused else Bt * G) * nc * Q * Q * 4
-    # fused relay form: a 10-slot fp32 chunk-state ring and a min(6, nc + 1)-slot operand ring
-    # (input dtype, bf16 here) per chain
-    relay_bytes = Bt * H * P * N * (4 * 10 + 2 * min(6, nc + 1))
+    # fused relay form: a 10-slot chunk-state ring (fp32; fp16 with fp16 state storage) and a
+    # min(6, nc + 1)-slot operand ring (input dtype, bf16 here) per chain
+    relay_bytes = Bt * H * P * N * ((2 if state == "f16" else 4) * 10 + 2 * min(6, nc + 1))
     assert lay.s_bytes == ((relay_bytes if relay_ws else 0) if fused else Bt * nc * H * P * N * 4)
     assert lay.states_bytes == Bt * K * H * P * N * es
     assert lay.seg_bytes == Bt * nc * Q * 4
