@@ -61,7 +61,9 @@ typedef enum {
     SSD_ERR_SCRATCH_TOO_SMALL = 10   /* ssd_prefill_noalloc: the problem's workspace exceeds the static scratch */
 } ssd_status_t;
 
-/* Problem description.  Set struct_size = sizeof(ssd_params_t). */
+/* Problem description.  Set struct_size = sizeof(ssd_params_t).  A caller built against ABI
+ * version 1 passes the smaller struct_size offsetof(ssd_params_t, relaxed) and gets the
+ * version-1 behaviour (relaxed = 0). */
 typedef struct {
     size_t struct_size;
     int batch;        /* B  >= 1 */
@@ -75,6 +77,11 @@ typedef struct {
     int state_dtype;  /* ssd_dtype_t */
     int dt_softplus;  /* 1: dt = softplus(dt_raw + dt_bias); 0: dt = dt_raw + dt_bias */
     int impl;         /* ssd_impl_t */
+    /* ABI version 2: */
+    int relaxed;      /* 0: exact intermediates; 1: relaxed ("Mamba-2炸裂升级！…", section
+                         "精度与性能的平衡艺术"): with 16-bit inputs CB = C B^T of each chunk is
+                         stored in in_dtype instead of fp32 (no effect for fp32 inputs) */
+    int reserved;     /* must be 0 */
 } ssd_params_t;
 
 /*

@@ -48,7 +48,8 @@ class Params(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_size_t), ("batch", ctypes.c_int), ("seqlen", ctypes.c_int),
                 ("nheads", ctypes.c_int), ("headdim", ctypes.c_int), ("dstate", ctypes.c_int),
                 ("ngroups", ctypes.c_int), ("chunk_size", ctypes.c_int), ("in_dtype", ctypes.c_int),
-                ("state_dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int), ("impl", ctypes.c_int)]
+                ("state_dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int), ("impl", ctypes.c_int),
+                ("relaxed", ctypes.c_int), ("reserved", ctypes.c_int)]
 
 
 class Layout(ctypes.Structure):
@@ -115,17 +116,17 @@ def _dtype_code(t):
 
 
 def make_params(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size=128, in_dtype="bf16",
-                state_dtype="f32", dt_softplus=True, impl="fused"):
+                state_dtype="f32", dt_softplus=True, impl="fused", relaxed=False):
     code = lambda d: d if isinstance(d, int) else DTYPE_CODES[d]  # noqa: E731
     return Params(ctypes.sizeof(Params), int(batch), int(seqlen), int(nheads), int(headdim), int(dstate),
                   int(ngroups), int(chunk_size), code(in_dtype), code(state_dtype), 1 if dt_softplus else 0,
-                  IMPL_CODES[impl] if isinstance(impl, str) else int(impl))
+                  IMPL_CODES[impl] if isinstance(impl, str) else int(impl), 1 if relaxed else 0, 0)
 
 
-def _params_for(x, B, chunk_size, state_dtype_code, dt_softplus, impl):
+def _params_for(x, B, chunk_size, state_dtype_code, dt_softplus, impl, relaxed=False):
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    return make_params(Bt, L, H, P, N, G, chunk_size, _dtype_code(x), state_dtype_code, dt_softplus, impl)
+    return make_params(Bt, L, H, P, N, G, chunk_size, _dtype_code(x), state_dtype_code, dt_softplus, impl, relaxed)
 
 
 def workspace_size(params):
@@ -192,7 +193,7 @@ def _check_tensors(x, dt, A, B, C, D, dt_bias, h0):
 
 def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_size=128, state_dtype=None,
                 impl="fused", dt_softplus=True, workspace=None, y=None, final_state=None, kernel_events=None,
-                seq_idx=None):
+                seq_idx=None, relaxed=False):
     """Run one SSD prefill on the GPU; returns (y[B,L,H,P], final_state[B,H,P,N]).
 
     ``state_dtype`` defaults to initial_state's dtype, else float32.  ``workspace``
@@ -200,7 +201,7 @@ def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_
     ``kernel_events`` = (begin, end) torch.cuda.Event(enable_timing=True) pair, recorded
     by the library around the SSD compute kernel(s) (ssd_prefill_timed).  ``seq_idx``
     (int32 [B, L]) packs several sequences per batch row: the recurrence restarts wherever
-    it changes (ssd_prefill_varlen)."""
+    it changes (ssd_prefill_varlen).  ``relaxed``: CB stored in the 16-bit input type."""
     import torch
     _check_tensors(x, dt, A, B, C, D, dt_bias, initial_state)
     if seq_idx is not None:
@@ -214,7 +215,7 @@ def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_
     sd = {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[state_dtype]
     if initial_state is not None and initial_state.dtype != state_dtype:
         raise ValueError("initial_state dtype %s != state_dtype %s" % (initial_state.dtype, state_dtype))
-    prm = _params_for(x, B, chunk_size, sd, dt_softplus, impl)
+    prm = _params_for(x, B, chunk_size, sd, dt_softplus, impl, relaxed)
     Bt, L, H, P = x.shape
     N = B.shape[3]
     if y is None:

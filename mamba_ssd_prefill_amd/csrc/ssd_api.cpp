@@ -2,6 +2,7 @@
 // only, before any HIP call), workspace carve-up and kernel dispatch.
 #include <hip/hip_runtime.h>
 
+#include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -22,6 +23,10 @@ constexpr int64_t kRelayMaxChains = 128;
 constexpr uint32_t kDefaultSpin = 1u << 22;
 
 size_t elem_size(int dt) { return dt == SSD_F32 ? 4 : 2; }
+
+// ssd_params_t of ABI version 1 ended before `relaxed`; such callers get relaxed = 0.
+constexpr size_t kParamsV1Size = offsetof(ssd_params_t, relaxed);
+int relaxed(const ssd_params_t* p) { return p->struct_size >= sizeof(ssd_params_t) ? p->relaxed : 0; }
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -76,6 +81,9 @@ bool relay_capable(const ssd_params_t* p) {
     return env >= 0 ? env != 0 : chain_count(p) <= kRelayMaxChains;
 }
 
+// Relaxed intermediates with 16-bit inputs: CB (C B^T of each chunk) stored in the input type.
+bool cb16(const ssd_params_t* p) { return relaxed(p) && p->in_dtype != SSD_F32; }
+
 // Relay form with fp16 state storage (16-bit inputs): the chunk states handed to the relay
 // items are stored as fp16 too, like every other inter-chunk state of that storage mode.
 bool agg16(const ssd_params_t* p) { return p->state_dtype == SSD_F16 && p->in_dtype != SSD_F32; }
@@ -95,7 +103,9 @@ size_t pair_slots_max(const ssd_params_t* p) { return (size_t)p->batch * p->ngro
 
 ssd_status_t validate(const ssd_params_t* p) {
     if (!p) return SSD_ERR_NULL_POINTER;
-    if (p->struct_size < sizeof(ssd_params_t)) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->struct_size < kParamsV1Size) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->struct_size >= sizeof(ssd_params_t) && ((p->relaxed != 0 && p->relaxed != 1) || p->reserved != 0))
+        return SSD_ERR_INVALID_ARGUMENT;
     if (p->in_dtype < SSD_F32 || p->in_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
     if (p->state_dtype < SSD_F32 || p->state_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
     if (p->impl != SSD_IMPL_UNFUSED && p->impl != SSD_IMPL_FUSED) return SSD_ERR_INVALID_ARGUMENT;
@@ -137,7 +147,7 @@ Layout layout(const ssd_params_t* p) {
     w.dt_bytes = B * nc * H * Q * 4;
     w.acs_bytes = w.dt_bytes;
     const size_t PS = fused ? pair_slots_max(p) : 0;
-    w.cb_bytes = (fused ? PS : B * G) * nc * Q * Q * 4;
+    w.cb_bytes = (fused ? PS : B * G) * nc * Q * Q * (cb16(p) ? 2 : 4);
     // relay form: the chunk-state ring (fp32) and then the operand ring (input dtype)
     l.op_slots = (int)(nc + 1 < (size_t)ssd::kRelaySlots ? nc + 1 : (size_t)ssd::kRelaySlots);
     l.agg_bytes = B * H * P * N * (agg16(p) ? 2 : 4) * ssd::kAggSlots;
@@ -226,6 +236,7 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.state_dtype = p->state_dtype;
     a.softplus = p->dt_softplus;
     a.agg16 = agg16(p);
+    a.cb16 = cb16(p);
     a.spin_limit = spin_limit();
     return a;
 }
@@ -374,7 +385,7 @@ SSD_EXPORT const char* ssd_status_string(ssd_status_t s) {
 // ---- the five unfused steps ---------------------------------------------------------------
 
 static ssd_status_t unfused_guard(const ssd_params_t* p) {
-    if (p && p->struct_size >= sizeof(ssd_params_t) && p->impl != SSD_IMPL_UNFUSED) return SSD_ERR_INVALID_ARGUMENT;
+    if (p && p->struct_size >= kParamsV1Size && p->impl != SSD_IMPL_UNFUSED) return SSD_ERR_INVALID_ARGUMENT;
     return SSD_OK;
 }
 
@@ -565,7 +576,7 @@ namespace {
 
 ssd_status_t validate_decode(const ssd_params_t* p) {
     if (!p) return SSD_ERR_NULL_POINTER;
-    if (p->struct_size < sizeof(ssd_params_t)) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->struct_size < kParamsV1Size) return SSD_ERR_INVALID_ARGUMENT;
     if (p->in_dtype < SSD_F32 || p->in_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
     if (p->state_dtype < SSD_F32 || p->state_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
     if (p->dt_softplus != 0 && p->dt_softplus != 1) return SSD_ERR_INVALID_ARGUMENT;

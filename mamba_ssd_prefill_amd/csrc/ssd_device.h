@@ -754,11 +754,17 @@ template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c
     }
 }
 
+// The Q x Q block of CB number idx in a.cb (fp32, or with a.cb16 the 16-bit input type).
+__device__ inline float* cb_at(const SsdArgs& a, size_t idx) {
+    return (float*)((char*)a.cb + idx * (size_t)a.chunk * a.chunk * (a.cb16 ? 2 : 4));
+}
+
 // ---- step 2: bmm ([KF] item 7) ---------------------------------------------------------
 // CB[i][j] = sum_n C_i[n] B_j[n] for one (b, c, g) into cbase[Q][Q], computed as CB^T blocks
 // (rows j, columns i) so each lane stores 4 consecutive j of one row i.  Only blocks with
 // i-block >= j-block are formed: the scan step reads j <= i only.  Fragments come straight
-// from global memory (rows are n-contiguous).
+// from global memory (rows are n-contiguous).  With a.cb16 (the relaxed intermediates of
+// "Mamba-2炸裂升级！…", section "精度与性能的平衡艺术") CB is rounded to the 16-bit input type.
 template <typename T, int N> __device__ void bmm_tile(const SsdArgs& a, int b, int c, int g, float* cbase) {
     constexpr int KPL = TT<T>::KPL, KI = 4 * KPL;
     const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -784,7 +790,14 @@ template <typename T, int N> __device__ void bmm_tile(const SsdArgs& a, int b, i
                                        : vzero<frag>();
                 acc = TT<T>::mma(af[ks], bf, acc);
             }
-            *(f32x4*)(cbase + (size_t)(ib * 16 + r16) * Q + jb * 16 + 4 * q) = acc;
+            const size_t o = (size_t)(ib * 16 + r16) * Q + jb * 16 + 4 * q;
+            if constexpr (sizeof(T) == 2) {
+                if (a.cb16) {
+                    *(typename TT<T>::v4*)((T*)cbase + o) = cvt4<T>(acc);
+                    continue;
+                }
+            }
+            *(f32x4*)(cbase + o) = acc;
         }
     }
 }

@@ -23,7 +23,7 @@ template <typename T> __global__ __launch_bounds__(256) void k_chunk_cumsum(SsdA
 }
 
 __device__ inline float* cb_global(const SsdArgs& a, int b, int c, int g) {
-    return a.cb + (((size_t)b * a.nchunks + c) * a.ngroups + g) * (size_t)a.chunk * a.chunk;
+    return cb_at(a, ((size_t)b * a.nchunks + c) * a.ngroups + g);
 }
 
 template <typename T, int N> __global__ __launch_bounds__(256) void k_bmm(SsdArgs a) {
@@ -199,7 +199,7 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                 cumsum_tile<T>(a, b, c, g * hpg + lo, g * hpg + hi);
                 publish_flag_block(a.cs_done + slot);
             } else {
-                bmm_tile<T, N>(a, b, c, g, a.cb + slot * Q * Q);
+                bmm_tile<T, N>(a, b, c, g, cb_at(a, slot));
                 publish_flag_block(a.bmm_done + slot);
             }
         } else if (t < f.first_chunk) {
@@ -249,7 +249,7 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                 wait_pair(a.cs_done, (uint32_t)it.slot, (uint32_t)(a.bmm_done - a.cs_done + it.slot), a);
             lds_barrier();  // every wave starts after the flags were seen
             const ClaimHook hook{a, x, &s_next, live == 1};
-            chunk(a, it.b, it.c, it.g, it.tig, a.cb + it.slot * Q * Q, hook);
+            chunk(a, it.b, it.c, it.g, it.tig, cb_at(a, it.slot), hook);
             lds_barrier();  // s_next holds the ticket claimed ahead
             pending = __builtin_amdgcn_readfirstlane(s_next);
         }

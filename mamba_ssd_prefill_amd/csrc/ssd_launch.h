@@ -25,7 +25,8 @@ struct SsdArgs {
     void* y;
     float* dtf;          // [B][nc][H][Q]
     float* acs;          // [B][nc][H][Q]
-    float* cb;           // unfused: [B][nc][G][Q][Q]; fused: [pair slot][nc][Q][Q]
+    float* cb;           // unfused: [B][nc][G][Q][Q]; fused: [pair slot][nc][Q][Q]; fp32, or the 16-bit
+                         // input type when cb16 (see cb_at)
     float* s;            // unfused: [B][nc][H][P][N]; fused relay form: the chunk-state ring
     void* states;        // unfused: [B][K][H][P][N]; fused: K ring slots per chain
     void* opnd;          // fused relay form: S_c in the operand type, op_slots slots per chain
@@ -54,6 +55,7 @@ struct SsdArgs {
     int relay;          // fused form: relay waves per chain part (2 or 4), 0 = no relay items
     int relay_admit;    // fused relay form: 0 makes every partition decide "chunk tiles hop" (a test knob)
     int agg16;          // fused relay form: the chunk-state ring holds fp16 (fp16 state storage), else fp32
+    int cb16;           // relaxed intermediates: CB stored in the 16-bit input type instead of fp32
     int part_max_work;  // host only: the longest partition queue
     int cu_count;       // host only: compute units of the device
     int fused_occ;      // host only: workgroups of the fused kernel one CU holds at once

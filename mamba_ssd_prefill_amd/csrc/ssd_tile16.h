@@ -149,35 +149,50 @@ template <typename T> __device__ inline typename TT<T>::frag pack8(f32x4 lo, f32
 
 // Copy the CB rows/columns the diagonal block reads (bands of the lower triangle, see
 // Geo16) from HBM into LDS.  AUX = AUX_L2 when CB was written by another workgroup of the
-// same launch (on the same XCD).
-template <int Q, int AUX> __device__ inline void dma_cb_bands(float* lds, const float* cb) {
+// same launch (on the same XCD).  ES: CB element size (4, or 2 for the relaxed 16-bit CB);
+// a 16-byte piece holds 16 / ES elements, so a band row of 32 (band + 1) columns is
+// 32 (band + 1) ES / 16 pieces plus one of padding.
+template <int ES> __host__ __device__ constexpr int cb_pitch(int band) { return 32 * (band + 1) * ES / 16 + 1; }
+template <int Q, int ES> __device__ constexpr int cb_band_base(int band) {
+    int t = 0;
+    for (int r = 0; r < band; ++r) t += ((32 * cb_pitch<ES>(r) + 63) / 64) * 64;
+    return t;
+}
+template <int Q, int AUX, int ES> __device__ inline void dma_cb_bands(float* lds, const float* cb) {
     const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(cb, (uint32_t)(Q * Q * 4));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(cb, (uint32_t)(Q * Q * ES));
+    constexpr int EPP = 16 / ES;  // elements per piece
     int base = 0;  // pieces
 #pragma unroll
     for (int band = 0; band < Q / 32; ++band) {
-        const int pitch = 8 * band + 9;  // pieces per row (8(band+1) data + 1 pad)
+        const int pitch = cb_pitch<ES>(band);
         const int used = 32 * pitch;
         const int ninst = (used + 63) / 64;
         for (int k = wave; k < ninst; k += 4) {
             const int f = k * 64 + lane;  // piece index inside the band
             const int row = f / pitch, pc = f - row * pitch;
-            const bool ok = f < used && pc < 8 * (band + 1);
-            const uint32_t voff = ok ? (uint32_t)(((32 * band + row) * Q + 4 * pc) * 4) : 0x40000000u;  // past num_records: reads as zeros
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SSD_LDS(void, lds + (base + k * 64) * 4), 16, voff, 0, 0, AUX);
+            const bool ok = f < used && pc < pitch - 1;
+            const uint32_t voff = ok ? (uint32_t)(((32 * band + row) * Q + EPP * pc) * ES) : 0x40000000u;  // past num_records: reads as zeros
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SSD_LDS(void, (char*)lds + (base + k * 64) * 16), 16, voff, 0, 0, AUX);
         }
         base += ((used + 63) / 64) * 64;
     }
 }
 
-// Offset (in floats) of CB[i][j] in the banded LDS copy.
-template <int Q> __device__ inline int cb_off(int i, int j) {
+// Offset (in elements of size ES) of CB[i][j] in the banded LDS copy.
+template <int Q, int ES> __device__ inline int cb_off(int i, int j) {
     const int band = i >> 5;
     int base = 0;
 #pragma unroll
     for (int r = 0; r < Q / 32; ++r)
-        if (r < band) base += ((32 * (8 * r + 9) + 63) / 64) * 64;
-    return (base + (i & 31) * (8 * band + 9)) * 4 + j;
+        if (r < band) base += ((32 * cb_pitch<ES>(r) + 63) / 64) * 64;
+    return (base + (i & 31) * cb_pitch<ES>(band)) * (16 / ES) + j;
+}
+
+// 8 consecutive CB values at element offset `off` of a 16-bit CB: one 16-byte read, widened.
+template <typename T> __device__ inline void cb16_widen(typename TT<T>::frag v, f32x4& lo, f32x4& hi) {
+    lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
 }
 
 // Piece offset (16-byte units) of L_h[i][8 jp .. 8 jp + 7] inside one head's bands.
@@ -242,8 +257,13 @@ template <typename T, typename G_, int AUX> struct LBuild {
         jp = 4 * b + (kl < 32 ? 0 : 2) + (kl & 1);
     }
 
-    __device__ inline void load(const float* cbp, int tid) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(cbp, (uint32_t)(Q * Q * 4));
+    // cb16: CB holds the 16-bit input type; the 8 values of an item then arrive in the first
+    // load and the second goes to an empty buffer range (zeros, no memory access), so both
+    // storage types issue the same loads into the same registers.
+    __device__ inline void load(const float* cbp, int tid, bool cb16) {
+        const int es = cb16 ? 2 : 4;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(cbp, (uint32_t)(Q * Q * es));
+        const __amdgpu_buffer_rsrc_t r2 = cb16 ? make_rsrc(cbp, 0u) : r;
 #pragma unroll
         for (int it = 0; it < FI; ++it) {
             const int k = tid + it * 256;
@@ -251,23 +271,31 @@ template <typename T, typename G_, int AUX> struct LBuild {
             if (k < NF) f_item(k, i, jp);
             fi[it] = i;
             fj[it] = jp;
-            const uint32_t off = k < NF ? (uint32_t)(i * Q + 8 * jp) * 4 : 0x40000000u;  // past the end: zeros
+            const uint32_t off = k < NF ? (uint32_t)(i * Q + 8 * jp) * es : 0x40000000u;  // past the end: zeros
             cf[it][0] = bload_f32x4<AUX>(r, off);
-            cf[it][1] = bload_f32x4<AUX>(r, off + 16);
+            cf[it][1] = bload_f32x4<AUX>(r2, off + 16);
         }
 #pragma unroll
         for (int it = 0; it < DI; ++it) {
             const int k = tid + it * 256;
             int i = 0, jp = 0;
             if (k < ND) d_item(k, i, jp);
-            const uint32_t off = k < ND ? (uint32_t)(i * Q + 8 * jp) * 4 : 0x40000000u;
+            const uint32_t off = k < ND ? (uint32_t)(i * Q + 8 * jp) * es : 0x40000000u;
             cd[it][0] = bload_f32x4<AUX>(r, off);
-            cd[it][1] = bload_f32x4<AUX>(r, off + 16);
+            cd[it][1] = bload_f32x4<AUX>(r2, off + 16);
         }
     }
 
     __device__ inline void store(T* sL, const float* sA2, const float* sF, const float* sDt, const int* sSeg,
-                                 bool varlen, int nvh, int tid) {
+                                 bool varlen, bool cb16, int nvh, int tid) {
+        if (cb16) {
+            // widen in place (here, not in load(), so the loads stay in flight until now): the 8
+            // 16-bit values of each item into its two fp32 vectors
+#pragma unroll
+            for (int it = 0; it < FI; ++it) cb16_widen<T>(__builtin_bit_cast(frag, cf[it][0]), cf[it][0], cf[it][1]);
+#pragma unroll
+            for (int it = 0; it < DI; ++it) cb16_widen<T>(__builtin_bit_cast(frag, cd[it][0]), cd[it][0], cd[it][1]);
+        }
 #pragma unroll
         for (int it = 0; it < FI; ++it) {
             const int k = tid + it * 256;
@@ -364,6 +392,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     float* sF = sW;
     int* sSeg = (int*)(sDt + HPT * Q);
     constexpr bool varlen = VL;
+    const bool cb16 = a.cb16 != 0;  // relaxed intermediates: CB in T
 
     // read now: a load issued just before its use in the y loop would make every row block wait
     // for all of the tile's outstanding memory operations
@@ -477,10 +506,14 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             // updates the state.
             lds_barrier();  // every wave is done reading x and B
             dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
-            if constexpr (G_::L_LDS)
-                lb.load(cbp, tid);
-            else if constexpr (CB_LDS)
-                dma_cb_bands<Q, CB_AUX>(sCB, cbp);
+            if constexpr (G_::L_LDS) {
+                lb.load(cbp, tid, cb16);
+            } else if constexpr (CB_LDS) {
+                if (cb16)
+                    dma_cb_bands<Q, CB_AUX, 2>(sCB, cbp);
+                else
+                    dma_cb_bands<Q, CB_AUX, 4>(sCB, cbp);
+            }
             hook.claim();
             if (a.relay && hook.relay_live()) {
                 // relay form: s_c to the chain's relay item, S_c back
@@ -518,10 +551,14 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         __syncthreads();
         // ---- round 2: CB (into registers for the L bands, else into LDS over x); S_c into registers
         __syncthreads();  // every wave holds its x operand in registers
-        if constexpr (G_::L_LDS)
-            lb.load(cbp, tid);
-        else if constexpr (CB_LDS)
-            dma_cb_bands<Q, 0>(sCB, cbp);
+        if constexpr (G_::L_LDS) {
+            lb.load(cbp, tid, cb16);
+        } else if constexpr (CB_LDS) {
+            if (cb16)
+                dma_cb_bands<Q, 0, 2>(sCB, cbp);
+            else
+                dma_cb_bands<Q, 0, 4>(sCB, cbp);
+        }
         if (hvalid) {
             const int K = a.slots, slot = c % K;
 #pragma unroll
@@ -580,7 +617,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         lds_barrier();
         if constexpr (G_::L_LDS) {
             const int nvh = hpg - tig * HPT < HPT ? hpg - tig * HPT : HPT;
-            lb.store((T*)smem, sA2, sF, sDt, sSeg, varlen, nvh, tid);  // over x (already in registers)
+            lb.store((T*)smem, sA2, sF, sDt, sSeg, varlen, cb16, nvh, tid);  // over x (already in registers)
             lds_barrier();                                             // L is complete
         }
         if (!hvalid) return;
@@ -612,7 +649,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 xs[kk][pb] = pack8<T>(lo, hi);
             }
         }
-        const __amdgpu_buffer_rsrc_t cbr = make_rsrc(cbp, (uint32_t)(Q * Q * 4));
+        const __amdgpu_buffer_rsrc_t cbr = make_rsrc(cbp, (uint32_t)(Q * Q * (cb16 ? 2 : 4)));
         // y: written once and never read here, so non-temporal (nt) stores keep it from
         // pushing the state slots and CB out of the L2
         const __amdgpu_buffer_rsrc_t yr =
@@ -660,11 +697,20 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 const int j0 = kk * 32 + 8 * q;
                 f32x4 c0, c1;
                 if constexpr (CB_LDS) {
-                    c0 = *(const f32x4*)(sCB + cb_off<Q>(i, j0));
-                    c1 = *(const f32x4*)(sCB + cb_off<Q>(i, j0 + 4));
+                    if (cb16) {
+                        cb16_widen<T>(*(const frag*)((const T*)sCB + cb_off<Q, 2>(i, j0)), c0, c1);
+                    } else {
+                        c0 = *(const f32x4*)(sCB + cb_off<Q, 4>(i, j0));
+                        c1 = *(const f32x4*)(sCB + cb_off<Q, 4>(i, j0 + 4));
+                    }
                 } else {
-                    c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0) * 4, 0, CB_AUX));
-                    c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0 + 4) * 4, 0, CB_AUX));
+                    if (cb16) {
+                        cb16_widen<T>(__builtin_bit_cast(frag, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0) * 2, 0, CB_AUX)),
+                                      c0, c1);
+                    } else {
+                        c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0) * 4, 0, CB_AUX));
+                        c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0 + 4) * 4, 0, CB_AUX));
+                    }
                 }
                 if (kk < kd) {
                     const float gx = __builtin_amdgcn_exp2f(ai2 - a2_h[kk * 32 + 31]);

@@ -46,24 +46,24 @@ def fused_form(impl):
             os.environ["MAMBA_SSD_RELAY"] = old
 
 
-def run_gpu(inp, chunk_size, impl, state_dtype=None, dev="cuda:0"):
+def run_gpu(inp, chunk_size, impl, state_dtype=None, dev="cuda:0", relaxed=False):
     """One ssd_prefill on the GPU; also requires the device status word to read SSD_OK."""
     with fused_form(impl) as name:
-        return _run_gpu(inp, chunk_size, name, state_dtype, dev)
+        return _run_gpu(inp, chunk_size, name, state_dtype, dev, relaxed)
 
 
-def _run_gpu(inp, chunk_size, impl, state_dtype, dev):
+def _run_gpu(inp, chunk_size, impl, state_dtype, dev, relaxed=False):
     g = inp.to(dev)
     if state_dtype is None:
         state_dtype = g.h0.dtype if g.h0 is not None else torch.float32
     Bt, L, H, P = g.x.shape
     G, N = g.B.shape[2], g.B.shape[3]
     prm = ssd.make_params(Bt, L, H, P, N, G, chunk_size, DT_NAME[g.x.dtype], _STATE_CODE[state_dtype],
-                          inp.dt_softplus, impl)
+                          inp.dt_softplus, impl, relaxed)
     ws = ssd.alloc_workspace(prm, g.x.device)
     y, fin = ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, g.h0, chunk_size=chunk_size,
                              impl=impl, dt_softplus=inp.dt_softplus,
-                             state_dtype=state_dtype, workspace=ws)
+                             state_dtype=state_dtype, workspace=ws, relaxed=relaxed)
     torch.cuda.synchronize()
     status = ssd.check_device_status(prm, ws)
     assert status == 0, "device status %d after %s Q=%d" % (status, impl, chunk_size)

@@ -105,6 +105,31 @@ def test_validate_rejects_short_struct_and_null(lib):
     assert lib.ssd_validate(ctypes.byref(p)) == BADARG
 
 
+def test_params_abi_version_1_and_relaxed_field(lib):
+    """A caller built against ABI version 1 passes the struct size that ends before `relaxed`
+    (56 bytes on LP64): accepted, with relaxed = 0 whatever the trailing bytes hold.  With the
+    full struct, relaxed must be 0 or 1 and reserved 0; relaxed halves the CB region (16-bit
+    inputs only)."""
+    p = base()
+    p.struct_size = ssd.Params.relaxed.offset
+    p.relaxed, p.reserved = 7, 9  # not read with the version-1 size
+    assert lib.ssd_validate(ctypes.byref(p)) == OK
+    p.struct_size = ssd.Params.relaxed.offset - 4
+    assert lib.ssd_validate(ctypes.byref(p)) == BADARG
+    q = base()
+    q.relaxed = 2
+    assert lib.ssd_validate(ctypes.byref(q)) == BADARG
+    q = base()
+    q.reserved = 1
+    assert lib.ssd_validate(ctypes.byref(q)) == BADARG
+    for impl in ("fused", "unfused"):
+        exact = ssd.workspace_layout(base(impl=impl))
+        rel = ssd.workspace_layout(base(impl=impl, relaxed=True))
+        assert rel.cb_bytes * 2 == exact.cb_bytes
+        f32 = ssd.workspace_layout(base(impl=impl, in_dtype="f32", relaxed=True))
+        assert f32.cb_bytes == ssd.workspace_layout(base(impl=impl, in_dtype="f32")).cb_bytes
+
+
 def test_validate_rejects_ticket_overflow(lib):
     p = base(batch=4096, seqlen=1 << 20, nheads=128, ngroups=128, chunk_size=64)
     assert lib.ssd_validate(ctypes.byref(p)) == SHAPE
