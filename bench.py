@@ -59,11 +59,11 @@ def measured_traffic(workload, Q):
     return t.get("bytes_per_launch")
 
 
-def time_impl(ssd, torch, g, w, Q, impl, steps, warmup, state_dtype=None):
+def time_impl(ssd, torch, g, w, Q, impl, steps, warmup, state_dtype=None, relaxed=False):
     """Warm up, then time `steps` calls; returns (ms per call, mean kernel ms)."""
     sd_name = state_dtype or w.state_dtype
     prm = ssd.make_params(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, Q, w.dtype,
-                          sd_name, True, impl)
+                          sd_name, True, impl, relaxed)
     ws = ssd.alloc_workspace(prm, g.x.device)
     y = torch.empty_like(g.x)
     sdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[sd_name]
@@ -73,7 +73,7 @@ def time_impl(ssd, torch, g, w, Q, impl, steps, warmup, state_dtype=None):
 
     def call(ev=None):
         ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, h0, chunk_size=Q, impl=impl,
-                        state_dtype=sdt, workspace=ws, y=y, final_state=fin, kernel_events=ev)
+                        state_dtype=sdt, workspace=ws, y=y, final_state=fin, kernel_events=ev, relaxed=relaxed)
 
     for _ in range(warmup):
         call()
@@ -308,6 +308,8 @@ def main():
     alg = comp + exch
     roof = {"bound": "hbm", "achieved": alg / k_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": alg / k_s / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+            # the HBM bytes the counters measured (when taken on these sources) over the same time
+            "frac_measured": (traffic / k_s / 1e9 / HBM_PEAK_GBS) if traffic else None,
             "kernel": "k_fused16" if w.dtype != "f32" else "k_fused", "kernel_ms": f_kms,
             "bytes_per_launch": alg, "compulsory_bytes": comp, "state_exchange_bytes": exch,
             "achieved_compulsory": comp / k_s / 1e9, "frac_compulsory": comp / k_s / 1e9 / HBM_PEAK_GBS,
@@ -324,7 +326,9 @@ def main():
         "roofline": roof,
         "unfused": {"ms_per_step": u_wall, "value": tokens / (u_wall / 1e3), "kernels_ms": u_kms,
                     "frac": alg / (u_kms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                    "frac_compulsory": comp / (u_kms / 1e3) / 1e9 / HBM_PEAK_GBS},
+                    "frac_compulsory": comp / (u_kms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                    "mfma_tflops": flops / (u_kms / 1e3) / 1e12,
+                    "mfma_frac": flops / (u_kms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]},
         "speedup_fused_vs_unfused": u_wall / f_wall,
     }
     if not args.no_sweep:
@@ -349,6 +353,23 @@ def main():
             c16, x16, _ = algorithmic(w.with_(state_dtype="f16"), Q, inp.h0 is not None)
             out["state_f16"] = {"fused_ms": hw, "fused_kernel_ms": hk, "value": tokens / (hw / 1e3),
                                 "frac": (c16 + x16) / (hk / 1e3) / 1e9 / HBM_PEAK_GBS}
+            # exact vs relaxed intermediates x fp32 vs fp16 state storage, at Q = 128 and 256
+            # (the pages' precision / performance trade-off), fused form
+            prec = {}
+            for q in (128, 256):
+                for sd in ("f32", "f16"):
+                    for rel in (False, True):
+                        key = "q%d_%s_%s" % (q, sd, "relaxed" if rel else "exact")
+                        if q == Q and sd == w.state_dtype and not rel:
+                            prec[key] = {"fused_ms": f_wall, "fused_kernel_ms": f_kms}
+                            continue
+                        log("precision point %s" % key)
+                        pw, pk = time_impl(ssd, torch, g, w, q, "fused", max(5, args.steps // 2), 2,
+                                           state_dtype=sd, relaxed=rel)
+                        prec[key] = {"fused_ms": pw, "fused_kernel_ms": pk}
+            for key, v in prec.items():
+                v["value"] = tokens / (v["fused_ms"] / 1e3)
+            out["precision_sweep"] = prec
         log("packed variable-length input")
         out["varlen"] = time_varlen(ssd, torch, 10)
         out["decode"] = decode_legs(ssd, torch, w)
