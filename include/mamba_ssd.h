@@ -161,6 +161,30 @@ ssd_status_t ssd_prefill_varlen(const ssd_params_t* p,
                                 void* y, void* final_state,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Packed variable-length input with a state per sequence (the same section of the kernel-fusion
+ * write-up: variable-length sequences and their initial states without padding, one pseudo-chunk
+ * per sequence in a chunk, handled by masking).  Same as ssd_prefill_varlen except:
+ *   - a sequence starts at t = 0 of every row as well as wherever seq_idx changes, and
+ *     seq_idx[b,t] in [0, nseq) is the number of the sequence holding token t; each number
+ *     labels one run of tokens (a number used by two runs gets either run's final state);
+ *   initial_states [nseq, H, P, N] state_dtype  NULL means 0; 16-byte aligned: sequence q starts
+ *                                               from initial_states[q];
+ *   final_states   [nseq, H, P, N] state_dtype  required output, 16-byte aligned: the state after
+ *                                               the last token of sequence q; entries of numbers
+ *                                               no run uses are left as they were.
+ * There is no per-row initial or final state.  Tokens whose number lies outside [0, nseq) run
+ * from a zero state and write no final state.  16-bit inputs only (fp32: SSD_ERR_UNSUPPORTED);
+ * the fused form hands states over in its chunk tiles (no relay items).  nseq < 1:
+ * SSD_ERR_INVALID_SHAPE. */
+ssd_status_t ssd_prefill_varlen_states(const ssd_params_t* p,
+                                       const void* x, const void* dt, const float* A,
+                                       const void* B, const void* C,
+                                       const float* D, const float* dt_bias,
+                                       const int32_t* seq_idx, int nseq,
+                                       const void* initial_states,
+                                       void* y, void* final_states,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ssd_prefill without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
  * workspace is a static device array inside the library, SSD_NOALLOC_SCRATCH_BYTES bytes on each

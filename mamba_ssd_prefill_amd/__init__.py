@@ -14,6 +14,7 @@ import os
 __all__ = ["ssd_prefill", "workspace_size", "workspace_layout", "Params", "SSDError", "library_path",
            "load_library", "step_chunk_cumsum", "step_bmm", "step_chunk_state", "step_state_passing",
            "step_chunk_scan", "check_device_status", "make_params", "ssd_decode_step", "ssd_prefill_noalloc",
+           "ssd_prefill_varlen_states",
            "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,7 +31,7 @@ EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill",
                     "ssd_check_device_status",
                     "ssd_status_string", "ssd_workspace_layout", "ssd_step_chunk_cumsum", "ssd_step_bmm",
                     "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan", "ssd_decode_step",
-                    "ssd_prefill_varlen", "ssd_prefill_noalloc"]
+                    "ssd_prefill_varlen", "ssd_prefill_noalloc", "ssd_prefill_varlen_states"]
 
 
 class SSDError(RuntimeError):
@@ -103,6 +104,8 @@ def load_library():
     lib.ssd_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_prefill_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_prefill_noalloc.restype = ctypes.c_int
+    lib.ssd_prefill_varlen_states.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, sz, vp]
+    lib.ssd_prefill_varlen_states.restype = ctypes.c_int
     for f in ("ssd_step_chunk_cumsum", "ssd_step_bmm", "ssd_step_chunk_state", "ssd_step_state_passing",
               "ssd_step_chunk_scan", "ssd_decode_step"):
         getattr(lib, f).restype = ctypes.c_int
@@ -238,6 +241,42 @@ def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_
         _check(load_library().ssd_prefill_timed(*args, ctypes.c_void_p(ev0.cuda_event), ctypes.c_void_p(ev1.cuda_event)),
                "ssd_prefill_timed")
     return y, final_state
+
+
+def ssd_prefill_varlen_states(x, dt, A, B, C, D=None, dt_bias=None, seq_idx=None, nseq=None, initial_states=None,
+                              chunk_size=128, state_dtype=None, impl="fused", dt_softplus=True, workspace=None,
+                              y=None, final_states=None, relaxed=False):
+    """Packed sequences with a state per sequence (ssd_prefill_varlen_states): seq_idx (int32
+    [B, L]) numbers the sequence of each token, in [0, nseq); ``initial_states`` (None: zeros)
+    and the returned ``final_states`` are [nseq, H, P, N].  Returns (y, final_states)."""
+    import torch
+    _check_tensors(x, dt, A, B, C, D, dt_bias, None)
+    if seq_idx is None or nseq is None:
+        raise ValueError("seq_idx and nseq are required")
+    if (tuple(seq_idx.shape) != tuple(x.shape[:2]) or seq_idx.dtype != torch.int32 or seq_idx.device != x.device
+            or not seq_idx.is_contiguous()):
+        raise ValueError("seq_idx must be a contiguous int32 [B, L] tensor on %s" % x.device)
+    Bt, L, H, P = x.shape
+    N = B.shape[3]
+    if state_dtype is None:
+        state_dtype = initial_states.dtype if initial_states is not None else torch.float32
+    for name, t in (("initial_states", initial_states), ("final_states", final_states)):
+        if t is not None and (tuple(t.shape) != (nseq, H, P, N) or t.dtype != state_dtype or t.device != x.device
+                              or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous %s [%d, %d, %d, %d] tensor" % (name, state_dtype, nseq, H, P, N))
+    sd = {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[state_dtype]
+    prm = _params_for(x, B, chunk_size, sd, dt_softplus, impl, relaxed)
+    if y is None:
+        y = torch.empty_like(x)
+    if final_states is None:
+        final_states = torch.zeros((nseq, H, P, N), dtype=state_dtype, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(prm, x.device)
+    _check(load_library().ssd_prefill_varlen_states(
+        ctypes.byref(prm), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(seq_idx),
+        int(nseq), _ptr(initial_states), _ptr(y), _ptr(final_states), _ptr(workspace), workspace.numel(),
+        _stream(x.device)), "ssd_prefill_varlen_states")
+    return y, final_states
 
 
 def ssd_prefill_noalloc(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_size=128, state_dtype=None,

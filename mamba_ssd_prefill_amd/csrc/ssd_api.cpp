@@ -471,12 +471,15 @@ SSD_EXPORT ssd_status_t ssd_step_chunk_scan(const ssd_params_t* p, const void* x
 ssd_status_t ssd::prefill_impl(const ssd_params_t* p, const void* x, const void* dt, const float* A, const void* B,
                                const void* C, const float* D, const float* dt_bias, const void* initial_state,
                                void* y, void* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                               hipEvent_t ev_begin, hipEvent_t ev_end, const int32_t* seq_idx) {
+                               hipEvent_t ev_begin, hipEvent_t ev_end, const int32_t* seq_idx,
+                               const ssd::SeqStates& ss) {
     Layout l;
     ssd_status_t s = check_ws(p, workspace, workspace_bytes, &l);
     if (s != SSD_OK) return s;
-    if (!aligned(seq_idx, 4)) return SSD_ERR_MISALIGNED;
-    if (!x || !dt || !A || !B || !C || !y || !final_state) return SSD_ERR_NULL_POINTER;
+    const bool seqst = ss.final_ != nullptr;
+    if (seqst && p->in_dtype == SSD_F32) return SSD_ERR_UNSUPPORTED;
+    if (!aligned(seq_idx, 4) || !aligned(ss.initial, 16) || !aligned(ss.final_, 16)) return SSD_ERR_MISALIGNED;
+    if (!x || !dt || !A || !B || !C || !y || (!final_state && !seqst)) return SSD_ERR_NULL_POINTER;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(final_state, 16) ||
         !aligned(initial_state, 16) || !aligned(dt, elem_size(p->in_dtype)) || !aligned(A, 4) || !aligned(D, 4) ||
         !aligned(dt_bias, 4))
@@ -491,6 +494,10 @@ ssd_status_t ssd::prefill_impl(const ssd_params_t* p, const void* x, const void*
     a.D = D;
     a.dt_bias = dt_bias;
     a.seq_idx = seq_idx;
+    a.seqstates = seqst ? 1 : 0;
+    a.nseq = ss.nseq;
+    a.seq_h0 = ss.initial;
+    a.seq_fin = ss.final_;
     a.y = y;
     a.has_h0 = initial_state != nullptr;
     hipError_t e;
@@ -501,6 +508,11 @@ ssd_status_t ssd::prefill_impl(const ssd_params_t* p, const void* x, const void*
         if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED_OCCUPANCY, p, a, st);
         if (e != hipSuccess) return hip_status(e);
         set_partitions(p, l, d, a);
+        if (seqst) {
+            // per-sequence states are handed off by the chunk tiles' own hop
+            a.relay = 0;
+            a.slots = 1;
+        }
         // initial state into the ring's slot 0; every sync word reset (chain counters to 1: the
         // state entering chunk 0 is ready -- in the relay form its relay waves publish it)
         // the 16-bit tile keeps p in its interleaved order; the fp32 tile in plain order
@@ -512,8 +524,9 @@ ssd_status_t ssd::prefill_impl(const ssd_params_t* p, const void* x, const void*
         if (e == hipSuccess) e = mark(ev_begin);
         if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED, p, a, st);
         if (e == hipSuccess) e = mark(ev_end);
-        // final state out of the last chunk's slot (the relay form keeps it in slot 1)
-        if (e == hipSuccess)
+        // final state out of the last chunk's slot (the relay form keeps it in slot 1); with
+        // per-sequence states the kernel wrote every final state itself
+        if (e == hipSuccess && !seqst)
             e = ssd::launch_ring_copy(a.states, final_state, 0, p->batch, p->nheads, p->headdim, pw, p->dstate, K,
                                       a.relay ? 1 : l.w.nchunks % K, es, pperm, nullptr, 0, 0, 1, 0u, st);
         return hip_status(e);
@@ -524,7 +537,7 @@ ssd_status_t ssd::prefill_impl(const ssd_params_t* p, const void* x, const void*
     if (e == hipSuccess) e = dispatch(ssd::STEP_CHUNK_STATE, p, a, st);
     if (e == hipSuccess) e = boundary_in(p, l, a, initial_state, a.status, 1, 0, st);
     if (e == hipSuccess) e = ssd::launch_state_passing(a, p->headdim * p->dstate, st);
-    if (e == hipSuccess) e = boundary_out(p, l, a, final_state, st);
+    if (e == hipSuccess && !seqst) e = boundary_out(p, l, a, final_state, st);
     if (e == hipSuccess) e = dispatch(ssd::STEP_CHUNK_SCAN, p, a, st);
     if (e == hipSuccess) e = mark(ev_end);
     return hip_status(e);
@@ -545,6 +558,17 @@ SSD_EXPORT ssd_status_t ssd_prefill_varlen(const ssd_params_t* p, const void* x,
     if (!seq_idx) return SSD_ERR_NULL_POINTER;
     return ssd::prefill_impl(p, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, workspace, workspace_bytes,
                              stream, nullptr, nullptr, seq_idx);
+}
+
+SSD_EXPORT ssd_status_t ssd_prefill_varlen_states(const ssd_params_t* p, const void* x, const void* dt,
+                                                 const float* A, const void* B, const void* C, const float* D,
+                                                 const float* dt_bias, const int32_t* seq_idx, int nseq,
+                                                 const void* initial_states, void* y, void* final_states,
+                                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (!seq_idx || !final_states) return SSD_ERR_NULL_POINTER;
+    if (nseq < 1) return SSD_ERR_INVALID_SHAPE;
+    return ssd::prefill_impl(p, x, dt, A, B, C, D, dt_bias, nullptr, y, nullptr, workspace, workspace_bytes, stream,
+                             nullptr, nullptr, seq_idx, ssd::SeqStates{initial_states, final_states, nseq});
 }
 
 SSD_EXPORT ssd_status_t ssd_prefill_timed(const ssd_params_t* p, const void* x, const void* dt, const float* A,

@@ -16,12 +16,28 @@ __global__ __launch_bounds__(256) void k_state_passing(SsdArgs a, int PN) {
     const int H = a.nheads, nc = a.nchunks, Q = a.chunk, K = a.slots;
     f32x4 S = load_state4(a.states, a.state_dtype, ((size_t)b * K * H + h) * PN + e);
     if (a.seq_idx) {
-        // packed input: a sequence that starts inside chunk c passes no state on
+        // packed input: a sequence that starts inside chunk c passes no state on; with
+        // per-sequence states the state passed on carries that sequence's initial state instead,
+        // decayed from just before its first token (found by bisecting the start counts) to the
+        // chunk end
         for (int c = 0; c < nc; ++c) {
-            const bool start = a.seg[((size_t)b * nc + c) * Q + Q - 1] != 0;
-            const float dec = start ? 0.f : __expf(a.acs[(((size_t)b * nc + c) * H + h) * Q + Q - 1]);
+            const int* sg = a.seg + ((size_t)b * nc + c) * Q;
+            const float* ac = a.acs + (((size_t)b * nc + c) * H + h) * Q;
+            const int kc = sg[Q - 1];
+            const float dec = kc != 0 ? 0.f : __expf(ac[Q - 1]);
             const f32x4 sl = *(const f32x4*)(a.s + (((size_t)b * nc + c) * H + h) * PN + e);
             S = dec * S + sl;
+            if (a.seqstates && a.seq_h0 && kc != 0) {
+                int lo = 0, hi = Q - 1;  // the first token with sg == kc
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (sg[mid] >= kc) hi = mid; else lo = mid + 1;
+                }
+                const int q = a.seq_idx[(size_t)b * a.seqlen + (size_t)c * Q + lo];
+                if (q >= 0 && q < a.nseq)
+                    S += __expf(ac[Q - 1] - (lo > 0 ? ac[lo - 1] : 0.f)) *
+                         load_state4(a.seq_h0, a.state_dtype, ((size_t)q * H + h) * PN + e);
+            }
             store_state4(a.states, a.state_dtype, (((size_t)b * K + c + 1) * H + h) * PN + e, S);
         }
         return;

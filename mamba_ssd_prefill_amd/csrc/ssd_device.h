@@ -482,7 +482,7 @@ template <typename T> __device__ inline u32x4 pack_unit(const f32x4* v) {
 // number of memory operations per chunk -- which the waits below count -- stays the same.  (A
 // run-time choice rather than another instantiation: four relay instantiations in the fused
 // kernel pushed its registers into spills.)
-template <typename T, int NT, int RWM, bool VL>
+template <typename T, int NT, int RWM, int VL>
 __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int w) {
     constexpr int TPU = tiles_per_unit<T>(), TPW = NT / relay_waves<T, NT, RWM>();
     static_assert(TPW % TPU == 0, "a relay wave holds whole operand units");
@@ -527,7 +527,7 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
         }
         d = bload_f32<AUX_L2>(make_rsrc(a.acs + (((size_t)b * nc + c) * H + h) * Q, (uint32_t)Q * 4),
                               (uint32_t)(Q - 1) * 4);
-        if constexpr (VL)
+        if constexpr (VL != 0)
             sg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.seg + ((size_t)b * nc + c) * Q, (uint32_t)Q * 4),
                                                       (uint32_t)(Q - 1) * 4, 0, AUX_L2);
         else
@@ -539,7 +539,7 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     // |St(c)| + |L(c + 1)| operations are pending (|St(c)| alone if L(c + 1) is not issued yet),
     // L(c) and everything before it (St(c - 1) too) are complete.  Any extra operation in
     // between (a poll, a flag) only makes the count wait for more.
-    constexpr int NST = TPW / TPU, NLD = NAL + (VL ? 2 : 1);
+    constexpr int NST = TPW / TPU, NLD = NAL + (VL != 0 ? 2 : 1);
     auto step = [&](int c, aggv (&cur)[NAL], float dcur, uint32_t gcur, aggv (&nxt)[NAL], float& dnxt,
                     uint32_t& gnxt) -> bool {
         const bool has_next = c + 1 < nc;
@@ -736,8 +736,9 @@ template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (k < V) {
+                // with per-sequence states a row's first token starts a sequence as well
                 const int t = c * Q + lane * V + k;
-                tot += (t > 0 && t < L && sq[t] != sq[t - 1]) ? 1 : 0;
+                tot += (t < L && (t > 0 ? sq[t] != sq[t - 1] : a.seqstates != 0)) ? 1 : 0;
             }
             run[k] = tot;
         }
@@ -757,6 +758,31 @@ template <typename T> __device__ void cumsum_tile(const SsdArgs& a, int b, int c
 // The Q x Q block of CB number idx in a.cb (fp32, or with a.cb16 the 16-bit input type).
 __device__ inline float* cb_at(const SsdArgs& a, size_t idx) {
     return (float*)((char*)a.cb + idx * (size_t)a.chunk * a.chunk * (a.cb16 ? 2 : 4));
+}
+
+// ---- per-sequence states of packed input ---------------------------------------------------
+// The chunk's segments (the pieces of its sequences, [KF] "与vLLM的深度融合": one pseudo-chunk per
+// sequence in a chunk) are numbered by seg: segment k holds the tokens with seg[i] == k.
+
+// First token of the chunk with seg >= k (Q when none): wave-uniform, one LDS read per lane
+// per 64 tokens (Q is a multiple of 64).
+__device__ inline int seg_first(const int* sSeg, int Q, int k) {
+    const int lane = tid_here() & 63;
+    for (int w0 = 0; w0 < Q; w0 += 64) {
+        const unsigned long long m = __ballot(sSeg[w0 + lane] >= k);
+        if (m) return w0 + __builtin_ctzll(m);
+    }
+    return Q;
+}
+
+// Sequence number of token t of row b (wave-uniform).
+__device__ inline int seq_at(const SsdArgs& a, int b, int t) {
+    return __builtin_amdgcn_readfirstlane(a.seq_idx[(size_t)b * a.seqlen + t]);
+}
+
+// Element offset of state element (p, n) of head h of sequence q in a [nseq][H][P][N] array.
+__device__ inline size_t seq_state_off(const SsdArgs& a, int q, int h, int p, int n, int P, int N) {
+    return (((size_t)q * a.nheads + h) * P + p) * N + n;
 }
 
 // ---- step 2: bmm ([KF] item 7) ---------------------------------------------------------
@@ -873,7 +899,7 @@ enum : int { MODE_STATE = 0, MODE_SCAN = 1, MODE_FUSED = 2 };
 //             + s_c to the next ring slot and release it, then chunk_scan with S_c.
 // relay_live (MODE_FUSED of a relay-form launch): the partition's relay items run.  VL: packed
 // variable-length input (a.seq_idx set), a separate instantiation.
-template <typename T, int P, int N, int MODE, bool VL>
+template <typename T, int P, int N, int MODE, int VL>
 __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbase,
                            bool relay_live = false) {
     typedef Geo<T, P, N> G_;
@@ -900,7 +926,7 @@ __device__ void chunk_tile(const SsdArgs& a, int b, int c, int g, int tig, char*
     float* sAcs = sDt + HPT * QMAX;             // [HPT][QMAX]
     float* sW = sAcs + HPT * QMAX;              // [HPT][QMAX] chunk-state weights
     int* sSeg = (int*)(sW + HPT * QMAX);        // [QMAX] packed input: sequence starts up to token i
-    constexpr bool varlen = VL;
+    constexpr bool varlen = VL != 0;
 
     {
         // heads of the tile past the group read as zeros

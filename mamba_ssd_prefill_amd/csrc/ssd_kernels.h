@@ -34,7 +34,7 @@ template <typename T, int N> __global__ __launch_bounds__(256) void k_bmm(SsdArg
 }
 
 // blockIdx.x -> (b, c, g, tile-in-group).  VL: packed variable-length input (a.seq_idx set).
-template <typename T, int P, int N, int MODE, bool VL> __global__ __launch_bounds__(256) void k_chunk(SsdArgs a) {
+template <typename T, int P, int N, int MODE, int VL> __global__ __launch_bounds__(256) void k_chunk(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo<T, P, N>::SMEM];
     int r = blockIdx.x;
     const int tig = r % a.tpg;
@@ -46,7 +46,7 @@ template <typename T, int P, int N, int MODE, bool VL> __global__ __launch_bound
     chunk_tile<T, P, N, MODE, VL>(a, b, c, g, tig, smem, cb_global(a, b, c, g));
 }
 
-template <typename T, int P, int N, int Q, int MODE, bool VL>
+template <typename T, int P, int N, int Q, int MODE, int VL>
 __global__ __launch_bounds__(256) void k_chunk16(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
     int r = blockIdx.x;
@@ -156,7 +156,7 @@ struct ClaimHook {
 };
 
 // chunk(args, b, c, g, tig, cb, hook) runs one chunk tile after its cumsum and bmm tiles are done.
-template <int HPT, int P, typename T, int N, bool VL, typename ChunkFn>
+template <int HPT, int P, typename T, int N, int VL, typename ChunkFn>
 __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     __shared__ uint32_t s_word, s_next;
     const uint32_t raw = xcc_id();
@@ -267,7 +267,7 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     }
 }
 
-template <typename T, int P, int N, bool VL> __global__ __launch_bounds__(256) void k_fused(SsdArgs a) {
+template <typename T, int P, int N, int VL> __global__ __launch_bounds__(256) void k_fused(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo<T, P, N>::SMEM];
     fused_loop<Geo<T, P, N>::HPT, P, T, N, VL>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
                                                       const float* cbp, const auto& hook) {
@@ -276,7 +276,7 @@ template <typename T, int P, int N, bool VL> __global__ __launch_bounds__(256) v
     });
 }
 
-template <typename T, int P, int N, int Q, bool VL>
+template <typename T, int P, int N, int Q, int VL>
 __global__ __launch_bounds__(256, (Geo16<T, P, N, Q>::OCC)) void k_fused16(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
     fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N, VL>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
@@ -317,8 +317,8 @@ inline hipError_t launch_fused(const void* fn, SsdArgs& a, hipStream_t st) {
     return launch(fn, grid, &a, st);
 }
 
-// VL: the packed-input instantiation (the caller passes a.seq_idx != nullptr).
-template <typename T, int P, int N, bool VL> hipError_t launch_step_t(int step, SsdArgs& a, hipStream_t st) {
+// VL: 0 plain input, 1 packed input, 2 packed input with per-sequence states.
+template <typename T, int P, int N, int VL> hipError_t launch_step_t(int step, SsdArgs& a, hipStream_t st) {
     typedef Geo<T, P, N> G_;
     const unsigned Bn = a.batch, nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
     switch (step) {
@@ -342,7 +342,7 @@ template <typename T, int P, int N, bool VL> hipError_t launch_step_t(int step, 
     (void)sizeof(G_);
 }
 
-template <typename T, int P, int N, int Q, bool VL> hipError_t launch_step16(int step, SsdArgs& a, hipStream_t st) {
+template <typename T, int P, int N, int Q, int VL> hipError_t launch_step16(int step, SsdArgs& a, hipStream_t st) {
     const unsigned Bn = a.batch, nc = a.nchunks, Gn = a.ngroups, tpg = a.tpg;
     switch (step) {
     case STEP_CUMSUM:
@@ -367,7 +367,7 @@ template <typename T, int P, int N, int Q, bool VL> hipError_t launch_step16(int
 // The (headdim, dstate) pairs each input type supports, dispatched to launch_step16 /
 // launch_step_t; hipErrorNotSupported otherwise.  One translation unit instantiates one
 // (type, chunk size, VL) combination.
-template <typename T, int Q, bool VL> hipError_t dispatch16(int step, int P, int N, SsdArgs& a, hipStream_t st) {
+template <typename T, int Q, int VL> hipError_t dispatch16(int step, int P, int N, SsdArgs& a, hipStream_t st) {
     if (P == 16 && N == 32) return launch_step16<T, 16, 32, Q, VL>(step, a, st);
     if (P == 16 && N == 64) return launch_step16<T, 16, 64, Q, VL>(step, a, st);
     if (P == 16 && N == 128) return launch_step16<T, 16, 128, Q, VL>(step, a, st);
@@ -383,7 +383,7 @@ template <typename T, int Q, bool VL> hipError_t dispatch16(int step, int P, int
     return hipErrorNotSupported;
 }
 
-template <bool VL> hipError_t dispatch32(int step, int P, int N, SsdArgs& a, hipStream_t st) {
+template <int VL> hipError_t dispatch32(int step, int P, int N, SsdArgs& a, hipStream_t st) {
     if (P == 16 && N == 16) return launch_step_t<float, 16, 16, VL>(step, a, st);
     if (P == 16 && N == 32) return launch_step_t<float, 16, 32, VL>(step, a, st);
     if (P == 16 && N == 64) return launch_step_t<float, 16, 64, VL>(step, a, st);

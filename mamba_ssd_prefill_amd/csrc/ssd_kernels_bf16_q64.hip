@@ -4,7 +4,7 @@
 namespace ssd {
 
 hipError_t launch_step_bf16_q64_vl0(int step, int P, int N, SsdArgs& a, hipStream_t st) {
-    return dispatch16<__bf16, 64, false>(step, P, N, a, st);
+    return dispatch16<__bf16, 64, 0>(step, P, N, a, st);
 }
 
 }  // namespace ssd

@@ -1,10 +1,10 @@
-// ssd_kernels_f16_q128_vl.hip -- kernel instantiations for f16 inputs, chunk size 128, packed variable-length input.
+// ssd_kernels_f16_q128_vl.hip -- kernel instantiations for f16 inputs, chunk size 128, packed variable-length input (with or without per-sequence states).
 #include "ssd_kernels.h"
 
 namespace ssd {
 
 hipError_t launch_step_f16_q128_vl1(int step, int P, int N, SsdArgs& a, hipStream_t st) {
-    return dispatch16<_Float16, 128, true>(step, P, N, a, st);
+    return a.seqstates ? dispatch16<_Float16, 128, 2>(step, P, N, a, st) : dispatch16<_Float16, 128, 1>(step, P, N, a, st);
 }
 
 }  // namespace ssd

@@ -4,7 +4,7 @@
 namespace ssd {
 
 hipError_t launch_step_f32_vl0(int step, int P, int N, SsdArgs& a, hipStream_t st) {
-    return dispatch32<false>(step, P, N, a, st);
+    return dispatch32<0>(step, P, N, a, st);
 }
 
 hipError_t launch_step_f32(int step, int P, int N, SsdArgs& a, hipStream_t st) {

@@ -4,7 +4,7 @@
 namespace ssd {
 
 hipError_t launch_step_f32_vl1(int step, int P, int N, SsdArgs& a, hipStream_t st) {
-    return dispatch32<true>(step, P, N, a, st);
+    return dispatch32<1>(step, P, N, a, st);
 }
 
 }  // namespace ssd

@@ -56,6 +56,13 @@ struct SsdArgs {
     int relay_admit;    // fused relay form: 0 makes every partition decide "chunk tiles hop" (a test knob)
     int agg16;          // fused relay form: the chunk-state ring holds fp16 (fp16 state storage), else fp32
     int cb16;           // relaxed intermediates: CB stored in the 16-bit input type instead of fp32
+    // packed input with per-sequence states (ssd_prefill_varlen_states): a row's first token
+    // starts a sequence too; seq_idx[b][t] in [0, nseq) numbers the sequence, whose initial
+    // state is seq_h0[q] (nullptr: zero) and whose final state goes to seq_fin[q], both
+    // [nseq][H][P][N] in the state dtype
+    int seqstates, nseq;
+    const void* seq_h0;
+    void* seq_fin;
     int part_max_work;  // host only: the longest partition queue
     int cu_count;       // host only: compute units of the device
     int fused_occ;      // host only: workgroups of the fused kernel one CU holds at once

@@ -355,10 +355,59 @@ template <typename T, typename G_, int AUX> struct LBuild {
     }
 };
 
+// Per-sequence states at the chunk's state hand-off (packed input with per-sequence states):
+//   inj:      the chunk's last segment starts inside it, so the state it passes on also carries
+//             that sequence's initial state, decayed from just before its first token to the
+//             chunk end (the chunk-state sum itself is already masked to the segment);
+//   done0:    segment 0 (begun in an earlier chunk) ends inside this chunk: its final state is
+//             the partial sum written by the chunk-state step plus S_c decayed to its last token;
+//   last_ends: the chunk's last segment ends at the chunk end (or the row's): its final state
+//             is the state passed on.
+// apply() adds these for one lane's 4 state elements (p, n .. n+3); sv = S_c, snew = S_{c+1}.
+struct SeqEnds {
+    bool any = false, inj = false, done0 = false, last_ends = false;
+    int qk = 0, q0 = 0, ql = 0;
+    float deck = 0.f, dec0 = 0.f;
+    __device__ inline void apply(const SsdArgs& a, int h, int p, int n, int P, int N, f32x4 sv, f32x4& snew) const {
+        const int sdt = a.state_dtype;
+        if (inj) snew += deck * load_state4(a.seq_h0, sdt, seq_state_off(a, qk, h, p, n, P, N));
+        if (done0) {
+            const size_t o = seq_state_off(a, q0, h, p, n, P, N);
+            store_state4(a.seq_fin, sdt, o, load_state4(a.seq_fin, sdt, o) + dec0 * sv);
+        }
+        if (last_ends) store_state4(a.seq_fin, sdt, seq_state_off(a, ql, h, p, n, P, N), snew);
+    }
+};
+
+// The hand-off facts of chunk c of row b for head h (a2_h = acs log2 e of the head); with_inj:
+// the caller forms S_{c+1} itself (the fused hop), else the state-passing step already did.
+__device__ inline SeqEnds seq_ends(const SsdArgs& a, int b, int c, int h, const int* sSeg, const float* a2_h,
+                                   int Q, int valid, bool with_inj) {
+    SeqEnds r;
+    const int tok0 = c * Q, L = a.seqlen;
+    const int Kc = sSeg[Q - 1];
+    const int sK = Kc >= 1 ? seg_first(sSeg, Q, Kc) : 0;
+    r.qk = Kc >= 1 ? seq_at(a, b, tok0 + sK) : 0;
+    r.inj = with_inj && Kc >= 1 && a.seq_h0 && r.qk >= 0 && r.qk < a.nseq;
+    r.deck = __builtin_amdgcn_exp2f(a2_h[Q - 1] - (sK > 0 ? a2_h[sK - 1] : 0.f));
+    r.q0 = seq_at(a, b, tok0);
+    if (sSeg[0] == 0 && Kc >= 1 && r.q0 >= 0 && r.q0 < a.nseq) {
+        r.done0 = true;
+        r.dec0 = __builtin_amdgcn_exp2f(a2_h[seg_first(sSeg, Q, 1) - 1]);
+        wait_vm_all();  // this wave's partial sum of q0 (the chunk-state step, same lanes) is stored
+    }
+    const int tn = tok0 + valid;
+    r.ql = Kc >= 1 ? r.qk : r.q0;
+    r.last_ends = (tn >= L || seq_at(a, b, tn) != seq_at(a, b, tn - 1)) && r.ql >= 0 && r.ql < a.nseq;
+    r.any = r.inj || r.done0 || r.last_ends;
+    return r;
+}
+
 // `hook` (fused form): claim() after the round-2 reads are issued; see ClaimHook.
-// VL: packed variable-length input (a.seq_idx set): the decays are masked by sequence; a
-// separate instantiation, so the plain kernels carry none of the masking code.
-template <typename T, int P, int N, int Q, int MODE, bool VL, typename Hook>
+// VL: 0 plain input; 1 packed variable-length input (a.seq_idx set: the decays are masked by
+// sequence); 2 packed input with per-sequence states (a.seqstates).  Separate instantiations, so
+// each kernel carries only the code of its own mode.
+template <typename T, int P, int N, int Q, int MODE, int VL, typename Hook>
 __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbp,
                              const Hook& hook) {
     typedef Geo16<T, P, N, Q> G_;
@@ -391,7 +440,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     float* sDt = sW + HPT * Q;
     float* sF = sW;
     int* sSeg = (int*)(sDt + HPT * Q);
-    constexpr bool varlen = VL;
+    constexpr bool varlen = VL != 0;
     const bool cb16 = a.cb16 != 0;  // relaxed intermediates: CB in T
 
     // read now: a load issued just before its use in the y loop would make every row block wait
@@ -464,6 +513,63 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             for (int pb = 0; pb < MBP; ++pb) acc[nb][pb] = vzero<f32x4>();
         int boff[NB];
         tr_lane_offs<N, NB>(boff);
+        if constexpr (VL == 2) {
+            if (a.seqstates && hvalid) {
+                // Per-sequence final states of the segments that end before the chunk's last
+                // one: the chunk state over the segment's tokens up to its last token e, plus (a
+                // segment that starts here) its sequence's initial state decayed to e.  Segment 0
+                // (begun in an earlier chunk) gets its partial sum here and the decayed entry state
+                // S_c at the hop (chunk_scan in the unfused form).
+                const int Kc = sSeg[Q - 1], k0 = sSeg[0] == 0 ? 0 : 1;
+                const float* dt_h = sDt + hs * Q;
+                for (int k = k0; k < Kc; ++k) {
+                    const int s = k == 0 ? 0 : seg_first(sSeg, Q, k);
+                    const int e = seg_first(sSeg, Q, k + 1) - 1;
+                    const int qs = seq_at(a, b, tok0 + s);
+                    const float a2e = a2_h[e];
+                    f32x4 pacc[NB][MBP];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int pb = 0; pb < MBP; ++pb) pacc[nb][pb] = vzero<f32x4>();
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk) {
+                        if (kk * 32 > e || kk * 32 + 31 < s) continue;
+                        frag af[NB];
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) af[nb] = tr_frag_at<T, N>(sBC, boff[nb], kk * 32);
+                        float w[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int j = kk * 32 + 8 * q + u;
+                            w[u] = sSeg[j] == k ? __builtin_amdgcn_exp2f(a2e - a2_h[j]) * dt_h[j] : 0.f;
+                        }
+                        frag xw[MBP];
+#pragma unroll
+                        for (int pb = 0; pb < MBP; ++pb)
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) xw[pb][u] = (T)((float)xf[kk][pb][u] * w[u]);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int pb = 0; pb < MBP; ++pb) pacc[nb][pb] = TT<T>::mma(af[nb], xw[pb], pacc[nb][pb]);
+                    }
+                    if (qs >= 0 && qs < a.nseq) {
+                        const float dec = (k >= 1 && a.seq_h0) ? __builtin_amdgcn_exp2f(a2e - (s > 0 ? a2_h[s - 1] : 0.f)) : 0.f;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int pb = 0; pb < MBP; ++pb) {
+                                const int p = ph * PW + G_::pcol(pb, r16), n = nb * 16 + 4 * q;
+                                const size_t o = seq_state_off(a, qs, h, p, n, P, N);
+                                f32x4 v = pacc[nb][pb];
+                                if (dec != 0.f) v += dec * load_state4(a.seq_h0, a.state_dtype, o);
+                                store_state4(a.seq_fin, a.state_dtype, o, v);
+                            }
+                    }
+                }
+            }
+        }
         if (hvalid) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
@@ -533,13 +639,21 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     ring_rsrc(a.states, a.state_dtype, ring_chain(b, sout, h, ph, K, H, WPH, NB * MBP), NB * MBP);
                 const float dec = carry ? __builtin_amdgcn_exp2f(a2_h[Q - 1]) : 0.f;
                 const bool zero0 = c == 0 && !a.has_h0;  // S_0 = 0: nothing to read
+                SeqEnds se;
+                if constexpr (VL == 2) {
+                    if (a.seqstates) se = seq_ends(a, b, c, h, sSeg, a2_h, Q, valid, true);
+                }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int pb = 0; pb < MBP; ++pb) {
                         const uint32_t off = ((nb * MBP + pb) * 64 + lane) * 4;
                         const f32x4 sv = zero0 ? vzero<f32x4>() : ring_load(rin, a.state_dtype, off);
-                        ring_store(rout, a.state_dtype, off, dec * sv + acc[nb][pb]);
+                        f32x4 snew = dec * sv + acc[nb][pb];
+                        if constexpr (VL == 2) {
+                            if (se.any) se.apply(a, h, ph * PW + G_::pcol(pb, r16), nb * 16 + 4 * q, P, N, sv, snew);
+                        }
+                        ring_store(rout, a.state_dtype, off, snew);
                         scb[nb][pb] = cvt4<T>(sv);
                     }
                 publish_flag_wave(fl, (uint32_t)c + 1 + base);  // its wait covers the copies too
@@ -568,6 +682,25 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     const int p = ph * PW + G_::pcol(pb, r16), n = nb * 16 + 4 * q;
                     scb[nb][pb] = cvt4<T>(load_state4(a.states, a.state_dtype, ((((size_t)b * K + slot) * H + h) * P + p) * N + n));
                 }
+            if constexpr (VL == 2) {
+                if (a.seqstates) {
+                    // per-sequence final states ending in this chunk, from the chunk-entry and
+                    // chunk-end states the state-passing step left in slots c and c + 1
+                    const SeqEnds se = seq_ends(a, b, c, h, sSeg, a2_h, Q, valid, false);
+                    if (se.any) {
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int pb = 0; pb < MBP; ++pb) {
+                                const int p = ph * PW + G_::pcol(pb, r16), n = nb * 16 + 4 * q;
+                                const size_t o = ((((size_t)b * K + slot) * H + h) * P + p) * N + n;
+                                const f32x4 sv = load_state4(a.states, a.state_dtype, o);
+                                f32x4 snew = load_state4(a.states, a.state_dtype, o + (size_t)H * P * N);
+                                se.apply(a, h, p, n, P, N, sv, snew);
+                            }
+                    }
+                }
+            }
         }
         wait_vm_all();
         __syncthreads();
@@ -682,6 +815,37 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             const float ei = (varlen && sSeg[i] != 0) ? 0.f : __builtin_amdgcn_exp2f(ai2);
 #pragma unroll
             for (int pb = 0; pb < MBP; ++pb) accY[pb] *= ei;
+            if constexpr (VL == 2) {
+                if (a.seqstates && a.seq_h0) {
+                    // the sequences that start in these 16 rows enter with their initial states:
+                    // + exp(acs_i - acs_{s-1}) C_i . h0_q for row i of the segment starting at s
+                    const int klo = sSeg[ib * 16] > 1 ? sSeg[ib * 16] : 1, khi = sSeg[ib * 16 + 15];
+                    for (int k = klo; k <= khi; ++k) {
+                        const int s = seg_first(sSeg, Q, k);
+                        const int qs = seq_at(a, b, tok0 + s);
+                        if (qs < 0 || qs >= a.nseq) continue;
+                        f32x4 tmp[MBP];
+#pragma unroll
+                        for (int pb = 0; pb < MBP; ++pb) tmp[pb] = vzero<f32x4>();
+#pragma unroll
+                        for (int ks = 0; ks < N / 32; ++ks) {
+                            const v4 lo = *(const v4*)(sBC + clo[ks] + ib * 16 * N);
+                            const v4 hi = *(const v4*)(sBC + chi[ks] + ib * 16 * N);
+                            const frag cf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                            for (int pb = 0; pb < MBP; ++pb) {
+                                const int p = ph * PW + G_::pcol(pb, r16);
+                                const f32x4 h_lo = load_state4(a.seq_h0, a.state_dtype, seq_state_off(a, qs, h, p, ks * 32 + 4 * q, P, N));
+                                const f32x4 h_hi = load_state4(a.seq_h0, a.state_dtype, seq_state_off(a, qs, h, p, ks * 32 + 16 + 4 * q, P, N));
+                                tmp[pb] = TT<T>::mma(pack8<T>(h_lo, h_hi), cf, tmp[pb]);
+                            }
+                        }
+                        const float fi = sSeg[i] == k ? __builtin_amdgcn_exp2f(ai2 - (s > 0 ? a2_h[s - 1] : 0.f)) : 0.f;
+#pragma unroll
+                        for (int pb = 0; pb < MBP; ++pb) accY[pb] += tmp[pb] * fi;
+                    }
+                }
+            }
             const int kd = ib >> 1;  // the diagonal 32-column block of these 16 rows
             if constexpr (G_::L_LDS) {
                 // L^T operand straight from the bands: lane (r16, q) takes L[i][32kk + 8q .. +7]

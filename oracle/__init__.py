@@ -10,6 +10,7 @@ imports, links or calls it, and it shares no code with the HIP library.
 * ``decode_step`` -- one token of the recurrence on a cached state (the decode step).
 * ``recurrence_varlen`` -- packed variable-length input: the recurrence restarted at every
   sequence start.
+* ``recurrence_varlen_states`` -- packed input with per-sequence initial and final states.
 
 Inputs may be torch CPU tensors or numpy arrays; 16-bit tensors are passed to C
 as their raw bits and widened exactly there.
@@ -239,3 +240,29 @@ def widen(t):
     out = np.empty(n)
     _load().ssd_oracle_widen(ctypes.c_void_p(ptr), code, n, _dptr(out))
     return out.reshape(tuple(t.shape))
+
+
+def recurrence_varlen_states(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, seq_idx=None, nseq=0,
+                             initial_states=None):
+    """Packed sequences with a state per sequence ("Mamba-2炸裂升级！…", section "与vLLM的深度融合":
+    variable-length sequences and initial states without padding).  A sequence starts at t = 0
+    of every row and wherever seq_idx changes; seq_idx[b, t] in [0, nseq) is its number.
+    Sequence q runs the recurrence from initial_states[q] (or zero) over its tokens;
+    final_states[q] is its state after its last token.  Returns y[B, L, H, P] and
+    final_states[nseq, H, P, N] in fp64 (NaN for numbers no run uses)."""
+    Bt, L, H, P = (int(s) for s in x.shape)
+    N = int(B.shape[3])
+    sidx = np.asarray(seq_idx.cpu() if hasattr(seq_idx, "cpu") else seq_idx)
+    y = np.empty((Bt, L, H, P))
+    fin = np.full((int(nseq), H, P, N), np.nan)
+    for b in range(Bt):
+        starts = [0] + [t for t in range(1, L) if sidx[b, t] != sidx[b, t - 1]] + [L]
+        for k in range(len(starts) - 1):
+            t0, t1 = starts[k], starts[k + 1]
+            q = int(sidx[b, t0])
+            part = lambda t: None if t is None else t[b:b + 1, t0:t1].contiguous()  # noqa: E731
+            init = initial_states[q:q + 1] if initial_states is not None else None
+            yk, fk = recurrence_full(part(x), part(dt), A, part(B), part(C), D, dt_bias, init, dt_softplus)
+            y[b, t0:t1] = yk[0]
+            fin[q] = fk[0]
+    return y, fin

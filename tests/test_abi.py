@@ -352,3 +352,21 @@ def test_noalloc_refuses_a_problem_larger_than_the_scratch(lib):
     assert ssd.STATUS_NAMES[rc] == "SSD_ERR_SCRATCH_TOO_SMALL"
     assert lib.ssd_prefill_noalloc(ctypes.byref(base(headdim=48)), fake, fake, fake, fake, fake, None, None, None,
                                    fake, fake, None) == UNSUP
+
+
+def test_varlen_states_validates_before_launch(lib):
+    """ssd_prefill_varlen_states refuses fp32 inputs, nseq < 1 and missing or misaligned state
+    arrays before any HIP call (fake pointers, no GPU needed)."""
+    p = base()
+    f = ctypes.c_void_p(FAKE)
+
+    def call(prm, nseq=3, seq=FAKE, h0=FAKE, fin=FAKE):
+        return lib.ssd_prefill_varlen_states(ctypes.byref(prm), f, f, f, f, f, None, None, ctypes.c_void_p(seq) if seq else None,
+                                             nseq, ctypes.c_void_p(h0) if h0 else None, f,
+                                             ctypes.c_void_p(fin) if fin else None, f, ssd.workspace_size(prm), None)
+    assert call(base(in_dtype="f32")) == UNSUP
+    assert call(p, nseq=0) == SHAPE
+    assert call(p, fin=0) == NULLP
+    assert call(p, seq=0) == NULLP
+    assert call(p, h0=FAKE + 8) == MISAL
+    assert call(p, fin=FAKE + 8) == MISAL

@@ -397,3 +397,53 @@ def test_varlen_ids_only_matter_where_they_change(oracle_mod):
     ya, fa = oracle_mod.recurrence_varlen(**inp.args(), seq_idx=a)
     yb, fb = oracle_mod.recurrence_varlen(**inp.args(), seq_idx=b)
     assert np.array_equal(ya, yb) and np.array_equal(fa, fb)
+
+
+def test_varlen_states_match_closed_form_sums(oracle_mod):
+    """Per-sequence initial and final states, against the sums written out in numpy: for
+    sequence q = tokens [s, e] of a row, with h0 = initial_states[q],
+      y_i     = sum_{s <= j <= i} (C_i . B_j) exp(sum_{j < k <= i} dA_k) dt_j x_j
+                + exp(sum_{s <= k <= i} dA_k) (h0 C_i) + D x_i,
+      final_q = sum_{s <= j <= e} exp(sum_{j < k <= e} dA_k) dt_j x_j (outer) B_j
+                + exp(sum_{s <= k <= e} dA_k) h0.
+    A row's first token starts a sequence too, so no state crosses rows."""
+    import torch
+    inp = small(seed=24, Bt=2, L=26, H=4, P=3, N=5, G=2, dt_scale=2.0)
+    seq = np.array([[4] * 6 + [0] * 1 + [2] * 9 + [1] * 10,
+                    [3] * 11 + [5] * 15], dtype=np.int32)
+    nseq = 7  # number 6 labels no run
+    g0 = torch.Generator().manual_seed(5)
+    h0s = 0.3 * torch.randn(nseq, 4, 3, 5, generator=g0, dtype=torch.float64).float()
+    args = {k: v for k, v in inp.args().items() if k != "h0"}
+    y, fin = oracle_mod.recurrence_varlen_states(**args, seq_idx=seq, nseq=nseq, initial_states=h0s)
+    x, dtr, A, Bm, Cm, D, bias = (f64(t) for t in (inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.dt_bias))
+    H0 = h0s.double().numpy()
+    L, H = 26, 4
+    yref = np.zeros_like(y)
+    fref = np.full_like(fin, np.nan)
+    for b in range(2):
+        runs, t = [], 0
+        while t < L:
+            e = t
+            while e + 1 < L and seq[b, e + 1] == seq[b, t]:
+                e += 1
+            runs.append((t, e))
+            t = e + 1
+        for h in range(H):
+            g = h // 2
+            d = np.logaddexp(0.0, dtr[b, :, h] + bias[h])
+            cum = np.concatenate([[0.0], np.cumsum(d * A[h])])
+            for (s0, e0) in runs:
+                q = seq[b, s0]
+                for i in range(s0, e0 + 1):
+                    acc = D[h] * x[b, i, h] + np.exp(cum[i + 1] - cum[s0]) * (H0[q, h] @ Cm[b, i, g])
+                    for j in range(s0, i + 1):
+                        acc = acc + (Cm[b, i, g] @ Bm[b, j, g]) * np.exp(cum[i + 1] - cum[j + 1]) * d[j] * x[b, j, h]
+                    yref[b, i, h] = acc
+                F = np.exp(cum[e0 + 1] - cum[s0]) * H0[q, h]
+                for j in range(s0, e0 + 1):
+                    F = F + np.exp(cum[e0 + 1] - cum[j + 1]) * d[j] * np.outer(x[b, j, h], Bm[b, j, g])
+                fref[q, h] = F
+    assert rel_err(y, yref) < REL
+    assert np.all(np.isnan(fin[6])) and np.all(np.isnan(fref[6]))
+    assert rel_err(fin[:6], fref[:6]) < REL
