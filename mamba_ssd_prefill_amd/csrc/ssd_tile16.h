@@ -782,7 +782,9 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 xs[kk][pb] = pack8<T>(lo, hi);
             }
         }
-        const __amdgpu_buffer_rsrc_t cbr = make_rsrc(cbp, (uint32_t)(Q * Q * (cb16 ? 2 : 4)));
+        const uint32_t ces = cb16 ? 2u : 4u;
+        const __amdgpu_buffer_rsrc_t cbr = make_rsrc(cbp, (uint32_t)(Q * Q) * ces);
+        const __amdgpu_buffer_rsrc_t cbr2 = cb16 ? make_rsrc(cbp, 0u) : cbr;
         // y: written once and never read here, so non-temporal (nt) stores keep it from
         // pushing the state slots and CB out of the L2
         const __amdgpu_buffer_rsrc_t yr =
@@ -868,13 +870,11 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                         c1 = *(const f32x4*)(sCB + cb_off<Q, 4>(i, j0 + 4));
                     }
                 } else {
-                    if (cb16) {
-                        cb16_widen<T>(__builtin_bit_cast(frag, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0) * 2, 0, CB_AUX)),
-                                      c0, c1);
-                    } else {
-                        c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0) * 4, 0, CB_AUX));
-                        c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0 + 4) * 4, 0, CB_AUX));
-                    }
+                    // the same two loads for either CB type (16-bit: all 8 values in the first, the
+                    // second from an empty range), then the 16-bit values are widened
+                    c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0) * ces, 0, CB_AUX));
+                    c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr2, (uint32_t)(i * Q + j0 + 4) * 4, 0, CB_AUX));
+                    if (cb16) cb16_widen<T>(__builtin_bit_cast(frag, c0), c0, c1);
                 }
                 if (kk < kd) {
                     const float gx = __builtin_amdgcn_exp2f(ai2 - a2_h[kk * 32 + 31]);
