@@ -53,6 +53,11 @@ def build(force=True, verbose=False):
             print(text)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join("== %s ==\n%s" % f for f in failed))
+    # MFMA results read too early on some control-flow path (a compiler hazard gap): fail here
+    from . import mfma_hazards
+    bad = mfma_hazards.check_objects(objs)
+    if bad:
+        raise RuntimeError("MFMA results read too early:\n" + "\n".join(bad[:40]))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)

@@ -153,46 +153,56 @@ template <typename T> __device__ inline typename TT<T>::frag pack8(f32x4 lo, f32
 // a 16-byte piece holds 16 / ES elements, so a band row of 32 (band + 1) columns is
 // 32 (band + 1) ES / 16 pieces plus one of padding.
 template <int ES> __host__ __device__ constexpr int cb_pitch(int band) { return 32 * (band + 1) * ES / 16 + 1; }
-template <int Q, int ES> __device__ constexpr int cb_band_base(int band) {
-    int t = 0;
-    for (int r = 0; r < band; ++r) t += ((32 * cb_pitch<ES>(r) + 63) / 64) * 64;
-    return t;
-}
-template <int Q, int AUX, int ES> __device__ inline void dma_cb_bands(float* lds, const float* cb) {
+// es is a run-time value: one copy loop for both CB types, so no control flow on the type
+// sits next to the MFMAs whose accumulators are read around it (see cb_widen_sel).
+template <int Q, int AUX> __device__ inline void dma_cb_bands(float* lds, const float* cb, int es) {
     const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(cb, (uint32_t)(Q * Q * ES));
-    constexpr int EPP = 16 / ES;  // elements per piece
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(cb, (uint32_t)(Q * Q * es));
+    const int epp = 16 / es;  // elements per piece
     int base = 0;  // pieces
 #pragma unroll
     for (int band = 0; band < Q / 32; ++band) {
-        const int pitch = cb_pitch<ES>(band);
+        const int pitch = 32 * (band + 1) * es / 16 + 1;
         const int used = 32 * pitch;
         const int ninst = (used + 63) / 64;
         for (int k = wave; k < ninst; k += 4) {
             const int f = k * 64 + lane;  // piece index inside the band
             const int row = f / pitch, pc = f - row * pitch;
             const bool ok = f < used && pc < pitch - 1;
-            const uint32_t voff = ok ? (uint32_t)(((32 * band + row) * Q + EPP * pc) * ES) : 0x40000000u;  // past num_records: reads as zeros
+            const uint32_t voff = ok ? (uint32_t)(((32 * band + row) * Q + epp * pc) * es) : 0x40000000u;  // past num_records: reads as zeros
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SSD_LDS(void, (char*)lds + (base + k * 64) * 16), 16, voff, 0, 0, AUX);
         }
         base += ((used + 63) / 64) * 64;
     }
 }
 
-// Offset (in elements of size ES) of CB[i][j] in the banded LDS copy.
-template <int Q, int ES> __device__ inline int cb_off(int i, int j) {
-    const int band = i >> 5;
-    int base = 0;
+// Byte offset of CB[i][j] in the banded LDS copy, i in band `band` (a compile-time value where
+// the caller unrolls its row blocks), for either CB type: the band's base and pitch for both
+// element sizes are constants, so the type only selects between scalars (no control flow).
+template <int Q> __device__ inline int cb_byte_off(int band, int i, int j, bool cb16) {
+    int base2 = 0, base4 = 0;  // pieces before the band
 #pragma unroll
     for (int r = 0; r < Q / 32; ++r)
-        if (r < band) base += ((32 * cb_pitch<ES>(r) + 63) / 64) * 64;
-    return (base + (i & 31) * cb_pitch<ES>(band)) * (16 / ES) + j;
+        if (r < band) {
+            base2 += ((32 * cb_pitch<2>(r) + 63) / 64) * 64;
+            base4 += ((32 * cb_pitch<4>(r) + 63) / 64) * 64;
+        }
+    const int base = cb16 ? base2 : base4, pitch = cb16 ? cb_pitch<2>(band) : cb_pitch<4>(band);
+    return (base + (i & 31) * pitch) * 16 + j * (cb16 ? 2 : 4);
 }
 
-// 8 consecutive CB values at element offset `off` of a 16-bit CB: one 16-byte read, widened.
-template <typename T> __device__ inline void cb16_widen(typename TT<T>::frag v, f32x4& lo, f32x4& hi) {
-    lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-    hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+// 8 consecutive CB values as two fp32 vectors, from either CB type: fp32 CB arrives as (lo, hi);
+// 16-bit CB arrives with all 8 values in lo, which are then widened.  Both results are formed
+// and one is selected, without a branch: the compiler let a uniform branch on the CB type sit
+// between a row block's MFMAs and the VALU reads of their accumulators, and on the short side
+// of it those reads came fewer wait states after the MFMAs than the hardware needs (stale
+// accumulator values).
+template <typename T> __device__ inline void cb_widen_sel(bool cb16, f32x4& lo, f32x4& hi) {
+    const typename TT<T>::frag v = __builtin_bit_cast(typename TT<T>::frag, lo);
+    const f32x4 wl = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    const f32x4 wh = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+    lo = cb16 ? wl : lo;
+    hi = cb16 ? wh : hi;
 }
 
 // Piece offset (16-byte units) of L_h[i][8 jp .. 8 jp + 7] inside one head's bands.
@@ -288,14 +298,12 @@ template <typename T, typename G_, int AUX> struct LBuild {
 
     __device__ inline void store(T* sL, const float* sA2, const float* sF, const float* sDt, const int* sSeg,
                                  bool varlen, bool cb16, int nvh, int tid) {
-        if (cb16) {
-            // widen in place (here, not in load(), so the loads stay in flight until now): the 8
-            // 16-bit values of each item into its two fp32 vectors
+        // widen in place (here, not in load(), so the loads stay in flight until now): with 16-bit
+        // CB the 8 values of each item into its two fp32 vectors
 #pragma unroll
-            for (int it = 0; it < FI; ++it) cb16_widen<T>(__builtin_bit_cast(frag, cf[it][0]), cf[it][0], cf[it][1]);
+        for (int it = 0; it < FI; ++it) cb_widen_sel<T>(cb16, cf[it][0], cf[it][1]);
 #pragma unroll
-            for (int it = 0; it < DI; ++it) cb16_widen<T>(__builtin_bit_cast(frag, cd[it][0]), cd[it][0], cd[it][1]);
-        }
+        for (int it = 0; it < DI; ++it) cb_widen_sel<T>(cb16, cd[it][0], cd[it][1]);
 #pragma unroll
         for (int it = 0; it < FI; ++it) {
             const int k = tid + it * 256;
@@ -615,10 +623,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             if constexpr (G_::L_LDS) {
                 lb.load(cbp, tid, cb16);
             } else if constexpr (CB_LDS) {
-                if (cb16)
-                    dma_cb_bands<Q, CB_AUX, 2>(sCB, cbp);
-                else
-                    dma_cb_bands<Q, CB_AUX, 4>(sCB, cbp);
+                dma_cb_bands<Q, CB_AUX>(sCB, cbp, cb16 ? 2 : 4);
             }
             hook.claim();
             if (a.relay && hook.relay_live()) {
@@ -668,10 +673,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         if constexpr (G_::L_LDS) {
             lb.load(cbp, tid, cb16);
         } else if constexpr (CB_LDS) {
-            if (cb16)
-                dma_cb_bands<Q, 0, 2>(sCB, cbp);
-            else
-                dma_cb_bands<Q, 0, 4>(sCB, cbp);
+            dma_cb_bands<Q, 0>(sCB, cbp, cb16 ? 2 : 4);
         }
         if (hvalid) {
             const int K = a.slots, slot = c % K;
@@ -863,18 +865,23 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                 const int j0 = kk * 32 + 8 * q;
                 f32x4 c0, c1;
                 if constexpr (CB_LDS) {
-                    if (cb16) {
-                        cb16_widen<T>(*(const frag*)((const T*)sCB + cb_off<Q, 2>(i, j0)), c0, c1);
-                    } else {
-                        c0 = *(const f32x4*)(sCB + cb_off<Q, 4>(i, j0));
-                        c1 = *(const f32x4*)(sCB + cb_off<Q, 4>(i, j0 + 4));
-                    }
+                    // two 16-byte reads for either CB type at offsets selected before them (16-bit:
+                    // the first holds all 8 values, the second reads the next piece of the band
+                    // row, at most its padding piece, and is not used), then the 16-bit values are
+                    // widened.  Control flow on the CB type here (a branch, or a second read that
+                    // the compiler may skip when it repeats the first) lands between this row
+                    // block's MFMAs and the reads of their accumulators; see cb_widen_sel.
+                    const int o0 = cb_byte_off<Q>(ib >> 1, i, j0, cb16);
+                    c0 = *(const f32x4*)((const char*)sCB + o0);
+                    c1 = *(const f32x4*)((const char*)sCB + o0 + 16);
+                    cb_widen_sel<T>(cb16, c0, c1);
                 } else {
                     // the same two loads for either CB type (16-bit: all 8 values in the first, the
-                    // second from an empty range), then the 16-bit values are widened
+                    // second from an empty range), then the 16-bit values are widened; no control
+                    // flow on the CB type (see cb_widen_sel)
                     c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr, (uint32_t)(i * Q + j0) * ces, 0, CB_AUX));
                     c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cbr2, (uint32_t)(i * Q + j0 + 4) * 4, 0, CB_AUX));
-                    if (cb16) cb16_widen<T>(__builtin_bit_cast(frag, c0), c0, c1);
+                    cb_widen_sel<T>(cb16, c0, c1);
                 }
                 if (kk < kd) {
                     const float gx = __builtin_amdgcn_exp2f(ai2 - a2_h[kk * 32 + 31]);
