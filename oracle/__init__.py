@@ -11,6 +11,8 @@ imports, links or calls it, and it shares no code with the HIP library.
 * ``recurrence_varlen`` -- packed variable-length input: the recurrence restarted at every
   sequence start.
 * ``recurrence_varlen_states`` -- packed input with per-sequence initial and final states.
+* ``conv_silu``, ``gated_rmsnorm``, ``block`` -- the convolution before and the norm after
+  the SSD, and the three composed.
 
 Inputs may be torch CPU tensors or numpy arrays; 16-bit tensors are passed to C
 as their raw bits and widened exactly there.
@@ -266,3 +268,80 @@ def recurrence_varlen_states(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=T
             y[b, t0:t1] = yk[0]
             fin[q] = fk[0]
     return y, fin
+
+
+def _f64(a):
+    """Exact fp64 values of a torch tensor / numpy array (16-bit types decoded by ``widen``)."""
+    if a is None:
+        return None
+    if hasattr(a, "cpu"):  # torch tensor
+        import torch
+        if a.dtype in (torch.float16, torch.bfloat16):
+            return widen(a)
+        return a.detach().cpu().to(torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def conv_silu(xbc, conv_w, conv_b=None, conv_state=None):
+    """The causal depthwise convolution before the SSD, then SiLU ("Mamba-2炸裂升级！…", section
+    "Mamba-2核心操作与融合的必要性": the depthwise convolution mixes the last few tokens; section
+    "未来展望与应用拓展": the convolution before the SSD).  Per channel ch and token t, with K the
+    width (conv_w [Ch, K]):
+
+        v[b,t,ch]   = conv_b[ch] + sum_k conv_w[ch,k] * in[b, t-(K-1)+k, ch]
+        out[b,t,ch] = v / (1 + exp(-v))
+
+    where in[b, t<0, ch] = conv_state[b, ch, t+K-1] (the K-1 inputs before token 0, the decode
+    cache's conv state of "Mamba-2状态空间模型的编译器优化与实现", section 2.2), zeros when
+    conv_state is None.  xbc [B, L, Ch]; returns fp64 [B, L, Ch]."""
+    x = _f64(xbc)
+    w = _f64(conv_w)
+    Bt, L, Ch = x.shape
+    K = w.shape[1]
+    prev = np.zeros((Bt, K - 1, Ch)) if conv_state is None else np.transpose(_f64(conv_state), (0, 2, 1))
+    full = np.concatenate([prev, x], axis=1)  # token t of the input is row t + K - 1
+    v = np.zeros((Bt, L, Ch)) if conv_b is None else np.broadcast_to(_f64(conv_b), (Bt, L, Ch)).copy()
+    for k in range(K):
+        v += w[:, k] * full[:, k:k + L, :]
+    return v / (1.0 + np.exp(-v))
+
+
+def gated_rmsnorm(y, z, norm_w, eps, ngroups):
+    """The norm after the SSD ("Mamba-2炸裂升级！…", section "未来展望与应用拓展"), read as Mamba-2's
+    gated RMS norm: g = y * silu(z) over the H*P channels of a token, normalised over each of
+    ngroups contiguous channel groups, scaled per channel:
+
+        out[b,t,c] = g[b,t,c] / sqrt(mean_{c' in group(c)} g[b,t,c']^2 + eps) * norm_w[c]
+
+    y, z [B, L, H*P] (or [B, L, H, P]); returns fp64 [B, L, H*P]."""
+    yv = _f64(y)
+    Bt, L = yv.shape[:2]
+    yv = yv.reshape(Bt, L, -1)
+    zv = _f64(z).reshape(Bt, L, -1)
+    C = yv.shape[2]
+    g = yv * (zv / (1.0 + np.exp(-zv)))
+    gg = g.reshape(Bt, L, ngroups, C // ngroups)
+    ms = np.mean(gg * gg, axis=3, keepdims=True)
+    return (gg / np.sqrt(ms + eps)).reshape(Bt, L, C) * _f64(norm_w)
+
+
+def block(xbc, conv_w, conv_b, conv_state, dt, A, D, dt_bias, z, norm_w, eps, nheads, headdim, ngroups, dstate,
+          h0=None, dt_softplus=True, in_dtype=None):
+    """The SSD with the convolution before it and the norm after it (the fusion the same section
+    describes): conv_silu over xBC = [x | B | C] (channels h*P + p, then H*P + g*N + n, then
+    H*P + G*N + g*N + n), the conv output rounded to the input dtype (the SSD's operands are in
+    that dtype), the recurrence, then gated_rmsnorm with one norm group per B/C group.
+    Returns (out [B, L, H*P], y [B, L, H, P], final [B, H, P, N]) in fp64."""
+    import torch
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    xc = conv_silu(xbc, conv_w, conv_b, conv_state)
+    Bt, L, _ = xc.shape
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[in_dtype or _dtype_name(xbc)]
+    xr = torch.from_numpy(xc).to(torch.float32).to(tdt)  # rounded as a kernel writing fp32 results would
+    HP = H * P
+    x = xr[..., :HP].reshape(Bt, L, H, P).contiguous()
+    Bm = xr[..., HP:HP + G * N].reshape(Bt, L, G, N).contiguous()
+    Cm = xr[..., HP + G * N:HP + 2 * G * N].reshape(Bt, L, G, N).contiguous()
+    y, fin = recurrence_full(x, dt, A, Bm, Cm, D, dt_bias, h0, dt_softplus)
+    out = gated_rmsnorm(y, z, norm_w, eps, G)
+    return out, y, fin

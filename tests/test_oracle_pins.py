@@ -447,3 +447,138 @@ def test_varlen_states_match_closed_form_sums(oracle_mod):
     assert rel_err(y, yref) < REL
     assert np.all(np.isnan(fin[6])) and np.all(np.isnan(fref[6]))
     assert rel_err(fin[:6], fref[:6]) < REL
+
+
+# ---- the convolution before and the norm after the SSD ("Mamba-2炸裂升级！…", section
+# "未来展望与应用拓展"; the depthwise convolution of section "Mamba-2核心操作与融合的必要性") ----
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def test_conv_silu_equals_numpy_convolve_per_channel(oracle_mod):
+    gen = torch.Generator().manual_seed(71)
+    Bt, L, Ch, K = 2, 13, 6, 4
+    x = torch.randn(Bt, L, Ch, generator=gen)
+    w = torch.randn(Ch, K, generator=gen)
+    bias = torch.randn(Ch, generator=gen)
+    st = torch.randn(Bt, Ch, K - 1, generator=gen)
+    out = oracle_mod.conv_silu(x, w, bias, st)
+    X, W, Bv, S = (t.double().numpy() for t in (x, w, bias, st))
+    for b in range(Bt):
+        for ch in range(Ch):
+            seq = np.concatenate([S[b, ch], X[b, :, ch]])
+            # numpy's convolve flips its second argument: correlation with the taps = convolve
+            # with the reversed taps; 'valid' keeps the L outputs that see K inputs
+            v = np.convolve(seq, W[ch, ::-1], mode="valid") + Bv[ch]
+            assert np.allclose(out[b, :, ch], _silu(v), rtol=1e-13, atol=1e-13)
+
+
+def test_conv_impulse_response_and_zero_state(oracle_mod):
+    Ch, K, L = 3, 4, 9
+    w = torch.arange(1.0, Ch * K + 1).reshape(Ch, K) / 10
+    x = torch.zeros(1, L, Ch)
+    x[0, 2, :] = 1.0
+    out = oracle_mod.conv_silu(x, w)
+    for ch in range(Ch):
+        for t in range(L):
+            k = t - 2  # the impulse at token 2 reaches token t through tap K-1-k
+            v = float(w[ch, K - 1 - k]) if 0 <= k < K else 0.0
+            assert out[0, t, ch] == pytest.approx(_silu(v), abs=1e-15)
+
+
+def test_conv_state_carries_across_a_split(oracle_mod):
+    gen = torch.Generator().manual_seed(72)
+    Bt, L, Ch, K = 2, 20, 5, 4
+    x = torch.randn(Bt, L, Ch, generator=gen)
+    w = torch.randn(Ch, K, generator=gen)
+    bias = torch.randn(Ch, generator=gen)
+    whole = oracle_mod.conv_silu(x, w, bias)
+    s = 7
+    tail = x[:, s - (K - 1):s, :].permute(0, 2, 1).contiguous()  # [B, Ch, K-1]: the state after token s-1
+    second = oracle_mod.conv_silu(x[:, s:], w, bias, tail)
+    assert np.allclose(second, whole[:, s:], rtol=1e-14, atol=1e-14)
+
+
+def test_gated_rmsnorm_against_torch_rms_norm(oracle_mod):
+    gen = torch.Generator().manual_seed(73)
+    Bt, L, C, G = 2, 5, 24, 3
+    y = torch.randn(Bt, L, C, generator=gen, dtype=torch.float64)
+    z = torch.randn(Bt, L, C, generator=gen, dtype=torch.float64)
+    w = torch.randn(C, generator=gen, dtype=torch.float64)
+    eps = 1e-5
+    out = oracle_mod.gated_rmsnorm(y, z, w, eps, G)
+    g = (y * torch.nn.functional.silu(z)).reshape(Bt, L, G, C // G)
+    ref = torch.nn.functional.rms_norm(g, (C // G,), None, eps).reshape(Bt, L, C) * w
+    assert np.allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_gated_rmsnorm_closed_forms(oracle_mod):
+    gen = torch.Generator().manual_seed(74)
+    Bt, L, C, G = 1, 4, 16, 2
+    y = torch.randn(Bt, L, C, generator=gen, dtype=torch.float64)
+    z = torch.randn(Bt, L, C, generator=gen, dtype=torch.float64)
+    ones = torch.ones(C, dtype=torch.float64)
+    eps = 1e-3
+    out = oracle_mod.gated_rmsnorm(y, z, ones, eps, G).reshape(Bt, L, G, C // G)
+    g = (y.numpy() * _silu(z.numpy())).reshape(Bt, L, G, C // G)
+    ms = np.mean(g * g, axis=3)
+    # the mean square of the output of a group is ms / (ms + eps)
+    assert np.allclose(np.mean(out * out, axis=3), ms / (ms + eps), rtol=1e-12)
+    # without eps the result does not depend on the scale of y
+    a = oracle_mod.gated_rmsnorm(y, z, ones, 0.0, G)
+    b = oracle_mod.gated_rmsnorm(3.5 * y, z, ones, 0.0, G)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+    # a zero gate gives zero
+    assert np.all(oracle_mod.gated_rmsnorm(y, torch.zeros_like(z), ones, eps, G) == 0.0)
+
+
+def test_block_carries_conv_and_ssm_state_across_a_split(oracle_mod):
+    """One call over L tokens = a call over the first s tokens, then a call over the rest with the
+    first call's last K-1 raw inputs as the conv state and its final state as h0."""
+    H, P, G, N, K = 4, 8, 2, 8, 4
+    Bt, L, s = 2, 30, 11
+    gen = torch.Generator().manual_seed(75)
+    Ch = H * P + 2 * G * N
+    xbc = torch.randn(Bt, L, Ch, generator=gen).to(torch.bfloat16)
+    w = (0.5 * torch.randn(Ch, K, generator=gen))
+    cb = 0.1 * torch.randn(Ch, generator=gen)
+    inp = make_inputs(Bt, L, H, P, N, G, dtype="bf16", state_dtype="f32", has_h0=True, seed=76)
+    z = torch.randn(Bt, L, H * P, generator=gen).to(torch.bfloat16)
+    nw = 1.0 + 0.1 * torch.randn(H * P, generator=gen)
+    kw = dict(nheads=H, headdim=P, ngroups=G, dstate=N, in_dtype="bf16")
+    out, y, fin = oracle_mod.block(xbc, w, cb, None, inp.dt, inp.A, inp.D, inp.dt_bias, z, nw, 1e-5, h0=inp.h0, **kw)
+    o1, y1, f1 = oracle_mod.block(xbc[:, :s], w, cb, None, inp.dt[:, :s], inp.A, inp.D, inp.dt_bias, z[:, :s], nw, 1e-5,
+                              h0=inp.h0, **kw)
+    st = xbc[:, s - (K - 1):s].permute(0, 2, 1).contiguous()
+    o2, y2, f2 = oracle_mod.block(xbc[:, s:].contiguous(), w, cb, st, inp.dt[:, s:].contiguous(), inp.A, inp.D, inp.dt_bias,
+                              z[:, s:].contiguous(), nw, 1e-5, h0=torch.from_numpy(f1).float(), **kw)
+    assert rel_err(np.concatenate([y1, y2], axis=1), y) < 1e-6
+    assert rel_err(np.concatenate([o1, o2], axis=1), out) < 1e-6
+    assert rel_err(f2, fin) < 1e-6
+
+
+def test_block_channel_layout_x_then_b_then_c(oracle_mod):
+    """xBC = [x | B | C] along channels: with the B channels' inputs and bias zero, B = silu(0) = 0,
+    so nothing enters the state (final state 0, y = D x); with the C channels zero instead, y is
+    still D x but the state fills."""
+    H, P, G, N, K = 2, 8, 1, 8, 4
+    Bt, L = 1, 12
+    HP, GN = H * P, G * N
+    gen = torch.Generator().manual_seed(77)
+    xbc = torch.randn(Bt, L, HP + 2 * GN, generator=gen)
+    w = 0.5 * torch.randn(HP + 2 * GN, K, generator=gen)
+    cb = 0.1 * torch.randn(HP + 2 * GN, generator=gen)
+    inp = make_inputs(Bt, L, H, P, N, G, dtype="f32", state_dtype="f32", has_h0=False, seed=78)
+    z = torch.randn(Bt, L, HP, generator=gen)
+    nw = torch.ones(HP)
+    kw = dict(nheads=H, headdim=P, ngroups=G, dstate=N, in_dtype="f32")
+    xconv = oracle_mod.conv_silu(xbc, w, cb)[..., :HP].astype(np.float32).astype(np.float64)
+    dx = inp.D.double().numpy()[None, None, :, None] * xconv.reshape(Bt, L, H, P)
+    for part, state_fills in ((slice(HP, HP + GN), False), (slice(HP + GN, HP + 2 * GN), True)):
+        xb, c2 = xbc.clone(), cb.clone()
+        xb[..., part] = 0.0
+        c2[part] = 0.0
+        out, y, fin = oracle_mod.block(xb, w, c2, None, inp.dt, inp.A, inp.D, inp.dt_bias, z, nw, 1e-5, **kw)
+        assert np.allclose(y, dx, rtol=1e-12, atol=1e-12)
+        assert (np.max(np.abs(fin)) > 1e-3) == state_fills
