@@ -342,6 +342,57 @@ ssd_status_t ssd_decode_step(const ssd_params_t* p,
                              const float* D, const float* dt_bias,
                              const void* state_in, void* state_out, void* y, void* stream);
 
+/* ---- The Mamba-2 block around the SSD ------------------------------------------------------
+ * The operations just before and after the SSD in a Mamba-2 block ("Mamba-2炸裂升级！…", section
+ * "Mamba-2核心操作与融合的必要性": the depthwise convolution over the last few tokens; section
+ * "未来展望与应用拓展": fusing the convolution before and the norm after the SSD into its launch,
+ * each saving a full write and read of an activation).  16-bit inputs only (fp32:
+ * SSD_ERR_UNSUPPORTED).  With Ch = H*P + 2*G*N channels:
+ *   xbc        [B, L, Ch]    in_dtype  required, 16-byte aligned: the SSD's inputs before the
+ *                                      convolution, channels [x (h*P + p) | B (g*N + n) | C (g*N + n)]
+ *   conv_w     [Ch, 4]       fp32      required, 16-byte aligned: the taps of the causal depthwise
+ *                                      convolution of width 4
+ *   conv_b     [Ch]          fp32      NULL means 0
+ *   conv_state [B, Ch, 3]    in_dtype  NULL means 0: the 3 inputs before token 0 (a decode
+ *                                      cache's convolution state)
+ * and the convolution is x, B, C = silu(conv_b + sum_k conv_w[:, k] * xbc[t - 3 + k]), rounded to
+ * in_dtype.  The norm after the SSD is Mamba-2's gated RMS norm with one group per B/C group:
+ *   z          [B, L, H*P]   in_dtype  required, 16-byte aligned
+ *   norm_w     [H*P]         fp32      required, 16-byte aligned
+ *   out[b,t,c] = g / sqrt(mean over the H/G*P channels of c's group of g^2 + norm_eps) * norm_w[c],
+ *                g = y[b,t,c] * silu(z[b,t,c]);  norm_eps >= 0 (else SSD_ERR_INVALID_ARGUMENT).
+ */
+
+/* The convolution alone: xbc -> x [B, L, H, P], B and C [B, L, G, N] (16-byte aligned). */
+ssd_status_t ssd_conv_silu(const ssd_params_t* p, const void* xbc, const float* conv_w, const float* conv_b,
+                           const void* conv_state, void* x, void* B, void* C, void* stream);
+
+/* The gated norm alone: y, z -> out, all [B, L, H*P] in_dtype (16-byte aligned). */
+ssd_status_t ssd_gated_norm(const ssd_params_t* p, const void* y, const void* z, const float* norm_w,
+                            float norm_eps, void* out, void* stream);
+
+/* Workspace bytes ssd_prefill_block needs (0 if *p is invalid or not 16-bit). */
+size_t ssd_prefill_block_workspace_size(const ssd_params_t* p);
+
+/* Convolution, SSD prefill and gated norm: out [B, L, H*P] and final_state [B, H, P, N] from xbc,
+ * dt, A, D, dt_bias, z, the initial state and the taps above (arguments as for ssd_prefill and
+ * the block section above; workspace 256-byte aligned, at least
+ * ssd_prefill_block_workspace_size() bytes).
+ *   SSD_IMPL_UNFUSED: the convolution kernel, the five SSD kernels and the norm kernel, with x,
+ *     B, C and y going through the workspace.
+ *   SSD_IMPL_FUSED: one launch (plus the boundary copies): the bmm tiles convolve B and C from
+ *     xbc, the chunk tiles convolve their x rows in LDS, and each chunk tile applies the norm to
+ *     its y rows once every tile of its (b, g) pair and chunk has added its share of the squared
+ *     sums -- when every pair's tiles fall in one work partition and fit on its XCD at once;
+ *     otherwise y goes through the workspace to the norm kernel.  headdim and dstate in
+ *     {64, 128} with H/G a multiple of the heads per tile (2 at headdim 64), else
+ *     SSD_ERR_UNSUPPORTED.  Test knob: MAMBA_SSD_BLOCK_NORM=0 sends y to the norm kernel. */
+ssd_status_t ssd_prefill_block(const ssd_params_t* p, const void* xbc, const float* conv_w, const float* conv_b,
+                               const void* conv_state, const void* dt, const float* A, const float* D,
+                               const float* dt_bias, const void* z, const float* norm_w, float norm_eps,
+                               const void* initial_state, void* out, void* final_state,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,7 @@ import os
 __all__ = ["ssd_prefill", "workspace_size", "workspace_layout", "Params", "SSDError", "library_path",
            "load_library", "step_chunk_cumsum", "step_bmm", "step_chunk_state", "step_state_passing",
            "step_chunk_scan", "check_device_status", "make_params", "ssd_decode_step", "ssd_prefill_noalloc",
-           "ssd_prefill_varlen_states",
+           "ssd_prefill_varlen_states", "conv_silu", "gated_norm", "ssd_prefill_block", "block_workspace_size",
            "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,8 @@ EXPORTED_SYMBOLS = ["ssd_prefill_workspace_size", "ssd_validate", "ssd_prefill",
                     "ssd_check_device_status",
                     "ssd_status_string", "ssd_workspace_layout", "ssd_step_chunk_cumsum", "ssd_step_bmm",
                     "ssd_step_chunk_state", "ssd_step_state_passing", "ssd_step_chunk_scan", "ssd_decode_step",
-                    "ssd_prefill_varlen", "ssd_prefill_noalloc", "ssd_prefill_varlen_states"]
+                    "ssd_prefill_varlen", "ssd_prefill_noalloc", "ssd_prefill_varlen_states", "ssd_conv_silu",
+                    "ssd_gated_norm", "ssd_prefill_block_workspace_size", "ssd_prefill_block"]
 
 
 class SSDError(RuntimeError):
@@ -106,8 +107,14 @@ def load_library():
     lib.ssd_prefill_noalloc.restype = ctypes.c_int
     lib.ssd_prefill_varlen_states.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, sz, vp]
     lib.ssd_prefill_varlen_states.restype = ctypes.c_int
+    fl = ctypes.c_float
+    lib.ssd_conv_silu.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_gated_norm.argtypes = [P, vp, vp, vp, fl, vp, vp]
+    lib.ssd_prefill_block_workspace_size.argtypes = [P]
+    lib.ssd_prefill_block_workspace_size.restype = sz
+    lib.ssd_prefill_block.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, fl, vp, vp, vp, vp, sz, vp]
     for f in ("ssd_step_chunk_cumsum", "ssd_step_bmm", "ssd_step_chunk_state", "ssd_step_state_passing",
-              "ssd_step_chunk_scan", "ssd_decode_step"):
+              "ssd_step_chunk_scan", "ssd_decode_step", "ssd_conv_silu", "ssd_gated_norm", "ssd_prefill_block"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -300,6 +307,82 @@ def ssd_prefill_noalloc(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None
                                               _ptr(dt_bias), _ptr(initial_state), _ptr(y), _ptr(final_state),
                                               _stream(x.device)), "ssd_prefill_noalloc")
     return y, final_state
+
+
+def _block_params(xbc, dt, nheads, headdim, ngroups, dstate, chunk_size, state_dtype, dt_softplus, impl):
+    import torch
+    Bt, L, ch = xbc.shape
+    if ch != nheads * headdim + 2 * ngroups * dstate:
+        raise ValueError("xbc has %d channels, expected H*P + 2*G*N = %d" % (ch, nheads * headdim + 2 * ngroups * dstate))
+    if tuple(dt.shape) != (Bt, L, nheads):
+        raise ValueError("dt must be [B, L, H]")
+    sd = {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[state_dtype]
+    return make_params(Bt, L, nheads, headdim, dstate, ngroups, chunk_size, _dtype_code(xbc), sd, dt_softplus, impl)
+
+
+def _device_contig(*ts):
+    for t in ts:
+        if t is not None and (t.device.type != "cuda" or not t.is_contiguous()):
+            raise ValueError("the block entry points need contiguous device tensors")
+
+
+def conv_silu(xbc, conv_w, conv_b=None, conv_state=None, *, nheads, headdim, ngroups, dstate):
+    """ssd_conv_silu: x [B, L, H, P], B and C [B, L, G, N] from xbc [B, L, H*P + 2*G*N]."""
+    import torch
+    _device_contig(xbc, conv_w, conv_b, conv_state)
+    Bt, L, _ = xbc.shape
+    prm = make_params(Bt, L, nheads, headdim, dstate, ngroups, 128, _dtype_code(xbc), SSD_F32, True, "unfused")
+    x = torch.empty((Bt, L, nheads, headdim), dtype=xbc.dtype, device=xbc.device)
+    Bm = torch.empty((Bt, L, ngroups, dstate), dtype=xbc.dtype, device=xbc.device)
+    Cm = torch.empty_like(Bm)
+    _check(load_library().ssd_conv_silu(ctypes.byref(prm), _ptr(xbc), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+                                        _ptr(x), _ptr(Bm), _ptr(Cm), _stream(xbc.device)), "ssd_conv_silu")
+    return x, Bm, Cm
+
+
+def gated_norm(y, z, norm_w, norm_eps, *, nheads, headdim, ngroups, out=None):
+    """ssd_gated_norm: out [B, L, H*P] = the gated RMS norm of y (y, z [B, L, H, P] or [B, L, H*P])."""
+    import torch
+    _device_contig(y, z, norm_w, out)
+    Bt, L = y.shape[:2]
+    hp = nheads * headdim
+    prm = make_params(Bt, L, nheads, headdim, 32, ngroups, 128, _dtype_code(y), SSD_F32, True, "unfused")
+    if out is None:
+        out = torch.empty((Bt, L, hp), dtype=y.dtype, device=y.device)
+    _check(load_library().ssd_gated_norm(ctypes.byref(prm), _ptr(y), _ptr(z), _ptr(norm_w), float(norm_eps), _ptr(out),
+                                         _stream(y.device)), "ssd_gated_norm")
+    return out
+
+
+def block_workspace_size(params):
+    n = load_library().ssd_prefill_block_workspace_size(ctypes.byref(params))
+    if n == 0:
+        raise SSDError(3, "ssd_prefill_block_workspace_size")
+    return n
+
+
+def ssd_prefill_block(xbc, conv_w, conv_b, conv_state, dt, A, D, dt_bias, z, norm_w, norm_eps, initial_state=None, *,
+                      nheads, headdim, ngroups, dstate, chunk_size=128, state_dtype=None, impl="fused",
+                      dt_softplus=True, workspace=None, out=None, final_state=None):
+    """ssd_prefill_block: the convolution, the SSD prefill and the gated norm.  Returns
+    (out [B, L, H*P], final_state [B, H, P, N])."""
+    import torch
+    _device_contig(xbc, conv_w, conv_b, conv_state, dt, A, D, dt_bias, z, norm_w, initial_state, out, final_state)
+    if state_dtype is None:
+        state_dtype = initial_state.dtype if initial_state is not None else torch.float32
+    prm = _block_params(xbc, dt, nheads, headdim, ngroups, dstate, chunk_size, state_dtype, dt_softplus, impl)
+    Bt, L, _ = xbc.shape
+    if out is None:
+        out = torch.empty((Bt, L, nheads * headdim), dtype=xbc.dtype, device=xbc.device)
+    if final_state is None:
+        final_state = torch.empty((Bt, nheads, headdim, dstate), dtype=state_dtype, device=xbc.device)
+    if workspace is None:
+        workspace = torch.empty(block_workspace_size(prm), dtype=torch.uint8, device=xbc.device)
+    _check(load_library().ssd_prefill_block(
+        ctypes.byref(prm), _ptr(xbc), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(dt), _ptr(A), _ptr(D),
+        _ptr(dt_bias), _ptr(z), _ptr(norm_w), float(norm_eps), _ptr(initial_state), _ptr(out), _ptr(final_state),
+        _ptr(workspace), workspace.numel(), _stream(xbc.device)), "ssd_prefill_block")
+    return out, final_state
 
 
 def check_device_status(params, workspace):

@@ -15,8 +15,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmamba_ssd.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = (["ssd_api.cpp", "ssd_noalloc.hip", "ssd_common.hip", "ssd_decode.hip", "ssd_kernels_f32.hip", "ssd_kernels_f32_vl.hip",
-            "ssd_kernels_f16.hip", "ssd_kernels_bf16.hip"]
+SOURCES = (["ssd_api.cpp", "ssd_noalloc.hip", "ssd_common.hip", "ssd_decode.hip", "ssd_block.hip", "ssd_kernels_f32.hip", "ssd_kernels_f32_vl.hip",
+            "ssd_kernels_f16.hip", "ssd_kernels_bf16.hip", "ssd_kernels_f16_blk.hip", "ssd_kernels_bf16_blk.hip"]
            + ["ssd_kernels_%s_q%d%s.hip" % (d, q, v) for d in ("f16", "bf16") for q in (64, 128, 256)
               for v in ("", "_vl")])
 

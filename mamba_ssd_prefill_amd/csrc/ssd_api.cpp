@@ -238,6 +238,7 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.agg16 = agg16(p);
     a.cb16 = cb16(p);
     a.spin_limit = spin_limit();
+    a.x_stride = p->nheads * p->headdim;
     return a;
 }
 
@@ -646,4 +647,179 @@ SSD_EXPORT ssd_status_t ssd_decode_step(const ssd_params_t* p, const void* x, co
     a.state_dtype = p->state_dtype;
     a.softplus = p->dt_softplus;
     return hip_status(ssd::launch_decode(a, p->in_dtype, (hipStream_t)stream));
+}
+
+// ---- the Mamba-2 block around the SSD: convolution before, gated norm after ----------------
+
+namespace {
+
+bool is16(const ssd_params_t* p) { return p->in_dtype == SSD_F16 || p->in_dtype == SSD_BF16; }
+
+// Workspace of ssd_prefill_block: the SSD's own layout, then (fused) the norm's per-token sums
+// and per-(b, c, g) tile counts appended to the sync words (so the copy-in launch clears them),
+// then the convolved B and C (and x for the unfused form) and y.
+struct BlockLayout {
+    Layout l;
+    size_t nsum_w, ncount_w, nsync_total;
+    size_t x_off, b_off, c_off, y_off, total;
+};
+
+BlockLayout block_layout(const ssd_params_t* p) {
+    BlockLayout k{};
+    k.l = layout(p);
+    const size_t B = p->batch, L = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups;
+    const size_t es = elem_size(p->in_dtype), nc = k.l.w.nchunks;
+    const bool fused = p->impl == SSD_IMPL_FUSED;
+    k.nsum_w = k.l.nsync;
+    k.ncount_w = k.nsum_w + (fused ? B * L * G : 0);
+    k.nsync_total = k.ncount_w + (fused ? B * nc * G : 0);
+    size_t off = align_up(k.l.w.sync_offset + 4 * k.nsync_total);
+    if (off < k.l.w.total_bytes) off = k.l.w.total_bytes;
+    k.x_off = off;
+    off = align_up(off + (fused ? 0 : B * L * H * P * es));
+    k.b_off = off;
+    off = align_up(off + B * L * G * N * es);
+    k.c_off = off;
+    off = align_up(off + B * L * G * N * es);
+    k.y_off = off;
+    off = align_up(off + B * L * H * P * es);
+    k.total = off;
+    return k;
+}
+
+ssd_status_t validate_block(const ssd_params_t* p) {
+    ssd_status_t s = validate(p);
+    if (s != SSD_OK) return s;
+    if (!is16(p)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+// The fused block form takes P, N in {64, 128} and tiles that never straddle two groups.
+bool block_fusable(const ssd_params_t* p) {
+    const int P = p->headdim, N = p->dstate;
+    if ((P != 64 && P != 128) || (N != 64 && N != 128)) return false;
+    return (p->nheads / p->ngroups) % ssd::heads_per_tile(P) == 0;
+}
+
+hipError_t launch_block(int step, const ssd_params_t* p, ssd::SsdArgs& a, hipStream_t st) {
+    if (p->in_dtype == SSD_F16) return ssd::launch_block_f16(step, p->headdim, p->dstate, p->chunk_size, a, st);
+    return ssd::launch_block_bf16(step, p->headdim, p->dstate, p->chunk_size, a, st);
+}
+
+}  // namespace
+
+SSD_EXPORT size_t ssd_prefill_block_workspace_size(const ssd_params_t* p) {
+    if (validate_block(p) != SSD_OK) return 0;
+    return block_layout(p).total;
+}
+
+SSD_EXPORT ssd_status_t ssd_conv_silu(const ssd_params_t* p, const void* xbc, const float* conv_w,
+                                      const float* conv_b, const void* conv_state, void* x, void* B, void* C,
+                                      void* stream) {
+    ssd_status_t s = validate_block(p);
+    if (s != SSD_OK) return s;
+    if (!xbc || !conv_w || !x || !B || !C) return SSD_ERR_NULL_POINTER;
+    if (!aligned(xbc, 16) || !aligned(conv_w, 16) || !aligned(conv_b, 4) || !aligned(conv_state, 2) ||
+        !aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16))
+        return SSD_ERR_MISALIGNED;
+    ssd::ConvArgs a{xbc, conv_w, conv_b, conv_state, x, B, C, p->batch, p->seqlen, p->nheads * p->headdim,
+                    p->ngroups * p->dstate};
+    return hip_status(ssd::launch_conv_silu(a, p->in_dtype, (hipStream_t)stream));
+}
+
+SSD_EXPORT ssd_status_t ssd_gated_norm(const ssd_params_t* p, const void* y, const void* z, const float* norm_w,
+                                       float norm_eps, void* out, void* stream) {
+    ssd_status_t s = validate_block(p);
+    if (s != SSD_OK) return s;
+    if (!y || !z || !norm_w || !out) return SSD_ERR_NULL_POINTER;
+    if (!aligned(y, 16) || !aligned(z, 16) || !aligned(norm_w, 16) || !aligned(out, 16)) return SSD_ERR_MISALIGNED;
+    if (!(norm_eps >= 0.f)) return SSD_ERR_INVALID_ARGUMENT;
+    ssd::NormArgs a{y, z, norm_w, out, (int64_t)p->batch * p->seqlen, p->nheads * p->headdim, p->ngroups, norm_eps};
+    return hip_status(ssd::launch_gated_norm(a, p->in_dtype, (hipStream_t)stream));
+}
+
+SSD_EXPORT ssd_status_t ssd_prefill_block(const ssd_params_t* p, const void* xbc, const float* conv_w,
+                                          const float* conv_b, const void* conv_state, const void* dt,
+                                          const float* A, const float* D, const float* dt_bias, const void* z,
+                                          const float* norm_w, float norm_eps, const void* initial_state, void* out,
+                                          void* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    ssd_status_t s = validate_block(p);
+    if (s != SSD_OK) return s;
+    const bool fused = p->impl == SSD_IMPL_FUSED;
+    if (fused && !block_fusable(p)) return SSD_ERR_UNSUPPORTED;
+    if (!xbc || !conv_w || !dt || !A || !z || !norm_w || !out || !final_state || !workspace) return SSD_ERR_NULL_POINTER;
+    if (!aligned(xbc, 16) || !aligned(conv_w, 16) || !aligned(conv_b, 4) || !aligned(conv_state, 2) ||
+        !aligned(dt, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(z, 16) ||
+        !aligned(norm_w, 16) || !aligned(initial_state, 16) || !aligned(out, 16) || !aligned(final_state, 16) ||
+        !aligned(workspace, kAlign))
+        return SSD_ERR_MISALIGNED;
+    if (!(norm_eps >= 0.f)) return SSD_ERR_INVALID_ARGUMENT;
+    const BlockLayout k = block_layout(p);
+    if (workspace_bytes < k.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    const size_t HP = (size_t)p->nheads * p->headdim, GN = (size_t)p->ngroups * p->dstate;
+    void* yw = ws + k.y_off;
+    if (!fused) {
+        // the three steps as separate launches: conv -> the five SSD kernels -> norm
+        ssd_status_t r = ssd_conv_silu(p, xbc, conv_w, conv_b, conv_state, ws + k.x_off, ws + k.b_off, ws + k.c_off,
+                                       stream);
+        if (r == SSD_OK)
+            r = ssd::prefill_impl(p, ws + k.x_off, dt, A, ws + k.b_off, ws + k.c_off, D, dt_bias, initial_state, yw,
+                                  final_state, workspace, k.l.w.total_bytes, stream, nullptr, nullptr, nullptr);
+        if (r == SSD_OK) r = ssd_gated_norm(p, yw, z, norm_w, norm_eps, out, stream);
+        return r;
+    }
+    const Layout& l = k.l;
+    ssd::SsdArgs a = make_args(p, l, workspace);
+    a.x = xbc;
+    a.x_stride = (int)(HP + 2 * GN);
+    a.xbc = xbc;
+    a.xbc_hp = (int)HP;
+    a.conv_w = conv_w;
+    a.conv_b = conv_b;
+    a.conv_state = conv_state;
+    a.dt = dt;
+    a.A = A;
+    a.B = ws + k.b_off;
+    a.C = ws + k.c_off;
+    a.D = D;
+    a.dt_bias = dt_bias;
+    a.y = yw;
+    a.z = z;
+    a.norm_w = norm_w;
+    a.norm_eps = norm_eps;
+    a.nsum = (float*)(ws + l.w.sync_offset) + k.nsum_w;
+    a.ncount = (uint32_t*)(ws + l.w.sync_offset) + k.ncount_w;
+    a.out = out;
+    a.has_h0 = initial_state != nullptr;
+    DevInfo d;
+    hipError_t e = device_info(&d);
+    if (e == hipSuccess) e = launch_block(ssd::STEP_FUSED_OCCUPANCY, p, a, st);
+    if (e != hipSuccess) return hip_status(e);
+    set_partitions(p, l, d, a);
+    // The norm fuses when every (b, g) pair's tiles share one partition (one XCD's L2 holds the
+    // sums) and can all be resident at once (a tile waits for the others of its pair and chunk);
+    // the tiles then pass the state themselves and claim whole pairs together.
+    const int per_part = (d.cus / d.nparts > 0 ? d.cus / d.nparts : 1) * (a.fused_occ > 0 ? a.fused_occ : 1);
+    bool aligned_parts = true;
+    for (int x = 0; x <= a.nparts; ++x) aligned_parts = aligned_parts && a.part_u0[x] % l.tpg == 0;
+    a.norm_fused = (aligned_parts && 2 * l.tpg <= per_part && env_int("MAMBA_SSD_BLOCK_NORM", 1) != 0) ? 1 : 0;
+    if (a.norm_fused) {
+        a.relay = 0;
+        a.slots = 1;
+        a.chain_group = 0;
+    }
+    const int es = (int)elem_size(p->state_dtype), K = a.slots, pperm = 1;
+    const int pw = ssd::p_per_wave(p->headdim);
+    e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, pw, p->dstate, K, 0, es,
+                              pperm, a.flags, k.nsync_total, l.nflags, (uint32_t)ssd::kChainStride,
+                              a.relay ? 0u : 1u, st);
+    if (e == hipSuccess) e = launch_block(ssd::STEP_FUSED, p, a, st);
+    if (e == hipSuccess)
+        e = ssd::launch_ring_copy(a.states, final_state, 0, p->batch, p->nheads, p->headdim, pw, p->dstate, K,
+                                  a.relay ? 1 : l.w.nchunks % K, es, pperm, nullptr, 0, 0, 1, 0u, st);
+    if (e != hipSuccess) return hip_status(e);
+    if (!a.norm_fused) return ssd_gated_norm(p, yw, z, norm_w, norm_eps, out, stream);
+    return SSD_OK;
 }

@@ -828,6 +828,102 @@ template <typename T, int N> __device__ void bmm_tile(const SsdArgs& a, int b, i
     }
 }
 
+// ---- the convolution before the SSD, inside the fused launch -----------------------------
+// silu(v) = v / (1 + e^-v) in fp32.
+__device__ inline float silu_f(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
+
+// Conv taps (width 4) and bias of channels ch0 .. ch0 + 7.
+struct ConvTaps {
+    float w[4][8], bias[8];
+    __device__ inline void load(const float* conv_w, const float* conv_b, int ch0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const f32x4 wv = *(const f32x4*)(conv_w + (size_t)(ch0 + e) * 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k][e] = wv[k];
+            bias[e] = conv_b ? conv_b[ch0 + e] : 0.f;
+        }
+    }
+};
+
+// The block form's convolution inputs, read once from the argument block (helpers take this
+// rather than the argument block itself).
+template <typename T> struct ConvSrc {
+    const T* xbc;         // [B][L][ch]
+    const T* state;       // [B][ch][3] or nullptr
+    const float* w;       // [ch][4]
+    const float* bias;    // [ch] or nullptr
+    int ch, L;
+    __device__ inline explicit ConvSrc(const SsdArgs& a)
+        : xbc((const T*)a.xbc), state((const T*)a.conv_state), w(a.conv_w), bias(a.conv_b), ch(a.x_stride),
+          L(a.seqlen) {}
+    // raw input of channels ch0 .. ch0 + 7 of token t of batch row b, as fp32: the xBC row for
+    // t >= 0, the conv state (the 3 inputs before token 0) or zeros for t < 0
+    __device__ inline void raw(int b, int t, int ch0, float (&v)[8]) const {
+        typedef typename TT<T>::v8 v8;
+        if (t >= 0) {
+            const v8 r = *(const v8*)(xbc + ((size_t)b * L + t) * ch + ch0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (float)r[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = state ? (float)state[((size_t)b * ch + ch0 + e) * 3 + (t + 3)] : 0.f;
+        }
+    }
+};
+
+// Eight consecutive outputs of one 8-channel piece from its 11 inputs in[0..10] (tokens
+// t0 - 3 .. t0 + 7): out[i] = silu(bias + sum_k w[k] in[i + k]).
+template <typename T> __device__ inline void conv8(const ConvTaps& k, const float (&in)[11][8], typename TT<T>::v8 (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            out[i][e] = (T)silu_f(k.bias[e] + k.w[0][e] * in[i][e] + k.w[1][e] * in[i + 1][e] + k.w[2][e] * in[i + 2][e] +
+                                  k.w[3][e] * in[i + 3][e]);
+}
+
+// Block form, before the bmm tile of (b, c, g): B and C of the chunk's tokens from the raw xBC
+// rows (channels H*P + g*N .. and H*P + G*N + g*N ..) through the convolution, into a.B / a.C
+// ([B][L][G][N], the layout of the plain inputs) for the bmm tile and the chunk tiles that read
+// them.  Items: (B or C, 8-channel piece, 8 tokens).
+template <typename T, int N> __device__ __forceinline__ void conv_bc_tile(const SsdArgs& a, int b, int c, int g) {
+    typedef typename TT<T>::v8 v8;
+    const int Q = a.chunk, L = a.seqlen, Gn = a.ngroups, hp = a.xbc_hp;
+    T* const Bw = (T*)a.B;
+    T* const Cw = (T*)a.C;
+    const ConvSrc<T> src(a);
+    const int tok0 = c * Q;
+    constexpr int NPC = N / 8;
+    const int items = 2 * NPC * (Q / 8);
+    for (int it = tid_here(); it < items; it += 256) {
+        const int which = it / (NPC * (Q / 8));  // 0: B, 1: C
+        const int rest = it - which * NPC * (Q / 8);
+        const int seg = rest / NPC, pc = rest - seg * NPC;
+        const int t0 = tok0 + seg * 8;
+        if (t0 >= L) continue;
+        const int ch0 = hp + which * Gn * N + g * N + pc * 8;
+        ConvTaps k;
+        k.load(src.w, src.bias, ch0);
+        float in[11][8];
+#pragma unroll
+        for (int r = 0; r < 11; ++r) {
+            const int t = t0 - 3 + r;
+            if (t < L) src.raw(b, t, ch0, in[r]);
+            else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) in[r][e] = 0.f;
+            }
+        }
+        v8 out[8];
+        conv8<T>(k, in, out);
+        T* dst = (which ? Cw : Bw) + (((size_t)b * L + t0) * Gn + g) * N + pc * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (t0 + i < L) *(v8*)(dst + (size_t)i * Gn * N) = out[i];
+    }
+}
+
 // ---- LDS staging helpers ---------------------------------------------------------------
 // Rows [t0, t0 + W) of a row-major [token][COLS] slice (row stride `rs` elements), stored
 // transposed: dst[col][jj] with row length LDW, zeros for tokens >= L.  Two consecutive

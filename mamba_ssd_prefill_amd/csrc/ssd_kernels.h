@@ -156,7 +156,8 @@ struct ClaimHook {
 };
 
 // chunk(args, b, c, g, tig, cb, hook) runs one chunk tile after its cumsum and bmm tiles are done.
-template <int HPT, int P, typename T, int N, int VL, typename ChunkFn>
+// BLK: the block form -- each bmm tile first convolves its chunk's B and C rows (conv_bc_tile).
+template <int HPT, int P, typename T, int N, int VL, int BLK = 0, typename ChunkFn>
 __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     __shared__ uint32_t s_word, s_next;
     const uint32_t raw = xcc_id();
@@ -199,6 +200,11 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                 cumsum_tile<T>(a, b, c, g * hpg + lo, g * hpg + hi);
                 publish_flag_block(a.cs_done + slot);
             } else {
+                if constexpr (BLK) {
+                    conv_bc_tile<T, N>(a, b, c, g);
+                    wait_vm_all();  // this workgroup's convolved rows are in the L2
+                    __syncthreads();
+                }
                 bmm_tile<T, N>(a, b, c, g, cb_at(a, slot));
                 publish_flag_block(a.bmm_done + slot);
             }
@@ -282,6 +288,17 @@ __global__ __launch_bounds__(256, (Geo16<T, P, N, Q>::OCC)) void k_fused16(SsdAr
     fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N, VL>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
                                                            const float* cbp, const auto& hook) {
         chunk_tile16<T, P, N, Q, MODE_FUSED, VL>(ai, b, c, g, tig, smem, cbp, hook);
+    });
+}
+
+// The block form: the convolution before and (a.norm_fused) the norm after the SSD in the same
+// launch ("Mamba-2炸裂升级！…", section "未来展望与应用拓展").
+template <typename T, int P, int N, int Q>
+__global__ __launch_bounds__(256, (Geo16<T, P, N, Q>::OCC)) void k_fused16_blk(SsdArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
+    fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N, 0, 1>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
+                                                             const float* cbp, const auto& hook) {
+        chunk_tile16<T, P, N, Q, MODE_FUSED, 0, 1>(ai, b, c, g, tig, smem, cbp, hook);
     });
 }
 
@@ -381,6 +398,20 @@ template <typename T, int Q, int VL> hipError_t dispatch16(int step, int P, int 
     if (P == 128 && N == 64) return launch_step16<T, 128, 64, Q, VL>(step, a, st);
     if (P == 128 && N == 128) return launch_step16<T, 128, 128, Q, VL>(step, a, st);
     return hipErrorNotSupported;
+}
+
+// The block form's (headdim, dstate) pairs: P in {64, 128} (whole token rows of y in LDS for
+// the norm), N in {64, 128}.
+template <typename T, int Q> hipError_t dispatch_blk16(int step, int P, int N, SsdArgs& a, hipStream_t st) {
+    const void* fn = nullptr;
+    if (P == 64 && N == 64) fn = (const void*)&k_fused16_blk<T, 64, 64, Q>;
+    else if (P == 64 && N == 128) fn = (const void*)&k_fused16_blk<T, 64, 128, Q>;
+    else if (P == 128 && N == 64) fn = (const void*)&k_fused16_blk<T, 128, 64, Q>;
+    else if (P == 128 && N == 128) fn = (const void*)&k_fused16_blk<T, 128, 128, Q>;
+    else return hipErrorNotSupported;
+    if (step == STEP_FUSED) return launch_fused(fn, a, st);
+    if (step == STEP_FUSED_OCCUPANCY) return fused_occupancy(fn, a);
+    return hipErrorInvalidValue;
 }
 
 template <int VL> hipError_t dispatch32(int step, int P, int N, SsdArgs& a, hipStream_t st) {

@@ -63,6 +63,26 @@ struct SsdArgs {
     int seqstates, nseq;
     const void* seq_h0;
     void* seq_fin;
+    // block form (the convolution before and the norm after the SSD in one launch): x is read
+    // from xbc [B][L][x_stride] (x_stride = H*P + 2*G*N; x in channels 0 .. H*P - 1, B at
+    // xbc_hp + g*N, C at xbc_hp + G*N + g*N) through the width-4 convolution (conv_w [ch][4],
+    // conv_b [ch] fp32, conv_state [B][ch][3] or nullptr); the bmm tiles convolve B and C into B
+    // and C (workspace, [B][L][G][N]).  With norm_fused the chunk tiles write
+    // out = norm(y silu(z)) instead of y, summing each token's squares in nsum [B][L][G] and
+    // counting finished tiles in ncount [B][nc][G].
+    int x_stride;       // elements between the token rows of x (H*P without the block form)
+    const void* xbc;
+    int xbc_hp;
+    const float* conv_w;
+    const float* conv_b;
+    const void* conv_state;
+    int norm_fused;
+    const void* z;
+    const float* norm_w;
+    float norm_eps;
+    float* nsum;
+    uint32_t* ncount;
+    void* out;
     int part_max_work;  // host only: the longest partition queue
     int cu_count;       // host only: compute units of the device
     int fused_occ;      // host only: workgroups of the fused kernel one CU holds at once
@@ -146,6 +166,36 @@ inline int decode_rows_per_block(int N) { return 4 * kDecodeIter * (256 / N); }
 
 // The decode step for dstate N in {16, 32, 64, 128, 256}; hipErrorNotSupported otherwise.
 hipError_t launch_decode(DecodeArgs& a, int in_dtype, hipStream_t st);
+
+// The steps around the SSD in the Mamba-2 block (ssd_block.hip), 16-bit inputs only.
+// conv: xbc [B][L][hp + 2 gn] -> x [B][L][hp], B and C [B][L][gn] (silu of the causal depthwise
+// convolution of width 4; w [ch][4], bias [ch] fp32; state [B][ch][3] or nullptr).
+struct ConvArgs {
+    const void* xbc;
+    const float* w;
+    const float* bias;
+    const void* state;
+    void* x;
+    void* B;
+    void* C;
+    int batch, seqlen, hp, gn;
+};
+// gated norm over rows tokens: out = y silu(z) / sqrt(mean_group (y silu(z))^2 + eps) * w,
+// y, z, out [rows][hp], w [hp] fp32, groups contiguous channel groups of hp / groups.
+struct NormArgs {
+    const void* y;
+    const void* z;
+    const float* w;
+    void* out;
+    int64_t rows;
+    int hp, groups;
+    float eps;
+};
+hipError_t launch_conv_silu(ConvArgs& a, int in_dtype, hipStream_t st);
+// The fused block form (STEP_FUSED / STEP_FUSED_OCCUPANCY), P and N in {64, 128}.
+hipError_t launch_block_f16(int step, int P, int N, int Q, SsdArgs& a, hipStream_t st);
+hipError_t launch_block_bf16(int step, int P, int N, int Q, SsdArgs& a, hipStream_t st);
+hipError_t launch_gated_norm(NormArgs& a, int in_dtype, hipStream_t st);
 
 // Non-templated kernels (ssd_common.hip).
 hipError_t launch_state_passing(SsdArgs& a, int PN, hipStream_t st);

@@ -411,11 +411,130 @@ __device__ inline SeqEnds seq_ends(const SsdArgs& a, int b, int c, int h, const 
     return r;
 }
 
+// Block form: the convolution before the SSD applied in place to the tile's x rows in LDS
+// (raw xBC rows, copied in by round 1), before any x operand is read.  An item is one 8-channel
+// piece of one head over 8 tokens; it needs the 3 raw rows above its first token (from LDS, or
+// from the previous chunk's rows / the conv state in memory for the first 8 tokens).  Items are
+// processed in rounds of 256 from the last rows up, each round reading all its inputs before a
+// barrier and writing after it, so no round overwrites a row a later round still reads raw.
+// Rows past the sequence end become zeros.
+template <typename T, int P, int Q, int HPT>
+__device__ void conv_x_tile(const ConvSrc<T> src, int b, int tok0, int valid, int head0, T* sX) {
+    typedef typename TT<T>::v8 v8;
+    constexpr int NPC = P / 8, SEGS = Q / 8, ITEMS = HPT * NPC * SEGS;
+    constexpr int ROUNDS = (ITEMS + 255) / 256;
+    static_assert(ITEMS % 256 == 0 || ROUNDS == 1, "a round must cover whole segments");
+    const int tid = tid_here();
+#pragma unroll 1
+    for (int rnd = ROUNDS - 1; rnd >= 0; --rnd) {
+        const int it = rnd * 256 + tid;
+        const bool act = it < ITEMS;
+        const int seg = it / (HPT * NPC), rem = it - seg * (HPT * NPC);
+        const int hh = rem / NPC, pc = rem - hh * NPC;
+        const int ch0 = (head0 + hh) * P + pc * 8;
+        T* tile = sX + hh * Q * P;
+        v8 raw[11];
+        ConvTaps k;
+        if (act) {
+            k.load(src.w, src.bias, ch0);
+#pragma unroll
+            for (int r = 0; r < 11; ++r) {
+                const int row = seg * 8 - 3 + r;
+                if (row >= 0) {
+                    raw[r] = *(const v8*)(tile + sw_off<P>(row, pc * 8));
+                } else {
+                    float v[8];
+                    src.raw(b, tok0 + row, ch0, v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) raw[r][e] = (T)v[e];
+                }
+            }
+        }
+        __syncthreads();  // this round's inputs are read
+        if (act) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = seg * 8 + i;
+                v8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float s = k.bias[e] + k.w[0][e] * (float)raw[i][e] + k.w[1][e] * (float)raw[i + 1][e] +
+                                    k.w[2][e] * (float)raw[i + 2][e] + k.w[3][e] * (float)raw[i + 3][e];
+                    o[e] = row < valid ? (T)silu_f(s) : (T)0.f;
+                }
+                *(v8*)(tile + sw_off<P>(row, pc * 8)) = o;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Block form with the norm fused: the tile's y rows (HPT heads, staged in LDS as whole token
+// rows of PPR 16-byte pieces, XOR-swizzled by the token) become
+//     out = g / sqrt(mean over the group's H/G heads of g^2 + eps) * norm_w,   g = y silu(z).
+// Pass 1 adds each token's sum of g^2 over the tile's channels to nsum (one float atomic per
+// token) and counts the tile in ncount; the tile then waits until all tpg tiles of its (b, g)
+// for this chunk have counted (they were claimed just before or after it, chunk-major, and
+// none of them waits on a later ticket), reads the sums and writes out in whole rows.
+template <typename T, int P, int Q, int PPR>
+__device__ void norm_rows(const SsdArgs& a, int b, int c, int g, int head0, int tok0, int valid, const char* sY) {
+    typedef typename TT<T>::v8 v8;
+    constexpr int ROWB = PPR * 16, KN = Q * PPR / 256;
+    const int tid = tid_here(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int L = a.seqlen, H = a.nheads, Gn = a.ngroups;
+    const uint32_t rs = (uint32_t)H * P * 2;  // bytes between token rows of z and out
+    const size_t row0 = ((size_t)b * L + tok0) * H * P + (size_t)head0 * P;
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc((const T*)a.z + row0, (uint32_t)(valid - 1) * rs + ROWB);
+    float* nsum = a.nsum + ((size_t)b * L + tok0) * Gn + g;
+    v8 zk[KN];
+#pragma unroll
+    for (int k = 0; k < KN; ++k) {
+        const int f = (k * 4 + wave) * 64 + lane, t = f / PPR, pc = f % PPR;
+        const v8 yv = *(const v8*)(sY + t * ROWB + ((pc ^ (t & (PPR - 1))) << 4));
+        zk[k] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(zr, (uint32_t)t * rs + (uint32_t)pc * 16, 0, 0));
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float gv = (float)yv[e] * silu_f((float)zk[k][e]);
+            ss += gv * gv;
+        }
+#pragma unroll
+        for (int m = PPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);  // the row's PPR lanes
+        if (pc == 0 && t < valid) atomicAdd(nsum + (size_t)t * Gn, ss);
+    }
+    wait_vm_all();  // this wave's sums have been added
+    __syncthreads();
+    uint32_t* cnt = a.ncount + ((size_t)b * a.nchunks + c) * Gn + g;
+    if (tid == 0) atomicAdd(cnt, 1u);
+    if (tid < 64) wait_flag(cnt, a, (uint32_t)a.tpg);
+    __syncthreads();
+    const float inv = 1.f / (float)(a.hpg * P);
+    const __amdgpu_buffer_rsrc_t ns = make_rsrc(nsum, (uint32_t)(valid * Gn * 4));
+    const __amdgpu_buffer_rsrc_t orow = make_rsrc((T*)a.out + row0, (uint32_t)(valid - 1) * rs + ROWB);
+#pragma unroll
+    for (int k = 0; k < KN; ++k) {
+        const int f = (k * 4 + wave) * 64 + lane, t = f / PPR, pc = f % PPR;
+        const v8 yv = *(const v8*)(sY + t * ROWB + ((pc ^ (t & (PPR - 1))) << 4));
+        const float r = __builtin_amdgcn_rsqf(bload_f32<AUX_L2>(ns, (uint32_t)(t * Gn) * 4) * inv + a.norm_eps);
+        const f32x4 w0 = *(const f32x4*)(a.norm_w + head0 * P + pc * 8);
+        const f32x4 w1 = *(const f32x4*)(a.norm_w + head0 * P + pc * 8 + 4);
+        v8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            o[e] = (T)((float)yv[e] * silu_f((float)zk[k][e]) * r * (e < 4 ? w0[e] : w1[e - 4]));
+        if (t < valid)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), orow, (uint32_t)t * rs + (uint32_t)pc * 16, 0, 2);
+    }
+}
+
 // `hook` (fused form): claim() after the round-2 reads are issued; see ClaimHook.
 // VL: 0 plain input; 1 packed variable-length input (a.seq_idx set: the decays are masked by
 // sequence); 2 packed input with per-sequence states (a.seqstates).  Separate instantiations, so
 // each kernel carries only the code of its own mode.
-template <typename T, int P, int N, int Q, int MODE, int VL, typename Hook>
+// BLK (fused form only): the block form -- x convolved from the raw xBC rows in LDS before
+// use, B and C read from the bmm tiles' convolved copies, and with a.norm_fused the gated norm
+// applied to y before it leaves (norm_rows).
+template <typename T, int P, int N, int Q, int MODE, int VL, int BLK = 0, typename Hook>
 __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, char* smem, const float* cbp,
                              const Hook& hook) {
     typedef Geo16<T, P, N, Q> G_;
@@ -454,21 +573,23 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     // read now: a load issued just before its use in the y loop would make every row block wait
     // for all of the tile's outstanding memory operations
     const float Dh = (MODE != MODE_STATE && a.D && hvalid) ? a.D[h] : 0.f;
-    const uint32_t xrs = (uint32_t)H * P * 2, bcrs = (uint32_t)Gn * N * 2;
+    const uint32_t xrs = (uint32_t)H * P * 2, bcrs = (uint32_t)Gn * N * 2;  // y rows; B, C rows
+    const size_t xel = BLK ? (size_t)a.x_stride : (size_t)H * P;            // x rows, elements
+    constexpr int BC_AUX = BLK ? AUX_L2 : 0;  // block form: B, C written inside the launch
     const uint32_t bc_bytes = (uint32_t)(valid - 1) * bcrs + N * 2;
     const size_t bc_off = (((size_t)b * L + tok0) * Gn + g) * N;
 
     // ---- round 1: x of every head of the tile, and B (or C), into LDS ----------------------
     for (int hh = 0; hh < HPT; ++hh) {
         const bool ok = (tig * HPT + hh) < hpg;
-        const T* xb = (const T*)a.x + (((size_t)b * L + tok0) * H + head0 + (ok ? hh : 0)) * P;
-        const uint32_t bytes = ok ? (uint32_t)(valid - 1) * xrs + P * 2 : 0u;
-        dma_rows<P, SWZ_TR, 2>(sX + hh * Q * P, make_rsrc(xb, bytes), Q, xrs);  // nt: x is read once
+        const T* xb = (const T*)a.x + ((size_t)b * L + tok0) * xel + (size_t)(head0 + (ok ? hh : 0)) * P;
+        const uint32_t bytes = ok ? (uint32_t)((valid - 1) * xel * 2) + P * 2 : 0u;
+        dma_rows<P, SWZ_TR, 2>(sX + hh * Q * P, make_rsrc(xb, bytes), Q, (uint32_t)(xel * 2));  // nt: read once
     }
     if constexpr (MODE != MODE_SCAN)
-        dma_rows<N, SWZ_TR>(sBC, make_rsrc((const T*)a.B + bc_off, bc_bytes), Q, bcrs);
+        dma_rows<N, SWZ_TR, BC_AUX>(sBC, make_rsrc((const T*)a.B + bc_off, bc_bytes), Q, bcrs);
     else
-        dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
+        dma_rows<N, SWZ_ROW, BC_AUX>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
     {
         // heads of the tile past the group read as zeros
         const int nvh = hpg - tig * HPT < HPT ? hpg - tig * HPT : HPT;
@@ -493,6 +614,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
     }
     wait_vm_all();
     __syncthreads();
+    if constexpr (BLK) conv_x_tile<T, P, Q, HPT>(ConvSrc<T>(a), b, tok0, valid, head0, sX);
 
     const float* a2_h = sA2 + hs * Q;
     // the state entering the chunk reaches its end unless a packed sequence starts inside it
@@ -619,7 +741,7 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             // bands, else into LDS.  The reads are in flight while the hop below waits for and
             // updates the state.
             lds_barrier();  // every wave is done reading x and B
-            dma_rows<N, SWZ_ROW>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
+            dma_rows<N, SWZ_ROW, BC_AUX>(sBC, make_rsrc((const T*)a.C + bc_off, bc_bytes), Q, bcrs);
             if constexpr (G_::L_LDS) {
                 lb.load(cbp, tid, cb16);
             } else if constexpr (CB_LDS) {
@@ -939,6 +1061,8 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
         // bands, x and CB are no longer read), then each wave stores four whole token rows per
         // instruction.  16-byte pieces are XOR-swizzled by the token so neither pass conflicts.
         constexpr int ROWB = HPT * P * 2, PPR = ROWB / 16;
+        static_assert(!BLK || (MBP == 2 && PPR == 16 && HPT * Q * P * 2 <= G_::SZ_R1 && XD_LDS),
+                      "the block form stages whole y rows in LDS and keeps the convolved x there");
         const int nvh_y = hpg - tig * HPT < HPT ? hpg - tig * HPT : HPT;
         if (MBP == 2 && PPR == 16 && HPT * Q * P * 2 <= G_::SZ_R1 && nvh_y == HPT) {
             char* sY = smem;
@@ -951,6 +1075,10 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
                     __builtin_bit_cast(u32x4, __builtin_shufflevector(yo[ib][0], yo[ib][1], 0, 1, 2, 3, 4, 5, 6, 7));
             }
             lds_barrier();
+            if (BLK && a.norm_fused) {
+                norm_rows<T, P, Q, PPR>(a, b, c, g, head0, tok0, valid, sY);
+                return;
+            }
             const __amdgpu_buffer_rsrc_t yrow =
                 make_rsrc((T*)a.y + (((size_t)b * L + tok0) * H + head0) * P, (uint32_t)(valid - 1) * xrs + ROWB);
 #pragma unroll

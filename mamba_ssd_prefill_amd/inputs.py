@@ -112,3 +112,40 @@ def workload_inputs(w: Workload, seed=None, **overrides):
     w = w.with_(**overrides) if overrides else w
     return make_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
                        w.dtype, w.state_dtype, w.has_h0, w.seed if seed is None else seed)
+
+
+@dataclass
+class BlockInputs:
+    """The block form's extra inputs (the convolution before and the gated norm after the SSD);
+    dt, A, D, dt_bias and h0 come from an SSDInputs of the same shape."""
+    xbc: "object"         # [B, L, H*P + 2*G*N], input dtype
+    conv_w: "object"      # [H*P + 2*G*N, 4] fp32
+    conv_b: "object"      # [H*P + 2*G*N] fp32
+    conv_state: "object"  # [B, H*P + 2*G*N, 3] input dtype, or None
+    z: "object"           # [B, L, H*P] input dtype
+    norm_w: "object"      # [H*P] fp32
+
+    def to(self, device):
+        mv = lambda t: None if t is None else t.to(device).contiguous()  # noqa: E731
+        return BlockInputs(mv(self.xbc), mv(self.conv_w), mv(self.conv_b), mv(self.conv_state), mv(self.z),
+                           mv(self.norm_w))
+
+
+def make_block_inputs(batch, seqlen, nheads, headdim, dstate, ngroups, dtype="bf16", has_state=True, seed=0):
+    """Recipe: the raw x channels of xBC ~ N(0, 1), the raw B and C channels ~ N(0, 1) / sqrt(N)
+    (the plain recipe's scale); taps ~ N(0, 0.5^2), bias ~ N(0, 0.1^2); the conv state drawn like
+    xBC's channels; z ~ N(0, 1); norm weights 1 + 0.1 N(0, 1).  Draw order from
+    ``torch.Generator().manual_seed(seed)``: xbc, conv_w, conv_b, conv_state, z, norm_w."""
+    import torch
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    gen = torch.Generator().manual_seed(seed)
+    hp, gn = nheads * headdim, ngroups * dstate
+    ch = hp + 2 * gn
+    scale = torch.cat([torch.ones(hp), torch.full((2 * gn,), 1.0 / math.sqrt(dstate))])
+    xbc = (torch.randn(batch, seqlen, ch, generator=gen) * scale).to(tdt)
+    conv_w = 0.5 * torch.randn(ch, 4, generator=gen)
+    conv_b = 0.1 * torch.randn(ch, generator=gen)
+    st = (torch.randn(batch, 3, ch, generator=gen) * scale).permute(0, 2, 1).contiguous().to(tdt)
+    z = torch.randn(batch, seqlen, hp, generator=gen).to(tdt)
+    norm_w = 1.0 + 0.1 * torch.randn(hp, generator=gen)
+    return BlockInputs(xbc, conv_w, conv_b, st if has_state else None, z, norm_w)
