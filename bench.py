@@ -201,6 +201,81 @@ def time_varlen(ssd, torch, steps):
             "packed_tokens_per_s": tokens / (res["packed"] / 1e3)}
 
 
+def time_block(ssd, torch, steps):
+    """The block form at the 2.7B layer shape (B=8, L=8192, H=80, P=64, N=128, G=1, Q=128, bf16,
+    fp32 state, initial state): the width-4 convolution before and the gated norm after the SSD.
+    Three ways, ms per call each: fused (one launch plus the boundary copies; the norm inside the
+    launch), separate (the conv kernel, the fused SSD, the norm kernel) and unfused (the conv
+    kernel, the five SSD kernels, the norm kernel).  Bytes: the fused block reads xBC, dt and z
+    and writes out once (plus the states); the separate form also writes and re-reads the
+    convolved x, B, C and y."""
+    from mamba_ssd_prefill_amd.inputs import WORKLOADS, make_block_inputs, workload_inputs
+    w = WORKLOADS["mamba2_2p7b_bf16"]
+    B_, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, 128
+    g = workload_inputs(w).to("cuda:0")
+    b = make_block_inputs(B_, L, H, P, N, G, dtype=w.dtype, has_state=False, seed=2003).to("cuda:0")
+    eps = 1e-5
+    T, e, hp, gn = B_ * L, ESZ[w.dtype], H * P, G * N
+    comp, exch, _ = algorithmic(w, Q, True)
+    fused_bytes = comp + exch + T * (2 * gn * e + hp * e)  # xBC instead of x, B, C: + z read; out replaces y
+    separate_bytes = fused_bytes + 2 * T * (hp + 2 * gn) * e + 2 * T * hp * e
+    out = torch.empty(B_, L, hp, dtype=b.xbc.dtype, device="cuda:0")
+    fin = torch.empty(B_, H, P, N, dtype=torch.float32, device="cuda:0")
+    res = {}
+    prm_f = ssd.make_params(B_, L, H, P, N, G, Q, w.dtype, "f32", True, "fused")
+    prm_u = ssd.make_params(B_, L, H, P, N, G, Q, w.dtype, "f32", True, "unfused")
+    ws_f = torch.empty(ssd.block_workspace_size(prm_f), dtype=torch.uint8, device="cuda:0")
+    ws_u = torch.empty(ssd.block_workspace_size(prm_u), dtype=torch.uint8, device="cuda:0")
+    ws_s = ssd.alloc_workspace(prm_f, "cuda:0")
+    x = torch.empty(B_, L, H, P, dtype=b.xbc.dtype, device="cuda:0")
+    Bm = torch.empty(B_, L, G, N, dtype=b.xbc.dtype, device="cuda:0")
+    Cm = torch.empty_like(Bm)
+    y = torch.empty_like(x)
+    kw = dict(nheads=H, headdim=P, ngroups=G, dstate=N, chunk_size=Q)
+
+    def fused():
+        ssd.ssd_prefill_block(b.xbc, b.conv_w, b.conv_b, None, g.dt, g.A, g.D, g.dt_bias, b.z, b.norm_w, eps, g.h0,
+                              impl="fused", workspace=ws_f, out=out, final_state=fin, **kw)
+
+    def unfused():
+        ssd.ssd_prefill_block(b.xbc, b.conv_w, b.conv_b, None, g.dt, g.A, g.D, g.dt_bias, b.z, b.norm_w, eps, g.h0,
+                              impl="unfused", workspace=ws_u, out=out, final_state=fin, **kw)
+
+    lib = ssd.load_library()
+    import ctypes
+
+    def separate():
+        st = ssd._stream(torch.device("cuda:0"))
+        ssd._check(lib.ssd_conv_silu(ctypes.byref(prm_f), ssd._ptr(b.xbc), ssd._ptr(b.conv_w), ssd._ptr(b.conv_b),
+                                     None, ssd._ptr(x), ssd._ptr(Bm), ssd._ptr(Cm), st), "ssd_conv_silu")
+        ssd.ssd_prefill(x, g.dt, g.A, Bm, Cm, g.D, g.dt_bias, g.h0, chunk_size=Q, impl="fused", workspace=ws_s, y=y,
+                        final_state=fin)
+        ssd._check(lib.ssd_gated_norm(ctypes.byref(prm_f), ssd._ptr(y), ssd._ptr(b.z), ssd._ptr(b.norm_w),
+                                      ctypes.c_float(eps), ssd._ptr(out), st), "ssd_gated_norm")
+
+    for name, fn in (("fused", fused), ("separate", separate), ("unfused", unfused)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    if ssd.check_device_status(prm_f, ws_f) != 0:
+        raise RuntimeError("device status after the fused block run")
+    r = {"workload": "2.7B layer shape, conv (width 4) + SSD + gated norm, bf16, Q=128",
+         "fused_ms": res["fused"], "separate_ms": res["separate"], "unfused_ms": res["unfused"],
+         "fused_tokens_per_s": T / (res["fused"] / 1e3), "separate_tokens_per_s": T / (res["separate"] / 1e3),
+         "speedup_fused_vs_separate": res["separate"] / res["fused"],
+         "bytes_fused": fused_bytes, "bytes_separate": separate_bytes,
+         "frac_fused": fused_bytes / (res["fused"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+         "frac_separate": separate_bytes / (res["separate"] / 1e3) / 1e9 / HBM_PEAK_GBS}
+    return r
+
+
 def copy_bandwidth(torch):
     """Bytes read plus written per second of a 512 MiB device-to-device copy (torch's copy
     kernel): what a plain streaming kernel reaches on this device, for context."""
@@ -372,6 +447,8 @@ def main():
             out["precision_sweep"] = prec
         log("packed variable-length input")
         out["varlen"] = time_varlen(ssd, torch, 10)
+        log("conv + SSD + norm block")
+        out["block"] = time_block(ssd, torch, 10)
         out["decode"] = decode_legs(ssd, torch, w)
     del g
     torch.cuda.empty_cache()

@@ -380,13 +380,14 @@ size_t ssd_prefill_block_workspace_size(const ssd_params_t* p);
  * ssd_prefill_block_workspace_size() bytes).
  *   SSD_IMPL_UNFUSED: the convolution kernel, the five SSD kernels and the norm kernel, with x,
  *     B, C and y going through the workspace.
- *   SSD_IMPL_FUSED: one launch (plus the boundary copies): the bmm tiles convolve B and C from
- *     xbc, the chunk tiles convolve their x rows in LDS, and each chunk tile applies the norm to
- *     its y rows once every tile of its (b, g) pair and chunk has added its share of the squared
- *     sums -- when every pair's tiles fall in one work partition and fit on its XCD at once;
- *     otherwise y goes through the workspace to the norm kernel.  headdim and dstate in
- *     {64, 128} with H/G a multiple of the heads per tile (2 at headdim 64), else
- *     SSD_ERR_UNSUPPORTED.  Test knob: MAMBA_SSD_BLOCK_NORM=0 sends y to the norm kernel. */
+ *   SSD_IMPL_FUSED: the convolution inside the SSD launch (plus the boundary copies): the bmm
+ *     tiles convolve B and C from xbc and the chunk tiles convolve their x rows in LDS; y goes
+ *     through the workspace to the norm kernel.  With MAMBA_SSD_BLOCK_NORM=1 the norm runs inside
+ *     the launch too, where every (b, g) pair's tiles fall in one work partition (one XCD): the
+ *     chunk tiles write y to out with each token's share of the squared sums of y silu(z), and a
+ *     norm item per tile, after all chunk tiles in the queue, scales those rows (measured slower
+ *     on MI355X than the norm kernel).  headdim and dstate in {64, 128} with H/G a multiple of
+ *     the heads per tile (2 at headdim 64), else SSD_ERR_UNSUPPORTED. */
 ssd_status_t ssd_prefill_block(const ssd_params_t* p, const void* xbc, const float* conv_w, const float* conv_b,
                                const void* conv_state, const void* dt, const float* A, const float* D,
                                const float* dt_bias, const void* z, const float* norm_w, float norm_eps,

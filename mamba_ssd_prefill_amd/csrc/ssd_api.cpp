@@ -798,13 +798,14 @@ SSD_EXPORT ssd_status_t ssd_prefill_block(const ssd_params_t* p, const void* xbc
     if (e == hipSuccess) e = launch_block(ssd::STEP_FUSED_OCCUPANCY, p, a, st);
     if (e != hipSuccess) return hip_status(e);
     set_partitions(p, l, d, a);
-    // The norm fuses when every (b, g) pair's tiles share one partition (one XCD's L2 holds the
-    // sums) and can all be resident at once (a tile waits for the others of its pair and chunk);
-    // the tiles then pass the state themselves and claim whole pairs together.
-    const int per_part = (d.cus / d.nparts > 0 ? d.cus / d.nparts : 1) * (a.fused_occ > 0 ? a.fused_occ : 1);
+    // The norm kernel after the launch is the default (measured faster on MI355X than every
+    // in-launch form tried).  MAMBA_SSD_BLOCK_NORM=1 runs the norm inside the launch instead,
+    // where every (b, g) pair's tiles share one partition (one XCD's L2 holds the rows and sums
+    // the norm items read back): the chunk tiles then pass the state themselves and claim whole
+    // pairs together, and a norm item waits only on chunk tiles with smaller tickets.
     bool aligned_parts = true;
     for (int x = 0; x <= a.nparts; ++x) aligned_parts = aligned_parts && a.part_u0[x] % l.tpg == 0;
-    a.norm_fused = (aligned_parts && 2 * l.tpg <= per_part && env_int("MAMBA_SSD_BLOCK_NORM", 1) != 0) ? 1 : 0;
+    a.norm_fused = (aligned_parts && env_int("MAMBA_SSD_BLOCK_NORM", 0) == 1) ? 1 : 0;
     if (a.norm_fused) {
         a.relay = 0;
         a.slots = 1;

@@ -96,8 +96,21 @@ __device__ inline FusedPart fused_part(const SsdArgs& a, int x) {
     f.pb = a.part_pb[x];
     f.n_cs = (uint32_t)f.np * a.nchunks;
     f.first_chunk = 2 * f.n_cs + (uint32_t)a.relay * f.nu;
-    f.n_total = f.first_chunk + (uint32_t)f.nu * a.nchunks;
+    // block form with the norm in the launch: a norm item per chunk tile, interleaved (norm_ticket)
+    f.n_total = f.first_chunk + (uint32_t)f.nu * a.nchunks * (a.norm_fused ? 2u : 1u);
     return f;
+}
+
+// Block form with the norm in the launch: the norm items follow all of the partition's chunk
+// tiles, in the same chunk-major order, so a norm item waits only on chunk tiles with smaller
+// tickets that have (almost always) finished.  Returns, for ticket t >= first_chunk, the chunk
+// tile ticket it stands for (first_chunk + c * nu + k), with *norm set for a norm item.
+// (Interleaving the norm items a chunk behind the tiles was measured slower: norm items claimed
+// while their chunk's tiles still ran held workgroups waiting.)
+__device__ inline uint32_t norm_ticket(const FusedPart& f, int nc, uint32_t t, bool* norm) {
+    const uint32_t tiles = (uint32_t)f.nu * (uint32_t)nc;
+    *norm = t - f.first_chunk >= tiles;
+    return *norm ? t - tiles : t;
 }
 
 // hardware id of the XCD this wave runs on (HW_REG_XCC_ID, bits [3:0])
@@ -156,8 +169,9 @@ struct ClaimHook {
 };
 
 // chunk(args, b, c, g, tig, cb, hook) runs one chunk tile after its cumsum and bmm tiles are done.
-// BLK: the block form -- each bmm tile first convolves its chunk's B and C rows (conv_bc_tile).
-template <int HPT, int P, typename T, int N, int VL, int BLK = 0, typename ChunkFn>
+// BLK: the block form -- each bmm tile first convolves its chunk's B and C rows (conv_bc_tile);
+// BQ: its chunk size (for the norm items).
+template <int HPT, int P, typename T, int N, int VL, int BLK = 0, int BQ = 0, typename ChunkFn>
 __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
     __shared__ uint32_t s_word, s_next;
     const uint32_t raw = xcc_id();
@@ -240,6 +254,17 @@ __device__ void fused_loop(const SsdArgs& a0, ChunkFn&& chunk) {
                     relay_chain<T, NT, 2, VL>(a, b, h, ph, WPH, rw);
             }
         } else {
+            if constexpr (BLK) {
+                if (a.norm_fused) {
+                    bool norm;
+                    t = norm_ticket(f, nc, t, &norm);
+                    if (norm) {
+                        const ChunkItem it = chunk_item(a, f, t);
+                        norm_item<T, P, HPT, BQ>(a, it.b, it.c, it.g, it.tig);
+                        continue;
+                    }
+                }
+            }
             const ChunkItem it = chunk_item(a, f, t);
             if (a.relay && live < 0) {
                 // the partition's relay decision (made by its first relay ticket, which is smaller)
@@ -296,7 +321,7 @@ __global__ __launch_bounds__(256, (Geo16<T, P, N, Q>::OCC)) void k_fused16(SsdAr
 template <typename T, int P, int N, int Q>
 __global__ __launch_bounds__(256, (Geo16<T, P, N, Q>::OCC)) void k_fused16_blk(SsdArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Geo16<T, P, N, Q>::SMEM];
-    fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N, 0, 1>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
+    fused_loop<Geo16<T, P, N, Q>::HPT, P, T, N, 0, 1, Q>(a, [&](const SsdArgs& ai, int b, int c, int g, int tig,
                                                              const float* cbp, const auto& hook) {
         chunk_tile16<T, P, N, Q, MODE_FUSED, 0, 1>(ai, b, c, g, tig, smem, cbp, hook);
     });

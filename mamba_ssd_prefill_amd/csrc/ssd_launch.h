@@ -67,9 +67,9 @@ struct SsdArgs {
     // from xbc [B][L][x_stride] (x_stride = H*P + 2*G*N; x in channels 0 .. H*P - 1, B at
     // xbc_hp + g*N, C at xbc_hp + G*N + g*N) through the width-4 convolution (conv_w [ch][4],
     // conv_b [ch] fp32, conv_state [B][ch][3] or nullptr); the bmm tiles convolve B and C into B
-    // and C (workspace, [B][L][G][N]).  With norm_fused the chunk tiles write
-    // out = norm(y silu(z)) instead of y, summing each token's squares in nsum [B][L][G] and
-    // counting finished tiles in ncount [B][nc][G].
+    // and C (workspace, [B][L][G][N]).  With norm_fused the chunk tiles write the gated rows
+    // y silu(z) to out instead of y, summing each token's squares in nsum [B][L][G] and counting
+    // finished tiles in ncount [B][nc][G]; norm items (norm_ticket) then scale those rows.
     int x_stride;       // elements between the token rows of x (H*P without the block form)
     const void* xbc;
     int xbc_hp;

@@ -469,13 +469,12 @@ __device__ void conv_x_tile(const ConvSrc<T> src, int b, int tok0, int valid, in
     __syncthreads();
 }
 
-// Block form with the norm fused: the tile's y rows (HPT heads, staged in LDS as whole token
-// rows of PPR 16-byte pieces, XOR-swizzled by the token) become
-//     out = g / sqrt(mean over the group's H/G heads of g^2 + eps) * norm_w,   g = y silu(z).
-// Pass 1 adds each token's sum of g^2 over the tile's channels to nsum (one float atomic per
-// token) and counts the tile in ncount; the tile then waits until all tpg tiles of its (b, g)
-// for this chunk have counted (they were claimed just before or after it, chunk-major, and
-// none of them waits on a later ticket), reads the sums and writes out in whole rows.
+// Block form with the norm in the launch, part 1 (end of the chunk tile): the tile's y rows
+// (HPT heads, staged in LDS as whole token rows of PPR 16-byte pieces, XOR-swizzled by the
+// token, already rounded to T as y would leave) go to out in whole rows; each token's sum of
+// g^2, g = y silu(z), over the tile's channels goes to nsum (one float atomic per token), then
+// the tile counts itself in ncount.  No wait: norm_item finishes the rows a chunk later, from
+// the same rounded y (so the result is the one the separate norm kernel gives on y).
 template <typename T, int P, int Q, int PPR>
 __device__ void norm_rows(const SsdArgs& a, int b, int c, int g, int head0, int tok0, int valid, const char* sY) {
     typedef typename TT<T>::v8 v8;
@@ -485,43 +484,75 @@ __device__ void norm_rows(const SsdArgs& a, int b, int c, int g, int head0, int 
     const uint32_t rs = (uint32_t)H * P * 2;  // bytes between token rows of z and out
     const size_t row0 = ((size_t)b * L + tok0) * H * P + (size_t)head0 * P;
     const __amdgpu_buffer_rsrc_t zr = make_rsrc((const T*)a.z + row0, (uint32_t)(valid - 1) * rs + ROWB);
+    const __amdgpu_buffer_rsrc_t orow = make_rsrc((T*)a.out + row0, (uint32_t)(valid - 1) * rs + ROWB);
     float* nsum = a.nsum + ((size_t)b * L + tok0) * Gn + g;
-    v8 zk[KN];
 #pragma unroll
     for (int k = 0; k < KN; ++k) {
         const int f = (k * 4 + wave) * 64 + lane, t = f / PPR, pc = f % PPR;
         const v8 yv = *(const v8*)(sY + t * ROWB + ((pc ^ (t & (PPR - 1))) << 4));
-        zk[k] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(zr, (uint32_t)t * rs + (uint32_t)pc * 16, 0, 0));
+        const v8 zv = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(zr, (uint32_t)t * rs + (uint32_t)pc * 16, 0, 0));
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float gv = (float)yv[e] * silu_f((float)zk[k][e]);
-            ss += gv * gv;
+            const float v = (float)yv[e] * silu_f((float)zv[e]);
+            ss += v * v;
         }
 #pragma unroll
         for (int m = PPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);  // the row's PPR lanes
-        if (pc == 0 && t < valid) atomicAdd(nsum + (size_t)t * Gn, ss);
+        if (t < valid) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yv), orow, (uint32_t)t * rs + (uint32_t)pc * 16, 0, 0);
+            if (pc == 0) atomicAdd(nsum + (size_t)t * Gn, ss);
+        }
     }
-    wait_vm_all();  // this wave's sums have been added
+    wait_vm_all();  // this wave's rows and sums have reached the L2
     __syncthreads();
+    if (tid == 0) atomicAdd(a.ncount + ((size_t)b * a.nchunks + c) * Gn + g, 1u);
+}
+
+// Block form with the norm in the launch, part 2: a norm item for the tile (b, c, g, tig) waits
+// until all tpg tiles of its (b, g) pair have counted for chunk c (in the queue it comes a
+// chunk after them), then turns its tile's y rows in out into out = g / sqrt(nsum / (H/G * P)
+// + eps) * norm_w, g = y silu(z).  Same XCD as the tiles (one partition), so the rows and sums
+// come from its L2.
+template <typename T, int P, int HPT, int Q>
+__device__ void norm_item(const SsdArgs& a, int b, int c, int g, int tig) {
+    typedef typename TT<T>::v8 v8;
+    constexpr int PPR = HPT * P / 8;  // 16-byte pieces of a token row of the tile
+    constexpr int KN = Q * PPR / 256;  // pieces per thread
+    const int tid = tid_here();
+    const int L = a.seqlen, H = a.nheads, Gn = a.ngroups;
+    const int head0 = g * a.hpg + tig * HPT, tok0 = c * Q;
+    const int valid = L - tok0 < Q ? L - tok0 : Q;
     uint32_t* cnt = a.ncount + ((size_t)b * a.nchunks + c) * Gn + g;
-    if (tid == 0) atomicAdd(cnt, 1u);
     if (tid < 64) wait_flag(cnt, a, (uint32_t)a.tpg);
     __syncthreads();
+    const uint32_t rs = (uint32_t)H * P * 2;
+    const size_t row0 = ((size_t)b * L + tok0) * H * P + (size_t)head0 * P;
+    // rows past the sequence end read as zeros and are not written
+    const __amdgpu_buffer_rsrc_t orow = make_rsrc((T*)a.out + row0, (uint32_t)(valid - 1) * rs + PPR * 16);
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc((const T*)a.z + row0, (uint32_t)(valid - 1) * rs + PPR * 16);
+    const __amdgpu_buffer_rsrc_t ns = make_rsrc(a.nsum + ((size_t)b * L + tok0) * Gn + g, (uint32_t)(valid * Gn * 4));
     const float inv = 1.f / (float)(a.hpg * P);
-    const __amdgpu_buffer_rsrc_t ns = make_rsrc(nsum, (uint32_t)(valid * Gn * 4));
-    const __amdgpu_buffer_rsrc_t orow = make_rsrc((T*)a.out + row0, (uint32_t)(valid - 1) * rs + ROWB);
+    // every load first, then the arithmetic and the stores (one wait for all of them)
+    v8 yv[KN], zv[KN];
+    float r[KN];
 #pragma unroll
     for (int k = 0; k < KN; ++k) {
-        const int f = (k * 4 + wave) * 64 + lane, t = f / PPR, pc = f % PPR;
-        const v8 yv = *(const v8*)(sY + t * ROWB + ((pc ^ (t & (PPR - 1))) << 4));
-        const float r = __builtin_amdgcn_rsqf(bload_f32<AUX_L2>(ns, (uint32_t)(t * Gn) * 4) * inv + a.norm_eps);
+        const int f = k * 256 + tid, t = f / PPR, pc = f % PPR;
+        const uint32_t off = (uint32_t)t * rs + (uint32_t)pc * 16;
+        yv[k] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(orow, off, 0, AUX_L2));
+        zv[k] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(zr, off, 0, 0));
+        r[k] = bload_f32<AUX_L2>(ns, (uint32_t)(t * Gn) * 4);
+    }
+#pragma unroll
+    for (int k = 0; k < KN; ++k) {
+        const int f = k * 256 + tid, t = f / PPR, pc = f % PPR;
+        const float rk = __builtin_amdgcn_rsqf(r[k] * inv + a.norm_eps);
         const f32x4 w0 = *(const f32x4*)(a.norm_w + head0 * P + pc * 8);
         const f32x4 w1 = *(const f32x4*)(a.norm_w + head0 * P + pc * 8 + 4);
         v8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            o[e] = (T)((float)yv[e] * silu_f((float)zk[k][e]) * r * (e < 4 ? w0[e] : w1[e - 4]));
+        for (int e = 0; e < 8; ++e) o[e] = (T)((float)yv[k][e] * silu_f((float)zv[k][e]) * rk * (e < 4 ? w0[e] : w1[e - 4]));
         if (t < valid)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), orow, (uint32_t)t * rs + (uint32_t)pc * 16, 0, 2);
     }

@@ -1,9 +1,9 @@
 """GPU parity of the block form: the convolution before and the gated norm after the SSD
 ("Mamba-2炸裂升级！…", section "未来展望与应用拓展"), through the C ABI, against the oracle's
 conv_silu / gated_rmsnorm / block (fp64).  The standalone kernels, the unfused block (three
-kernels with the SSD's five between) and the fused block with the norm inside the launch and with
-y sent to the norm kernel (MAMBA_SSD_BLOCK_NORM=0), at shapes whose (b, g) pairs fall on whole
-work partitions (norm fused) and shapes whose pairs straddle them (norm kernel).
+kernels with the SSD's five between) and the fused block (convolution inside the launch) with
+y sent to the norm kernel (the default) and with the norm inside the launch as well
+(MAMBA_SSD_BLOCK_NORM=1, at shapes whose (b, g) pairs fall on whole work partitions).
 """
 import os
 
@@ -95,17 +95,20 @@ def test_block_fused(case, Q):
     gate(f64(fin), rfin, "f32", "bf16", name="block final")
 
 
-@pytest.mark.parametrize("case", CASES[:2], ids=lambda c: "_".join(map(str, c)))
-def test_block_fused_norm_kernel_and_unfused(case, monkeypatch):
+@pytest.mark.parametrize("Q", [64, 128, 256])
+@pytest.mark.parametrize("case", CASES[:3], ids=lambda c: "_".join(map(str, c)))
+def test_block_fused_norm_in_launch_and_unfused(case, Q, monkeypatch):
     Bt, L, H, P, N, G = case
-    inp, blk = inputs(Bt, L, H, P, N, G, seed=11)
+    inp, blk = inputs(Bt, L, H, P, N, G, seed=11 + Q)
     rout, ry, rfin = ref_block(inp, blk, H, P, G, N, "bf16")
-    say("block fused, norm kernel %s" % (case,))
-    monkeypatch.setenv("MAMBA_SSD_BLOCK_NORM", "0")
-    out, fin = run_block(inp, blk, H, P, G, N, 128, "fused")
-    gate(f64(out), rout, "bf16", "bf16", name="block out (norm kernel)")
-    gate(f64(fin), rfin, "f32", "bf16", name="block final (norm kernel)")
+    say("block fused, norm in the launch %s Q=%d" % (case, Q))
+    monkeypatch.setenv("MAMBA_SSD_BLOCK_NORM", "1")
+    out, fin = run_block(inp, blk, H, P, G, N, Q, "fused")
+    gate(f64(out), rout, "bf16", "bf16", name="block out (norm in the launch)")
+    gate(f64(fin), rfin, "f32", "bf16", name="block final (norm in the launch)")
     monkeypatch.delenv("MAMBA_SSD_BLOCK_NORM")
+    if Q != 128:
+        return
     say("block unfused %s" % (case,))
     out, fin = run_block(inp, blk, H, P, G, N, 128, "unfused")
     gate(f64(out), rout, "bf16", "bf16", name="block out (unfused)")
@@ -159,7 +162,8 @@ def test_block_refuses_unsupported():
 
 def test_block_norm_runs_inside_the_launch_where_pairs_are_whole():
     """The y region of the workspace (its last region) is left alone when the norm runs inside the
-    launch, and written when y goes to the norm kernel."""
+    launch (the chunk tiles write y to out, the norm items scale it there), and written when y
+    goes to the norm kernel."""
     Bt, L, H, P, N, G = CASES[0]
     inp, blk = inputs(Bt, L, H, P, N, G, seed=51)
     g, b = inp.to("cuda:0"), blk.to("cuda:0")
@@ -179,4 +183,28 @@ def test_block_norm_runs_inside_the_launch_where_pairs_are_whole():
             touched[norm] = bool((ws[total - ysz:] != 0xFF).any())
         finally:
             del os.environ["MAMBA_SSD_BLOCK_NORM"]
-    assert touched == {"1": False, "0": True}
+    assert touched == {"1": False, "0": True}  # 1: norm items in the launch; 0 (default): norm kernel
+
+
+@pytest.mark.parametrize("norm", ["0", "1"])
+def test_block_2p7b_full_every_row(norm, monkeypatch):
+    """The fused block at the 2.7B layer shape (B=8, L=8192, H=80, P=64, N=128, G=1, Q=128; every
+    batch row is one work partition, so the norm can run inside the launch), with the norm kernel
+    and with the norm in the launch, compared with the oracle's block row by row on every element
+    of out and of the final state."""
+    monkeypatch.setenv("MAMBA_SSD_BLOCK_NORM", norm)
+    from mamba_ssd_prefill_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["mamba2_2p7b_bf16"]
+    Bt, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    inp = workload_inputs(w)
+    blk = make_block_inputs(Bt, L, H, P, N, G, dtype=w.dtype, has_state=True, seed=2003)
+    say("block 2.7B full size")
+    out, fin = run_block(inp, blk, H, P, G, N, 128, "fused")
+    out, fin = f64(out), f64(fin)
+    for b in range(Bt):
+        row = lambda t: None if t is None else t[b:b + 1].contiguous()  # noqa: E731
+        rout, ry, rfin = oracle.block(row(blk.xbc), blk.conv_w, blk.conv_b, row(blk.conv_state), row(inp.dt), inp.A,
+                                      inp.D, inp.dt_bias, row(blk.z), blk.norm_w, EPS, nheads=H, headdim=P, ngroups=G,
+                                      dstate=N, h0=row(inp.h0), in_dtype=w.dtype)
+        gate(out[b:b + 1], rout, "bf16", "bf16", name="2.7B block out row %d" % b)
+        gate(fin[b:b + 1], rfin, "f32", "bf16", name="2.7B block final row %d" % b)
