@@ -96,27 +96,30 @@ def short_paths(ins, labels):
         if op not in REQUIRED:
             raise ValueError("no wait-state figure for %s" % op)
         req = REQUIRED[op]
-        dst = _regs(_operands(args)[0])
+        dst0 = frozenset(_regs(_operands(args)[0]))
         best = {}
-        stack = [(j, 0) for j in succ[k]]
+        stack = [(j, 0, dst0) for j in succ[k]]
         while stack:
-            j, d = stack.pop()
-            if d >= req or best.get(j, req) <= d:
+            j, d, dst = stack.pop()
+            if d >= req or best.get((j, dst), req) <= d:
                 continue
-            best[j] = d
+            best[(j, dst)] = d
             op2, a2 = ins[j]
             o2 = _operands(a2)
             if op2.startswith("s_"):
                 step = int(a2, 0) + 1 if op2 == "s_nop" else 1
-                stack.extend((s, d + step) for s in succ[j])
+                stack.extend((s_, d + step, dst) for s_ in succ[j])
                 continue
             if op2.startswith("v_mfma"):
                 ab = _regs(o2[1]) | _regs(o2[2])
-                c = _regs(o2[3]) if len(o2) > 3 else set()
+                c = frozenset(_regs(o2[3])) if len(o2) > 3 else frozenset()
                 # accumulating onto exactly these registers (C = the earlier result) is chained
                 # by the hardware; as an A/B operand or in part of C they are a read
                 if ab & dst or (c & dst and c != dst):
                     found.append((d, req, k, j))
+                    continue
+                dst = dst - _regs(o2[0])  # registers this MFMA writes now hold its result
+                if not dst:
                     continue
             else:
                 # a read; or a VALU overwrite before the result has landed (a load's data comes
@@ -126,7 +129,7 @@ def short_paths(ins, labels):
                 if touched & dst:
                     found.append((d, req, k, j))
                     continue
-            stack.extend((s, d + 1) for s in succ[j])
+            stack.extend((s_, d + 1, dst) for s_ in succ[j])
     return found
 
 

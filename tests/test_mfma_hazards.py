@@ -85,3 +85,11 @@ def test_built_objects_are_clean():
     if not objs:
         pytest.skip("library not built")
     assert mh.check_objects(objs) == []
+
+
+def test_registers_an_accumulation_chain_overwrote_are_not_tracked():
+    # the second MFMA accumulates onto the first's result and writes part of it anew; the third
+    # reads that part as its C: a read of the second's result, chained, not of the first's
+    assert _check(["v_mfma_f32_16x16x32_f16 v[56:59], v[110:113], v[74:77], v[62:65]",
+                   "v_mfma_f32_16x16x32_f16 v[54:57], v[106:109], v[86:89], v[56:59]",
+                   "v_mfma_f32_16x16x32_f16 v[30:33], v[114:117], v[94:97], v[54:57]", "s_endpgm"]) == []
