@@ -327,6 +327,8 @@ def main():
                     help="only the decode-step legs (for a kernel trace of k_decode); prints their JSON")
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="with --decode-only: this batch size only (default: the workload's and 16 times it)")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only the block-form leg (convolution + SSD + gated norm; for a kernel trace); prints its JSON")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 1 GiB device copy (counter calibration), "
                          "then --steps fused calls; prints nothing")
@@ -350,6 +352,9 @@ def main():
     Q = args.chunk or w.chunk_size
     if args.decode_only:
         print(json.dumps(decode_legs(ssd, torch, w, args.decode_batch)), flush=True)
+        return
+    if args.block_only:
+        print(json.dumps(time_block(ssd, torch, args.steps)), flush=True)
         return
     log("generating %s inputs" % w.name)
     inp = workload_inputs(w)
