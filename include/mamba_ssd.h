@@ -81,8 +81,22 @@ typedef struct {
     int relaxed;      /* 0: exact intermediates; 1: relaxed ("Mamba-2炸裂升级！…", section
                          "精度与性能的平衡艺术"): with 16-bit inputs CB = C B^T of each chunk is
                          stored in in_dtype instead of fp32 (no effect for fp32 inputs) */
-    int reserved;     /* must be 0 */
+    int flags;        /* 0, or SSD_FLAG_WORKSPACE_READY (below); other bits must be 0 */
 } ssd_params_t;
+
+/* flags bit 0 (fused form; ignored by the unfused form and by ssd_prefill_block): the
+ * workspace's synchronisation words are as the previous fused call on this workspace left them,
+ * and that call had the same parameters (every field but flags) and ran in this process.  Every
+ * fused call that writes a final_state resets those words for the next call in the launch that
+ * copies the final state out, so a caller that reuses one workspace for a run of identical calls
+ * sets this bit on all but the first: a call without an initial state then skips the launch that
+ * would reset them (one launch fewer per call).  The library keeps, per workspace address, the
+ * parameters of the last call that left it ready; when they differ, or the last call on the
+ * workspace was not such a call, the bit is ignored and the words are reset as usual.  A caller
+ * who wrote to the workspace in between, or freed and re-allocated it, must not set the bit.
+ * The device status word (ssd_check_device_status) is cleared only by a call that resets the
+ * words: after an error, calls with this bit keep reporting it until a call without the bit. */
+#define SSD_FLAG_WORKSPACE_READY 1
 
 /*
  * Tensor arguments (all device pointers):
@@ -105,6 +119,7 @@ typedef struct {
  *   workspace     bytes         -            required, 256-byte aligned, at least
  *                                            ssd_prefill_workspace_size() bytes; its contents
  *                                            need no initialisation and are overwritten
+ *                                            (but see SSD_FLAG_WORKSPACE_READY)
  */
 
 /* Bytes of workspace ssd_prefill needs for *p (0 if *p is invalid: see ssd_validate). */

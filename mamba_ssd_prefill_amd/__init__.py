@@ -23,6 +23,7 @@ _LIB_PATH = os.environ.get("MAMBA_SSD_LIB", os.path.join(_HERE, "libmamba_ssd.so
 SSD_F32, SSD_F16, SSD_BF16 = 0, 1, 2
 DTYPE_CODES = {"f32": SSD_F32, "f16": SSD_F16, "bf16": SSD_BF16}
 IMPL_CODES = {"unfused": 0, "fused": 1}
+FLAG_WORKSPACE_READY = 1  # ssd_params_t.flags bit: see ssd_prefill(workspace_ready=...)
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_POINTER", 2: "SSD_ERR_INVALID_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
                 4: "SSD_ERR_MISALIGNED", 5: "SSD_ERR_WORKSPACE_TOO_SMALL", 6: "SSD_ERR_HIP",
                 7: "SSD_ERR_SYNC_TIMEOUT", 8: "SSD_ERR_INVALID_ARGUMENT", 9: "SSD_ERR_SCHEDULE",
@@ -51,7 +52,7 @@ class Params(ctypes.Structure):
                 ("nheads", ctypes.c_int), ("headdim", ctypes.c_int), ("dstate", ctypes.c_int),
                 ("ngroups", ctypes.c_int), ("chunk_size", ctypes.c_int), ("in_dtype", ctypes.c_int),
                 ("state_dtype", ctypes.c_int), ("dt_softplus", ctypes.c_int), ("impl", ctypes.c_int),
-                ("relaxed", ctypes.c_int), ("reserved", ctypes.c_int)]
+                ("relaxed", ctypes.c_int), ("flags", ctypes.c_int)]
 
 
 class Layout(ctypes.Structure):
@@ -126,17 +127,18 @@ def _dtype_code(t):
 
 
 def make_params(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size=128, in_dtype="bf16",
-                state_dtype="f32", dt_softplus=True, impl="fused", relaxed=False):
+                state_dtype="f32", dt_softplus=True, impl="fused", relaxed=False, flags=0):
     code = lambda d: d if isinstance(d, int) else DTYPE_CODES[d]  # noqa: E731
     return Params(ctypes.sizeof(Params), int(batch), int(seqlen), int(nheads), int(headdim), int(dstate),
                   int(ngroups), int(chunk_size), code(in_dtype), code(state_dtype), 1 if dt_softplus else 0,
-                  IMPL_CODES[impl] if isinstance(impl, str) else int(impl), 1 if relaxed else 0, 0)
+                  IMPL_CODES[impl] if isinstance(impl, str) else int(impl), 1 if relaxed else 0, int(flags))
 
 
-def _params_for(x, B, chunk_size, state_dtype_code, dt_softplus, impl, relaxed=False):
+def _params_for(x, B, chunk_size, state_dtype_code, dt_softplus, impl, relaxed=False, flags=0):
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    return make_params(Bt, L, H, P, N, G, chunk_size, _dtype_code(x), state_dtype_code, dt_softplus, impl, relaxed)
+    return make_params(Bt, L, H, P, N, G, chunk_size, _dtype_code(x), state_dtype_code, dt_softplus, impl, relaxed,
+                       flags)
 
 
 def workspace_size(params):
@@ -203,7 +205,7 @@ def _check_tensors(x, dt, A, B, C, D, dt_bias, h0):
 
 def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_size=128, state_dtype=None,
                 impl="fused", dt_softplus=True, workspace=None, y=None, final_state=None, kernel_events=None,
-                seq_idx=None, relaxed=False):
+                seq_idx=None, relaxed=False, workspace_ready=False):
     """Run one SSD prefill on the GPU; returns (y[B,L,H,P], final_state[B,H,P,N]).
 
     ``state_dtype`` defaults to initial_state's dtype, else float32.  ``workspace``
@@ -211,7 +213,10 @@ def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_
     ``kernel_events`` = (begin, end) torch.cuda.Event(enable_timing=True) pair, recorded
     by the library around the SSD compute kernel(s) (ssd_prefill_timed).  ``seq_idx``
     (int32 [B, L]) packs several sequences per batch row: the recurrence restarts wherever
-    it changes (ssd_prefill_varlen).  ``relaxed``: CB stored in the 16-bit input type."""
+    it changes (ssd_prefill_varlen).  ``relaxed``: CB stored in the 16-bit input type.
+    ``workspace_ready``: SSD_FLAG_WORKSPACE_READY -- ``workspace`` is untouched since the previous
+    call with the same arguments' shapes and types (the library then skips the launch that
+    resets it when there is no initial state; it checks that the previous call matches)."""
     import torch
     _check_tensors(x, dt, A, B, C, D, dt_bias, initial_state)
     if seq_idx is not None:
@@ -225,7 +230,9 @@ def ssd_prefill(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None, chunk_
     sd = {torch.float32: SSD_F32, torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}[state_dtype]
     if initial_state is not None and initial_state.dtype != state_dtype:
         raise ValueError("initial_state dtype %s != state_dtype %s" % (initial_state.dtype, state_dtype))
-    prm = _params_for(x, B, chunk_size, sd, dt_softplus, impl, relaxed)
+    if workspace_ready and workspace is None:
+        raise ValueError("workspace_ready needs the workspace of the previous call")
+    prm = _params_for(x, B, chunk_size, sd, dt_softplus, impl, relaxed, FLAG_WORKSPACE_READY if workspace_ready else 0)
     Bt, L, H, P = x.shape
     N = B.shape[3]
     if y is None:

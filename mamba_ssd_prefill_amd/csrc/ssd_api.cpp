@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -104,7 +105,8 @@ size_t pair_slots_max(const ssd_params_t* p) { return (size_t)p->batch * p->ngro
 ssd_status_t validate(const ssd_params_t* p) {
     if (!p) return SSD_ERR_NULL_POINTER;
     if (p->struct_size < kParamsV1Size) return SSD_ERR_INVALID_ARGUMENT;
-    if (p->struct_size >= sizeof(ssd_params_t) && ((p->relaxed != 0 && p->relaxed != 1) || p->reserved != 0))
+    if (p->struct_size >= sizeof(ssd_params_t) &&
+        ((p->relaxed != 0 && p->relaxed != 1) || (p->flags & ~SSD_FLAG_WORKSPACE_READY) != 0))
         return SSD_ERR_INVALID_ARGUMENT;
     if (p->in_dtype < SSD_F32 || p->in_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
     if (p->state_dtype < SSD_F32 || p->state_dtype > SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
@@ -319,13 +321,77 @@ void set_partitions(const ssd_params_t* p, const Layout& l, const DevInfo& d, ss
     a.slots = a.relay ? l.w.state_slots : 1;
 }
 
-ssd_status_t check_ws(const ssd_params_t* p, void* ws, size_t ws_bytes, Layout* l) {
+// Workspaces whose synchronisation words the last fused call reset for the next one (in its
+// final-state copy), with what that call was: a call flagged SSD_FLAG_WORKSPACE_READY skips
+// the reset launch only when it is the same.  A few entries; the oldest is dropped.
+struct ReadyKey {
+    const void* ws;
+    ssd_params_t p;  // flags cleared
+    int relay, slots;
+    size_t nsync;
+    bool operator==(const ReadyKey& o) const {
+        return ws == o.ws && memcmp(&p, &o.p, sizeof(p)) == 0 && relay == o.relay && slots == o.slots &&
+               nsync == o.nsync;
+    }
+};
+constexpr int kReadyEntries = 16;
+std::mutex ready_mu;
+ReadyKey ready_tab[kReadyEntries];
+int ready_n = 0;
+
+ReadyKey ready_key(const ssd_params_t* p, const void* ws, int relay, int slots, size_t nsync) {
+    ReadyKey k;
+    memset(&k, 0, sizeof(k));
+    k.ws = ws;
+    memcpy(&k.p, p, p->struct_size < sizeof(k.p) ? p->struct_size : sizeof(k.p));
+    k.p.struct_size = sizeof(k.p);
+    k.p.flags = 0;
+    if (p->struct_size < sizeof(ssd_params_t)) k.p.relaxed = 0;
+    k.relay = relay;
+    k.slots = slots;
+    k.nsync = nsync;
+    return k;
+}
+
+// Drops the workspace's entry; returns whether it matched k.
+bool ready_take(const ReadyKey& k) {
+    std::lock_guard<std::mutex> lock(ready_mu);
+    for (int i = 0; i < ready_n; ++i) {
+        if (ready_tab[i].ws != k.ws) continue;
+        const bool same = ready_tab[i] == k;
+        ready_tab[i] = ready_tab[--ready_n];
+        return same;
+    }
+    return false;
+}
+
+void ready_drop(const void* ws) {
+    std::lock_guard<std::mutex> lock(ready_mu);
+    for (int i = 0; i < ready_n; ++i)
+        if (ready_tab[i].ws == ws) ready_tab[i] = ready_tab[--ready_n];
+}
+
+void ready_put(const ReadyKey& k) {
+    std::lock_guard<std::mutex> lock(ready_mu);
+    for (int i = 0; i < ready_n; ++i)
+        if (ready_tab[i].ws == k.ws) ready_tab[i] = ready_tab[--ready_n];
+    if (ready_n == kReadyEntries) {
+        for (int i = 1; i < ready_n; ++i) ready_tab[i - 1] = ready_tab[i];
+        --ready_n;
+    }
+    ready_tab[ready_n++] = k;
+}
+
+// Validates and lays out; a call that will write the workspace forgets that it was left ready
+// (keep_ready: the fused form, which looks the entry up itself).
+ssd_status_t check_ws(const ssd_params_t* p, void* ws, size_t ws_bytes, Layout* l, bool keep_ready = false) {
     ssd_status_t s = validate(p);
     if (s != SSD_OK) return s;
     if (!ws) return SSD_ERR_NULL_POINTER;
     if (!aligned(ws, kAlign)) return SSD_ERR_MISALIGNED;
     *l = layout(p);
     if (ws_bytes < l->w.total_bytes) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    if (!keep_ready) ready_drop(ws);
     return SSD_OK;
 }
 
@@ -475,7 +541,7 @@ ssd_status_t ssd::prefill_impl(const ssd_params_t* p, const void* x, const void*
                                hipEvent_t ev_begin, hipEvent_t ev_end, const int32_t* seq_idx,
                                const ssd::SeqStates& ss) {
     Layout l;
-    ssd_status_t s = check_ws(p, workspace, workspace_bytes, &l);
+    ssd_status_t s = check_ws(p, workspace, workspace_bytes, &l, p && p->impl == SSD_IMPL_FUSED);
     if (s != SSD_OK) return s;
     const bool seqst = ss.final_ != nullptr;
     if (seqst && p->in_dtype == SSD_F32) return SSD_ERR_UNSUPPORTED;
@@ -516,20 +582,30 @@ ssd_status_t ssd::prefill_impl(const ssd_params_t* p, const void* x, const void*
         }
         // initial state into the ring's slot 0; every sync word reset (chain counters to 1: the
         // state entering chunk 0 is ready -- in the relay form its relay waves publish it)
-        // the 16-bit tile keeps p in its interleaved order; the fp32 tile in plain order
+        // the 16-bit tile keeps p in its interleaved order; the fp32 tile in plain order.
+        // Skipped without an initial state when the previous call on this workspace, the same
+        // one, left the words reset (SSD_FLAG_WORKSPACE_READY).
         const int es = (int)elem_size(p->state_dtype), K = a.slots, pperm = p->in_dtype != SSD_F32;
         const int pw = ssd::p_per_wave(p->headdim);
-        e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, pw, p->dstate, K, 0,
-                                  es, pperm, a.flags, l.nsync, l.nflags, (uint32_t)ssd::kChainStride,
-                                  a.relay ? 0u : 1u, st);
+        const uint32_t flag_init = a.relay ? 0u : 1u;
+        const ReadyKey key = ready_key(p, workspace, a.relay, a.slots, l.nsync);
+        const bool was_ready = ready_take(key);  // (the entry stays dropped until this call's copy-out)
+        if (!(was_ready && (p->flags & SSD_FLAG_WORKSPACE_READY) && !initial_state && !seqst))
+            e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, pw, p->dstate, K,
+                                      0, es, pperm, a.flags, l.nsync, l.nflags, (uint32_t)ssd::kChainStride,
+                                      flag_init, ~(size_t)0, st);
         if (e == hipSuccess) e = mark(ev_begin);
         if (e == hipSuccess) e = dispatch(ssd::STEP_FUSED, p, a, st);
         if (e == hipSuccess) e = mark(ev_end);
-        // final state out of the last chunk's slot (the relay form keeps it in slot 1); with
-        // per-sequence states the kernel wrote every final state itself
-        if (e == hipSuccess && !seqst)
+        // final state out of the last chunk's slot (the relay form keeps it in slot 1), and every
+        // sync word but the status word reset for the next call; with per-sequence states the
+        // kernel wrote every final state itself
+        if (e == hipSuccess && !seqst) {
             e = ssd::launch_ring_copy(a.states, final_state, 0, p->batch, p->nheads, p->headdim, pw, p->dstate, K,
-                                      a.relay ? 1 : l.w.nchunks % K, es, pperm, nullptr, 0, 0, 1, 0u, st);
+                                      a.relay ? 1 : l.w.nchunks % K, es, pperm, a.flags, l.nsync, l.nflags,
+                                      (uint32_t)ssd::kChainStride, flag_init, l.status_w, st);
+            if (e == hipSuccess) ready_put(key);
+        }
         return hip_status(e);
     }
     e = mark(ev_begin);
@@ -756,6 +832,7 @@ SSD_EXPORT ssd_status_t ssd_prefill_block(const ssd_params_t* p, const void* xbc
     if (!(norm_eps >= 0.f)) return SSD_ERR_INVALID_ARGUMENT;
     const BlockLayout k = block_layout(p);
     if (workspace_bytes < k.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    ready_drop(workspace);  // this form always resets the sync words itself
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
     const size_t HP = (size_t)p->nheads * p->headdim, GN = (size_t)p->ngroups * p->dstate;
@@ -815,11 +892,11 @@ SSD_EXPORT ssd_status_t ssd_prefill_block(const ssd_params_t* p, const void* xbc
     const int pw = ssd::p_per_wave(p->headdim);
     e = ssd::launch_ring_copy(initial_state, a.states, 1, p->batch, p->nheads, p->headdim, pw, p->dstate, K, 0, es,
                               pperm, a.flags, k.nsync_total, l.nflags, (uint32_t)ssd::kChainStride,
-                              a.relay ? 0u : 1u, st);
+                              a.relay ? 0u : 1u, ~(size_t)0, st);
     if (e == hipSuccess) e = launch_block(ssd::STEP_FUSED, p, a, st);
     if (e == hipSuccess)
         e = ssd::launch_ring_copy(a.states, final_state, 0, p->batch, p->nheads, p->headdim, pw, p->dstate, K,
-                                  a.relay ? 1 : l.w.nchunks % K, es, pperm, nullptr, 0, 0, 1, 0u, st);
+                                  a.relay ? 1 : l.w.nchunks % K, es, pperm, nullptr, 0, 0, 1, 0u, ~(size_t)0, st);
     if (e != hipSuccess) return hip_status(e);
     if (!a.norm_fused) return ssd_gated_norm(p, yw, z, norm_w, norm_eps, out, stream);
     return SSD_OK;

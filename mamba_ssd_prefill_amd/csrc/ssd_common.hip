@@ -78,63 +78,62 @@ __global__ __launch_bounds__(256) void k_boundary(const char* src, size_t src_bs
 // copies slot `slot` out to dst (src == nullptr: no initial state, nothing is copied).  One
 // thread per 4 consecutive n of one (b, h, p).  pperm = 1:
 // the 16-bit tile's interleaved p order (Geo16::pcol), else p block pb = pw / 16, lane pw % 16.  Also
-// resets nsync sync words: word i becomes flag_init when i < nflags and i % flag_period < 4
-// (the progress counters of every chain, one per relay wave: 1 = the state entering chunk 0
-// is ready), else 0.
+// resets nsync sync words, all but word `keep`: word i becomes flag_init when i < nflags and
+// i % flag_period < 4 (the progress counters of every chain, one per relay wave: 1 = the state
+// entering chunk 0 is ready), else 0.  The final-state copy does this for the next call.
 __global__ __launch_bounds__(256) void k_ring_copy(const char* src, char* dst, int to_ring, int B, int H, int P,
                                                     int PW, int N, int K, int slot, int es, int pperm,
                                                     uint32_t* sync, size_t nsync, size_t nflags,
-                                                    uint32_t flag_period, uint32_t flag_init) {
+                                                    uint32_t flag_period, uint32_t flag_init, size_t keep) {
     const int WPH = P / PW, MBP = PW / 16, NB = N / 16;
     const int n4 = N / 4, per_bh = P * n4;  // items (4 consecutive n) per (b, h); P, N powers of 2
-    const int nsh = __builtin_ctz((unsigned)n4);
+    const int nsh = __builtin_ctz((unsigned)n4), bsh = __builtin_ctz((unsigned)per_bh);
     // no initial state: the fused kernel never reads slot 0 before writing it, so nothing to copy
-    const size_t nbh = (to_ring && src == nullptr) ? 0 : (size_t)B * H;
-    // one workgroup per (b, h) at a time, 32-bit index arithmetic inside it
-    for (size_t bh = blockIdx.x; bh < nbh; bh += gridDim.x) {
+    const size_t items = (to_ring && src == nullptr) ? 0 : (size_t)B * H * per_bh;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < items; i += stride) {
+        const size_t bh = i >> bsh;
+        const int e = (int)(i & (size_t)(per_bh - 1));
         const int b = (int)(bh / (size_t)H), h = (int)(bh - (size_t)b * H);
-        const size_t user0 = bh * P * N;
-        for (int e = threadIdx.x; e < per_bh; e += 256) {
-            const int p = e >> nsh, n = (e & (n4 - 1)) * 4;
-            const int ph = p / PW, pw = p - ph * PW;
-            int pb = pw >> 4, r16 = pw & 15;
-            if (pperm) {
-                const int q8 = pw / (4 * MBP), rem = pw - q8 * 4 * MBP;
-                pb = rem >> 2;
-                r16 = 4 * q8 + (rem & 3);
-            }
-            const int nb = n >> 4, q = (n & 15) >> 2;
-            const size_t ring =
-                ring_chain(b, slot, h, ph, K, H, WPH, NB * MBP) + (size_t)(((nb * MBP + pb) * 64 + 16 * q + r16) * 4);
-            const size_t user = user0 + (size_t)(p * N + n);
-            const size_t from = to_ring ? user : ring, to = to_ring ? ring : user;
-            if (es == 4) {
-                uint4 v = {0u, 0u, 0u, 0u};
-                if (src) v = *(const uint4*)(src + from * 4);
-                *(uint4*)(dst + to * 4) = v;
-            } else {
-                uint2 v = {0u, 0u};
-                if (src) v = *(const uint2*)(src + from * 2);
-                *(uint2*)(dst + to * 2) = v;
-            }
+        const int p = e >> nsh, n = (e & (n4 - 1)) * 4;
+        const int ph = p / PW, pw = p - ph * PW;
+        int pb = pw >> 4, r16 = pw & 15;
+        if (pperm) {
+            const int q8 = pw / (4 * MBP), rem = pw - q8 * 4 * MBP;
+            pb = rem >> 2;
+            r16 = 4 * q8 + (rem & 3);
+        }
+        const int nb = n >> 4, q = (n & 15) >> 2;
+        const size_t ring =
+            ring_chain(b, slot, h, ph, K, H, WPH, NB * MBP) + (size_t)(((nb * MBP + pb) * 64 + 16 * q + r16) * 4);
+        const size_t user = bh * P * N + (size_t)(p * N + n);
+        const size_t from = to_ring ? user : ring, to = to_ring ? ring : user;
+        if (es == 4) {
+            uint4 v = {0u, 0u, 0u, 0u};
+            if (src) v = *(const uint4*)(src + from * 4);
+            *(uint4*)(dst + to * 4) = v;
+        } else {
+            uint2 v = {0u, 0u};
+            if (src) v = *(const uint2*)(src + from * 2);
+            *(uint2*)(dst + to * 2) = v;
         }
     }
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsync; i += stride)
-        sync[i] = (i < nflags && (i % flag_period) < 4u) ? flag_init : 0u;
+        if (i != keep) sync[i] = (i < nflags && (i % flag_period) < 4u) ? flag_init : 0u;
 }
 
 hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int PW, int N, int K,
                             int slot, int es, int pperm, uint32_t* sync, size_t nsync, size_t nflags,
-                            uint32_t flag_period, uint32_t flag_init, hipStream_t st) {
-    const size_t bh = (size_t)B * H, sync_blocks = (nsync + 255) / 256;
-    size_t grid = bh > sync_blocks ? bh : sync_blocks;
+                            uint32_t flag_period, uint32_t flag_init, size_t keep, hipStream_t st) {
+    const size_t items = (to_ring && src == nullptr) ? 0 : (size_t)B * H * P * (N / 4);
+    const size_t big = items > nsync ? items : nsync;
+    size_t grid = (big + 255) / 256;
     if (grid < 1) grid = 1;
     if (grid > 8192) grid = 8192;
     const char* s = (const char*)src;
     char* d = (char*)dst;
     void* args[] = {&s, &d, &to_ring, &B, &H, &P, &PW, &N, &K, &slot, &es, &pperm, &sync, &nsync, &nflags,
-                    &flag_period, &flag_init};
+                    &flag_period, &flag_init, &keep};
     return hipLaunchKernel((const void*)&k_ring_copy, dim3((unsigned)grid), dim3(256), args, 0, st);
 }
 

@@ -199,9 +199,11 @@ hipError_t launch_gated_norm(NormArgs& a, int in_dtype, hipStream_t st);
 
 // Non-templated kernels (ssd_common.hip).
 hipError_t launch_state_passing(SsdArgs& a, int PN, hipStream_t st);
+// keep: index of a sync word left as it is (the status word, when the final-state copy resets
+// the words for the next call), ~0 for none.
 hipError_t launch_ring_copy(const void* src, void* dst, int to_ring, int B, int H, int P, int PW, int N, int K,
                             int slot, int es, int pperm, uint32_t* sync, size_t nsync, size_t nflags,
-                            uint32_t flag_period, uint32_t flag_init, hipStream_t st);
+                            uint32_t flag_period, uint32_t flag_init, size_t keep, hipStream_t st);
 hipError_t launch_boundary(const void* src, size_t src_bs, void* dst, size_t dst_bs, size_t bytes_per_b,
                            int batch, uint32_t* sync, size_t nsync, size_t nflags, uint32_t flag_period,
                            hipStream_t st);

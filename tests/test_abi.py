@@ -108,11 +108,11 @@ def test_validate_rejects_short_struct_and_null(lib):
 def test_params_abi_version_1_and_relaxed_field(lib):
     """A caller built against ABI version 1 passes the struct size that ends before `relaxed`
     (56 bytes on LP64): accepted, with relaxed = 0 whatever the trailing bytes hold.  With the
-    full struct, relaxed must be 0 or 1 and reserved 0; relaxed halves the CB region (16-bit
-    inputs only)."""
+    full struct, relaxed must be 0 or 1 and flags 0 or SSD_FLAG_WORKSPACE_READY; relaxed halves
+    the CB region (16-bit inputs only)."""
     p = base()
     p.struct_size = ssd.Params.relaxed.offset
-    p.relaxed, p.reserved = 7, 9  # not read with the version-1 size
+    p.relaxed, p.flags = 7, 9  # not read with the version-1 size
     assert lib.ssd_validate(ctypes.byref(p)) == OK
     p.struct_size = ssd.Params.relaxed.offset - 4
     assert lib.ssd_validate(ctypes.byref(p)) == BADARG
@@ -120,8 +120,12 @@ def test_params_abi_version_1_and_relaxed_field(lib):
     q.relaxed = 2
     assert lib.ssd_validate(ctypes.byref(q)) == BADARG
     q = base()
-    q.reserved = 1
-    assert lib.ssd_validate(ctypes.byref(q)) == BADARG
+    q.flags = ssd.FLAG_WORKSPACE_READY
+    assert lib.ssd_validate(ctypes.byref(q)) == OK
+    assert ssd.workspace_size(q) == ssd.workspace_size(base())  # the flag changes no size
+    for bad in (2, 4, -1):
+        q.flags = bad
+        assert lib.ssd_validate(ctypes.byref(q)) == BADARG
     for impl in ("fused", "unfused"):
         exact = ssd.workspace_layout(base(impl=impl))
         rel = ssd.workspace_layout(base(impl=impl, relaxed=True))
