@@ -74,11 +74,21 @@ template <typename T, int P, int N, int Q> struct Geo16 {
 };
 
 // Swizzle of the 16-byte piece index inside a row of CH pieces.  A transposed operand read
-// touches rows k0 + 8q + m (q, m = 0..3, k0 a multiple of 32; the second read adds 4); the
-// swizzle sends those 16 rows to distinct 16-byte bank groups of a 256-byte bank line.
+// touches rows k0 + 8q + m (q, m = 0..3, k0 a multiple of 32; the second read adds 4), each lane
+// 8 bytes, the four lanes of a row 32 contiguous bytes before the swizzle.  The LDS serves such a
+// read (and ds_read_b64) 32 lanes per cycle -- lanes 0-31 are the rows with q = 0, 1 -- from 64
+// four-byte banks (a 256-byte bank line); measured on MI355X with rocprofv3's
+// SQ_LDS_BANK_CONFLICT.  So the swizzle must spread the 8 rows of each half-wave apart:
+//   CH = 16 (256-byte rows, one bank line each): s = 2m + 8(q & 1) + (q >> 1) puts those 8 rows
+//           on 8 distinct 32-byte pairs of pieces (a row's two pieces stay one aligned pair);
+//   CH = 8 (128-byte rows, two per line): s = 2(m >> 1) + 4(q & 1) + (q >> 1) with the row's
+//           line half (bit 0) spreads them over the line's 16 pieces;
+// the 16-row row-wise reads of the D x term (16 bytes a lane) measured conflict-free with the
+// CH = 8 form too.  Neither depends on row bit 2 (the +4) or bits 5 and up (k0).
 template <int CH> __device__ inline int swz(int row) {
-    if constexpr (CH >= 16) return ((row & 3) | ((row >> 1) & 12)) & (CH - 1);
-    else if constexpr (CH == 8) return ((row >> 1) & 1) | ((row >> 2) & 6);  // 2 rows per bank line
+    const int m = row & 3, q = (row >> 3) & 3;
+    if constexpr (CH >= 16) return ((m << 1) | ((q & 1) << 3) | (q >> 1)) & (CH - 1);
+    else if constexpr (CH == 8) return ((m >> 1) << 1) | ((q & 1) << 2) | (q >> 1);
     else if constexpr (CH == 4) return (row >> 3) & 3;                        // 4 rows per bank line
     else return (row >> 3) & 1;
 }
@@ -959,10 +969,16 @@ __device__ void chunk_tile16(const SsdArgs& a, int b, int c, int g, int tig, cha
             f32x4 accY[MBP];
 #pragma unroll
             for (int pb = 0; pb < MBP; ++pb) accY[pb] = vzero<f32x4>();
+            // The row block's offset is hidden from the compiler so that it keeps the C reads
+            // single ds_read_b64 (32 lanes a cycle, conflict-free with the row swizzle) instead of
+            // merging the reads of two row blocks into ds_read2st64_b64, which the LDS serves 16
+            // lanes a cycle (measured: four times the cycles of the two reads apart).
+            int cblk = ib * 16 * N;
+            asm volatile("" : "+v"(cblk));
 #pragma unroll
             for (int ks = 0; ks < N / 32; ++ks) {
-                const v4 lo = *(const v4*)(sBC + clo[ks] + ib * 16 * N);
-                const v4 hi = *(const v4*)(sBC + chi[ks] + ib * 16 * N);
+                const v4 lo = *(const v4*)(sBC + clo[ks] + cblk);
+                const v4 hi = *(const v4*)(sBC + chi[ks] + cblk);
                 const frag cf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int pb = 0; pb < MBP; ++pb) accY[pb] = TT<T>::mma(sop[ks][pb], cf, accY[pb]);
