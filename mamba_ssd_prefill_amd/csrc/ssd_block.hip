@@ -117,6 +117,52 @@ template <typename T> __global__ __launch_bounds__(256) void k_gated_norm(NormAr
     }
 }
 
+// The same in one pass when a wave's share of the group fits in registers (at most MAXP pieces
+// per lane): y silu(z) of every piece is kept in fp32 while the wave sums its squares, so y and
+// z are read once.  The per-element values and the order of the sum are those of k_gated_norm,
+// so the results are bit-identical.
+template <typename T, int MAXP> __global__ __launch_bounds__(256) void k_gated_norm1(NormArgs a) {
+    typedef typename TT<T>::v8 v8;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, group)
+    if (row >= (int64_t)a.rows * a.groups) return;
+    const int cg = a.hp / a.groups, np = cg / 8;
+    const int64_t tok = row / a.groups;
+    const int g = (int)(row % a.groups);
+    const size_t base = (size_t)tok * a.hp + (size_t)g * cg;
+    const T* yp = (const T*)a.y + base;
+    const T* zp = (const T*)a.z + base;
+    float gv[MAXP][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+        const int pc = lane + 64 * k;
+        if (pc < np) {
+            const v8 yv = *(const v8*)(yp + pc * 8), zv = *(const v8*)(zp + pc * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gv[k][e] = (float)yv[e] * silu_f((float)zv[e]);
+                ss += gv[k][e] * gv[k][e];
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float rs = __builtin_amdgcn_rsqf(ss / (float)cg + a.eps);
+    T* op = (T*)a.out + base;
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+        const int pc = lane + 64 * k;
+        if (pc < np) {
+            const f32x4 w0 = *(const f32x4*)(a.w + g * cg + pc * 8), w1 = *(const f32x4*)(a.w + g * cg + pc * 8 + 4);
+            v8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (T)(gv[k][e] * rs * (e < 4 ? w0[e] : w1[e - 4]));
+            *(v8*)(op + pc * 8) = o;
+        }
+    }
+}
+
 template <typename T> hipError_t launch_conv_t(ConvArgs& a, hipStream_t st) {
     const int npc = (a.hp + 2 * a.gn) / 8;
     const int64_t items = (int64_t)a.batch * ((a.seqlen + kConvRows - 1) / kConvRows) * npc;
@@ -127,8 +173,12 @@ template <typename T> hipError_t launch_conv_t(ConvArgs& a, hipStream_t st) {
 
 template <typename T> hipError_t launch_norm_t(NormArgs& a, hipStream_t st) {
     const int64_t waves = (int64_t)a.rows * a.groups;
+    const int ppl = (a.hp / a.groups / 8 + 63) / 64;  // pieces per lane
+    const void* fn = ppl <= 4 ? (const void*)&k_gated_norm1<T, 4>
+                   : ppl <= 8 ? (const void*)&k_gated_norm1<T, 8>
+                   : ppl <= 12 ? (const void*)&k_gated_norm1<T, 12> : (const void*)&k_gated_norm<T>;
     void* args[] = {&a};
-    return hipLaunchKernel((const void*)&k_gated_norm<T>, dim3((unsigned)((waves + 3) / 4)), dim3(256), args, 0, st);
+    return hipLaunchKernel(fn, dim3((unsigned)((waves + 3) / 4)), dim3(256), args, 0, st);
 }
 
 hipError_t launch_conv_silu(ConvArgs& a, int in_dtype, hipStream_t st) {

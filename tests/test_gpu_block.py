@@ -59,13 +59,17 @@ def test_conv_silu_kernel():
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
 
 
-def test_gated_norm_kernel():
-    Bt, L, H, P, G = 2, 33, 8, 64, 2
-    gen = torch.Generator().manual_seed(5)
+# (H, P, G): a group's pieces of 8 channels per lane of its wave are 1 (ragged), 2 (ragged), 4,
+# 8, 10 (the 2.7B block's one group of 5120 channels) and 16 (the two-pass kernel)
+@pytest.mark.parametrize("H,P,G", [(8, 64, 2), (25, 32, 1), (32, 64, 1), (64, 64, 1), (80, 64, 1),
+                                   (128, 64, 1)], ids=lambda v: str(v))
+def test_gated_norm_kernel(H, P, G):
+    Bt, L = 2, 33
+    gen = torch.Generator().manual_seed(5 + H + G)
     y = torch.randn(Bt, L, H * P, generator=gen).to(torch.bfloat16)
     z = torch.randn(Bt, L, H * P, generator=gen).to(torch.bfloat16)
     w = 1.0 + 0.1 * torch.randn(H * P, generator=gen)
-    say("gated_norm")
+    say("gated_norm H=%d P=%d G=%d" % (H, P, G))
     out = ssd.gated_norm(y.cuda(), z.cuda(), w.cuda(), EPS, nheads=H, headdim=P, ngroups=G)
     torch.cuda.synchronize()
     ref = oracle.gated_rmsnorm(y, z, w, EPS, G)
