@@ -94,6 +94,8 @@ typedef struct {
  * parameters of the last call that left it ready; when they differ, or the last call on the
  * workspace was not such a call, the bit is ignored and the words are reset as usual.  A caller
  * who wrote to the workspace in between, or freed and re-allocated it, must not set the bit.
+ * As with any reuse of one workspace, the calls must be ordered on the device (one stream, or
+ * the earlier call complete before the later one starts).
  * The device status word (ssd_check_device_status) is cleared only by a call that resets the
  * words: after an error, calls with this bit keep reporting it until a call without the bit. */
 #define SSD_FLAG_WORKSPACE_READY 1
