@@ -160,6 +160,20 @@ def test_fused_is_deterministic_and_matches_unfused(form):
     gate(f64(f1), f64(fu), "f32", "bf16", name="fused vs unfused final")
 
 
+@pytest.mark.parametrize("group", [1, 3, 7])
+def test_claim_groups_change_nothing(group, monkeypatch):
+    """Chains claimed in groups (MAMBA_SSD_CHAIN_GROUP; chosen automatically for many short
+    chains) give the same bits as one group: only the order of the claims changes."""
+    # 4 batch rows x 2 groups x 4 two-head tiles = 32 chains (4 per partition), 8 chunks
+    inp = make_inputs(4, 1000, 16, 64, 128, 2, dtype="bf16", has_h0=True, seed=12)
+    say("claim groups", group)
+    y0, f0 = run_gpu(inp, 128, "fused_hop")
+    monkeypatch.setenv("MAMBA_SSD_CHAIN_GROUP", str(group))
+    y1, f1 = run_gpu(inp, 128, "fused_hop")
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    check_full(inp, y1, f1, "claim groups %d" % group)
+
+
 def test_workspace_reuse_across_shapes():
     """A workspace sized for a larger call is reused for a smaller one (flags reset)."""
     big = make_inputs(1, 1024, 8, 64, 128, 1, dtype="bf16", has_h0=True, seed=10)
