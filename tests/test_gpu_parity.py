@@ -160,13 +160,14 @@ def test_fused_is_deterministic_and_matches_unfused(form):
     gate(f64(f1), f64(fu), "f32", "bf16", name="fused vs unfused final")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("group", [1, 3, 7])
-def test_claim_groups_change_nothing(group, monkeypatch):
+def test_claim_groups_change_nothing(group, dtype, monkeypatch):
     """Chains claimed in groups (MAMBA_SSD_CHAIN_GROUP; chosen automatically for many short
     chains) give the same bits as one group: only the order of the claims changes."""
-    # 4 batch rows x 2 groups x 4 two-head tiles = 32 chains (4 per partition), 8 chunks
-    inp = make_inputs(4, 1000, 16, 64, 128, 2, dtype="bf16", has_h0=True, seed=12)
-    say("claim groups", group)
+    # 4 batch rows x 2 groups x 16 heads: 32 two-head chains (4 per partition) at 16 bits, 8 chunks
+    inp = make_inputs(4, 1000, 16, 64, 128, 2, dtype=dtype, has_h0=True, seed=12)
+    say("claim groups", group, dtype)
     y0, f0 = run_gpu(inp, 128, "fused_hop")
     monkeypatch.setenv("MAMBA_SSD_CHAIN_GROUP", str(group))
     y1, f1 = run_gpu(inp, 128, "fused_hop")
