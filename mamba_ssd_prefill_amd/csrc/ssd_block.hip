@@ -2,32 +2,38 @@
 // causal depthwise convolution with SiLU before it and the gated RMS norm after it
 // ("Mamba-2炸裂升级！…", section "未来展望与应用拓展": these are the operations before and after
 // the SSD that a deeper fusion takes into the SSD launch; the fused form is in ssd_tile16.h).
-// Both are HBM-bound streams: 16-byte pieces of 8 channels per lane, consecutive lanes on
-// consecutive pieces of a token row.  16-bit inputs only.
+// Both are HBM-bound streams: each lane owns a piece of consecutive channels of a token row and
+// consecutive lanes take consecutive pieces.  16-bit inputs only.
 #include "ssd_device.h"
 
 namespace ssd {
 
 // conv: out[b,t,ch] = silu(bias[ch] + sum_k w[ch][k] * in[b, t-3+k, ch]), K = 4, where
-// in[b, t<0, ch] = state[b][ch][t+3] (zeros without a state).  Each lane owns the 8 channels of
-// one 16-byte piece over kConvRows consecutive tokens and slides a 3-row window down them.  The
+// in[b, t<0, ch] = state[b][ch][t+3] (zeros without a state).  Each lane owns kConvCW channels
+// (one 8-byte piece) over kConvRows consecutive tokens and slides a 3-row window down them.  The
 // output goes to x [B,L,H*P], B [B,L,G*N] or C [B,L,G*N] by channel range (H*P and G*N are
-// multiples of 8, so a piece never straddles two of them).
+// multiples of 8, so a piece never straddles two of them).  Measured on MI355X: 4 channels per
+// lane (50 registers instead of 84, so more waves in flight) beat 8 by a fifth of the kernel's time,
+// and 2 channels per lane were slower again.
 constexpr int kConvRows = 16;
+constexpr int kConvCW = 4;  // channels per lane
 
-template <typename T> __global__ __launch_bounds__(256) void k_conv_silu(ConvArgs a) {
-    typedef typename TT<T>::v8 v8;
-    const int ch = a.hp + 2 * a.gn, npc = ch / 8, L = a.seqlen;
+template <typename T, int CW> struct ConvVec { typedef typename TT<T>::v8 type; };
+template <typename T> struct ConvVec<T, 4> { typedef typename TT<T>::v4 type; };
+
+template <typename T, int CW> __global__ __launch_bounds__(256) void k_conv_silu(ConvArgs a) {
+    typedef typename ConvVec<T, CW>::type v8;
+    const int ch = a.hp + 2 * a.gn, npc = ch / CW, L = a.seqlen;
     const int nseg = (L + kConvRows - 1) / kConvRows;
     const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (item >= (int64_t)a.batch * nseg * npc) return;
     const int pc = (int)(item % npc);
     const int seg = (int)((item / npc) % nseg);
     const int b = (int)(item / ((int64_t)npc * nseg));
-    const int c0 = pc * 8, t0 = seg * kConvRows;
-    float w[4][8], bias[8], win[3][8];
+    const int c0 = pc * CW, t0 = seg * kConvRows;
+    float w[4][CW], bias[CW], win[3][CW];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < CW; ++e) {
         const f32x4 wv = *(const f32x4*)(a.w + (size_t)(c0 + e) * 4);
 #pragma unroll
         for (int k = 0; k < 4; ++k) w[k][e] = wv[k];
@@ -40,10 +46,10 @@ template <typename T> __global__ __launch_bounds__(256) void k_conv_silu(ConvArg
         if (t >= 0) {
             const v8 v = *(const v8*)(src + (size_t)t * ch);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) win[r][e] = (float)v[e];
+            for (int e = 0; e < CW; ++e) win[r][e] = (float)v[e];
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+            for (int e = 0; e < CW; ++e)
                 win[r][e] = a.state ? (float)((const T*)a.state)[((size_t)b * ch + c0 + e) * 3 + (t + 3)] : 0.f;
         }
     }
@@ -65,7 +71,7 @@ template <typename T> __global__ __launch_bounds__(256) void k_conv_silu(ConvArg
         const v8 v = *(const v8*)(src + (size_t)t * ch);
         v8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < CW; ++e) {
             const float cur = (float)v[e];
             const float s = bias[e] + w[0][e] * win[0][e] + w[1][e] * win[1][e] + w[2][e] * win[2][e] + w[3][e] * cur;
             o[e] = (T)silu_f(s);
@@ -164,11 +170,11 @@ template <typename T, int MAXP> __global__ __launch_bounds__(256) void k_gated_n
 }
 
 template <typename T> hipError_t launch_conv_t(ConvArgs& a, hipStream_t st) {
-    const int npc = (a.hp + 2 * a.gn) / 8;
+    const int npc = (a.hp + 2 * a.gn) / kConvCW;
     const int64_t items = (int64_t)a.batch * ((a.seqlen + kConvRows - 1) / kConvRows) * npc;
     void* args[] = {&a};
-    return hipLaunchKernel((const void*)&k_conv_silu<T>, dim3((unsigned)((items + 255) / 256)), dim3(256), args, 0,
-                           st);
+    return hipLaunchKernel((const void*)&k_conv_silu<T, kConvCW>, dim3((unsigned)((items + 255) / 256)), dim3(256),
+                           args, 0, st);
 }
 
 template <typename T> hipError_t launch_norm_t(NormArgs& a, hipStream_t st) {
