@@ -350,8 +350,9 @@ inline hipError_t launch_fused(const void* fn, SsdArgs& a, hipStream_t st) {
     }
     const int per_xcd = (a.cu_count / a.nparts > 0 ? a.cu_count / a.nparts : 1) * a.fused_occ;
     const int wgs = per_xcd < a.part_max_work ? per_xcd : a.part_max_work;
-    // default: all of a partition's chains in one group (measured fastest: smaller groups keep
-    // fewer state slots live but serialise on the chunk-to-chunk hand-off)
+    // no group chosen on the host (set_partitions picks one only for many short chains): all of
+    // a partition's chains in one group (smaller groups keep fewer state slots live, but long
+    // chains then serialise on the chunk-to-chunk hand-off)
     if (a.chain_group <= 0) a.chain_group = 1 << 30;
     unsigned grid = (unsigned)(a.nparts * (wgs > 0 ? wgs : 1));
     const char* lim = getenv("MAMBA_SSD_GRID_LIMIT");  // test knob (see ssd_api.cpp)
