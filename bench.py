@@ -95,6 +95,35 @@ def time_impl(ssd, torch, g, w, Q, impl, steps, warmup, state_dtype=None, relaxe
     return wall, kms
 
 
+# warmup calls of each auxiliary leg (chunk sweep, fp16 state, precision points): each switches
+# kernels and buffers, and its first few calls run slower than the steady state
+SWEEP_WARMUP = 10
+
+
+def settle(ssd, torch, g, w, Q, seconds):
+    """Untimed fused and unfused calls, alternating, for about `seconds` before anything is
+    timed: a fresh process's first ~25 calls run up to 8 % slower (measured on MI355X: clocks
+    and first use of the buffers), so without this the first timed form would be measured
+    during that ramp and the second after it.  Both forms are then timed at steady state, after
+    their own warmup steps."""
+    sdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.state_dtype]
+    h0 = g.h0.to(sdt) if g.h0 is not None else None
+    y = torch.empty_like(g.x)
+    fin = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=sdt, device=g.x.device)
+    wss = {}
+    for impl in ("fused", "unfused"):
+        prm = ssd.make_params(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, Q, w.dtype,
+                              w.state_dtype, True, impl)
+        wss[impl] = ssd.alloc_workspace(prm, g.x.device)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for impl in ("fused", "unfused"):
+            ssd.ssd_prefill(g.x, g.dt, g.A, g.B, g.C, g.D, g.dt_bias, h0, chunk_size=Q, impl=impl,
+                            state_dtype=sdt, workspace=wss[impl], y=y, final_state=fin)
+        torch.cuda.synchronize()
+    del wss, y, fin
+
+
 def decode_bytes(w, batch):
     """Algorithmic HBM bytes of one decode step: the state read and written once, x, dt, B, C
     read and y written once, and the per-head parameters."""
@@ -325,6 +354,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle", type=float, default=0.25,
+                    help="seconds of untimed fused and unfused calls before the first timed form (0: none)")
     ap.add_argument("--workload", default="mamba2_2p7b_bf16")
     ap.add_argument("--chunk", type=int, default=0, help="chunk size (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -383,6 +414,8 @@ def main():
             torch.cuda.synchronize()
         return
 
+    log("settling (%.2f s of untimed fused and unfused calls)" % args.settle)
+    settle(ssd, torch, g, w, Q, args.settle)
     log("timing fused Q=%d" % Q)
     f_wall, f_kms = time_impl(ssd, torch, g, w, Q, "fused", args.steps, args.warmup)
     log("timing unfused Q=%d" % Q)
@@ -417,6 +450,7 @@ def main():
                     "mfma_tflops": flops / (u_kms / 1e3) / 1e12,
                     "mfma_frac": flops / (u_kms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]},
         "speedup_fused_vs_unfused": u_wall / f_wall,
+        "settle_s": args.settle,
     }
     if not args.no_sweep:
         sweep = {}
@@ -425,8 +459,8 @@ def main():
                 sweep[str(q)] = {"fused_ms": f_wall, "unfused_ms": u_wall}
                 continue
             log("sweep Q=%d" % q)
-            fw, fk = time_impl(ssd, torch, g, w, q, "fused", max(5, args.steps // 2), 2)
-            uw, uk = time_impl(ssd, torch, g, w, q, "unfused", max(5, args.steps // 2), 2)
+            fw, fk = time_impl(ssd, torch, g, w, q, "fused", max(10, args.steps // 2), SWEEP_WARMUP)
+            uw, uk = time_impl(ssd, torch, g, w, q, "unfused", max(10, args.steps // 2), SWEEP_WARMUP)
             sweep[str(q)] = {"fused_ms": fw, "unfused_ms": uw, "fused_kernel_ms": fk}
         for q, v in sweep.items():
             # the roofline fraction of the fused kernel at this chunk size (its own algorithmic bytes)
@@ -436,7 +470,7 @@ def main():
         if w.state_dtype == "f32" and w.dtype != "f32":
             # the same call with the inter-chunk states (and h0 / final state) stored in fp16
             log("fp16 state Q=%d" % Q)
-            hw, hk = time_impl(ssd, torch, g, w, Q, "fused", max(5, args.steps // 2), 2, state_dtype="f16")
+            hw, hk = time_impl(ssd, torch, g, w, Q, "fused", max(10, args.steps // 2), SWEEP_WARMUP, state_dtype="f16")
             c16, x16, _ = algorithmic(w.with_(state_dtype="f16"), Q, inp.h0 is not None)
             out["state_f16"] = {"fused_ms": hw, "fused_kernel_ms": hk, "value": tokens / (hw / 1e3),
                                 "frac": (c16 + x16) / (hk / 1e3) / 1e9 / HBM_PEAK_GBS}
@@ -451,7 +485,7 @@ def main():
                             prec[key] = {"fused_ms": f_wall, "fused_kernel_ms": f_kms}
                             continue
                         log("precision point %s" % key)
-                        pw, pk = time_impl(ssd, torch, g, w, q, "fused", max(5, args.steps // 2), 2,
+                        pw, pk = time_impl(ssd, torch, g, w, q, "fused", max(10, args.steps // 2), SWEEP_WARMUP,
                                            state_dtype=sd, relaxed=rel)
                         prec[key] = {"fused_ms": pw, "fused_kernel_ms": pk}
             for key, v in prec.items():
