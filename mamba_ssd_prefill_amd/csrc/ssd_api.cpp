@@ -94,7 +94,7 @@ struct Layout {
     size_t nflags, nsync;
     size_t flags_w, cs_w, bmm_w, ticket_w, owner_w, exit_w, abort_w, status_w;
     size_t agg_bytes;  // relay form: bytes of the chunk-state ring at the start of `s`
-    int tpg, wph, op_slots;
+    int tpg, wph, op_slots, agg_slots;
 };
 
 // Upper bound of the fused form's (b, g) pair slots: the B*G pairs, plus one more for every
@@ -151,7 +151,8 @@ Layout layout(const ssd_params_t* p) {
     w.cb_bytes = (fused ? PS : B * G) * nc * Q * Q * (cb16(p) ? 2 : 4);
     // relay form: the chunk-state ring (fp32) and then the operand ring (input dtype)
     l.op_slots = (int)(nc + 1 < (size_t)ssd::kRelaySlots ? nc + 1 : (size_t)ssd::kRelaySlots);
-    l.agg_bytes = B * H * P * N * (agg16(p) ? 2 : 4) * ssd::kAggSlots;
+    l.agg_slots = nc > (size_t)ssd::kLongChainChunks ? ssd::kAggSlotsLong : ssd::kAggSlots;
+    l.agg_bytes = B * H * P * N * (agg16(p) ? 2 : 4) * (size_t)l.agg_slots;
     w.s_bytes = fused ? (relay ? l.agg_bytes + B * H * P * N * elem_size(p->in_dtype) * l.op_slots : 0)
                       : B * nc * H * P * N * 4;
     w.states_bytes = B * K * H * P * N * elem_size(p->state_dtype);
@@ -237,6 +238,7 @@ ssd::SsdArgs make_args(const ssd_params_t* p, const Layout& l, void* ws) {
     a.state_dtype = p->state_dtype;
     a.softplus = p->dt_softplus;
     a.agg16 = agg16(p);
+    a.agg_slots = l.agg_slots;
     a.cb16 = cb16(p);
     a.spin_limit = spin_limit();
     a.x_stride = p->nheads * p->headdim;

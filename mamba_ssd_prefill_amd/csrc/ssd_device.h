@@ -416,7 +416,7 @@ __device__ inline void ring_store(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t 
 // nanoseconds, so moving a wave's 16 KB of state costs microseconds.  The relay form gives every
 // chain (b, h, p-slice) a dedicated state-passing item whose relay waves each keep a share of S
 // (whole accumulator tiles) in fp32 registers and stream the chunk states through:
-//   chunk tile c:  s_c -> chunk-state ring slot c % kAggSlots (fp32; fp16 with fp16 state
+//   chunk tile c:  s_c -> chunk-state ring slot c % agg_slots (fp32; fp16 with fp16 state
 //                  storage), slot word = c + 1; wait
 //                  until every relay wave's counter >= c + 1, read S_c (operand type) from
 //                  operand slot c % op_slots, read word = c + 1
@@ -427,7 +427,7 @@ __device__ inline void ring_store(__amdgpu_buffer_rsrc_t r, int dtype, uint32_t 
 // The tiles read S_c only as an MFMA operand, so the relay hands it over already rounded to
 // the operand type (half the bytes and instructions of fp32).  A chunk tile overwrites its
 // chunk-state slot only after every relay wave has used the previous occupant (counters >=
-// c - kAggSlots + 2); a relay wave overwrites an operand slot only after the tile that read the
+// c - agg_slots + 2); a relay wave overwrites an operand slot only after the tile that read the
 // previous occupant said so (read word).  A relay wave loads s_{c+1} while s_c is being folded
 // in and publishes S_c one chunk later, once its stores are known complete.  Both rings keep
 // each lane's 16-byte pieces contiguous (see ring_chain): a chunk-state slot holds the NT
@@ -450,9 +450,15 @@ __device__ inline size_t chain_index(const SsdArgs& a, int b, int h, int ph, int
 // The chunk-state ring slot of chain (b, h, ph): NT accumulator tiles of 64 lanes x 4 floats,
 // lane after lane as in ring_chain.  a.agg16: 4 fp16 instead, tiles 2u and 2u + 1 of a lane
 // side by side in its 16-byte unit u (unit u of lane l at byte (u * 64 + l) * 16).
+// c modulo the ring size, which is one of two constants (a division by an unknown divisor
+// would lengthen every step of the relay's serial chain)
+__device__ inline int agg_slot(const SsdArgs& a, int c) {
+    return a.agg_slots == kAggSlotsLong ? c % kAggSlotsLong : c % kAggSlots;
+}
+
 template <int NT> __device__ inline __amdgpu_buffer_rsrc_t agg_rsrc(const SsdArgs& a, int b, int h, int ph, int WPH,
                                                                      int slot) {
-    const size_t chain = chain_index(a, b, h, ph, WPH) * kAggSlots + slot;
+    const size_t chain = chain_index(a, b, h, ph, WPH) * a.agg_slots + slot;
     const int es = a.agg16 ? 2 : 4;
     return make_rsrc((const char*)a.s + chain * NT * 256 * es, NT * 256 * es);
 }
@@ -517,7 +523,7 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     // L(c): TPW loads of s_c, one of acs_c[Q-1] and (packed input) one of seg_c[Q-1], nonzero
     // when a sequence starts inside chunk c, which then passes no state on; into buf / d / sg
     auto issue_load = [&](int c, aggv (&buf)[NAL], float& d, uint32_t& sg) {
-        const __amdgpu_buffer_rsrc_t r = agg_rsrc<NT>(a, b, h, ph, WPH, c % kAggSlots);
+        const __amdgpu_buffer_rsrc_t r = agg_rsrc<NT>(a, b, h, ph, WPH, agg_slot(a, c));
         const __amdgpu_buffer_rsrc_t rnone = make_rsrc(a.s, 0u);
 #pragma unroll
         for (int t = 0; t < NAL; ++t) {
@@ -566,7 +572,7 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
                 wait_vm<0>();
                 raise_flag(my_cnt, (uint32_t)c + 1);
             }
-            const int n = wait_run(agg_words, kAggSlots, (uint32_t)c + 1, 0u, a);
+            const int n = wait_run(agg_words, a.agg_slots, (uint32_t)c + 1, 0u, a);
             if (n == 0) return false;
             agg_hi = c + 1 + n;
             asm volatile("" ::: "memory");
@@ -603,7 +609,7 @@ __device__ void relay_chain(const SsdArgs& a, int b, int h, int ph, int WPH, int
     };
     bool ok = true;
     {
-        const int n = wait_run(agg_words, kAggSlots, 0u, 0u, a);
+        const int n = wait_run(agg_words, a.agg_slots, 0u, 0u, a);
         ok = n > 0;
         agg_hi = n;
     }
@@ -630,9 +636,10 @@ __device__ inline bool relay_handoff(const SsdArgs& a, int b, int c, int h, int 
     typedef typename TT<T>::v4 v4;
     const uint32_t lane = (uint32_t)tid_here() & 63u;
     uint32_t* cnt = chain_counter(a, b, h, ph, WPH);
-    // the slot's previous chunk state (chunk c - kAggSlots) has been folded in
-    bool ok = c < kAggSlots || wait_words(cnt, RW, a, (uint32_t)(c - kAggSlots) + 2u);
-    const __amdgpu_buffer_rsrc_t ra = agg_rsrc<NT>(a, b, h, ph, WPH, c % kAggSlots);
+    // the slot's previous chunk state (chunk c - agg_slots) has been folded in
+    const int KA = a.agg_slots;
+    bool ok = c < KA || wait_words(cnt, RW, a, (uint32_t)(c - KA) + 2u);
+    const __amdgpu_buffer_rsrc_t ra = agg_rsrc<NT>(a, b, h, ph, WPH, agg_slot(a, c));
     if (a.agg16) {
         // tile t of this lane: 8 bytes at ((t / 2) * 64 + lane) * 16 + (t % 2) * 8
 #pragma unroll
@@ -653,7 +660,7 @@ __device__ inline bool relay_handoff(const SsdArgs& a, int b, int c, int h, int 
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[nb][pb]), ra,
                                                        ((uint32_t)(nb * MBP + pb) * 64 + lane) * 16, 0, 0);
     }
-    publish_flag_wave(cnt + kChainAggWords + c % kAggSlots, (uint32_t)c + 1);
+    publish_flag_wave(cnt + kChainAggWords + agg_slot(a, c), (uint32_t)c + 1);
     ok = wait_words(cnt, RW, a, (uint32_t)c + 1) && ok;
     const int KO = a.op_slots;
     const __amdgpu_buffer_rsrc_t rin = opnd_rsrc<T, NT>(a, b, h, ph, WPH, c % KO);

@@ -55,6 +55,7 @@ struct SsdArgs {
     int relay;          // fused form: relay waves per chain part (2 or 4), 0 = no relay items
     int relay_admit;    // fused relay form: 0 makes every partition decide "chunk tiles hop" (a test knob)
     int agg16;          // fused relay form: the chunk-state ring holds fp16 (fp16 state storage), else fp32
+    int agg_slots;      // fused relay form: chunk-state ring slots per chain part (<= kAggSlots)
     int cb16;           // relaxed intermediates: CB stored in the 16-bit input type instead of fp32
     // packed input with per-sequence states (ssd_prefill_varlen_states): a row's first token
     // starts a sequence too; seq_idx[b][t] in [0, nseq) numbers the sequence, whose initial
@@ -100,7 +101,13 @@ constexpr int kChainReadWords = 64;
 // 10 and 6 slots beat 32 and 16 by 4-5 % on the relay-form shapes; the chunk tiles run only a
 // few chunks ahead of the relay waves anyway).
 constexpr int kRelaySlots = 6;
-constexpr int kAggSlots = 10;
+constexpr int kAggSlots = 10;  // chunk-state ring slots per chain part (the most; SsdArgs::agg_slots)
+// Long chains (more than kLongChainChunks chunks) get a ring of kAggSlotsLong: measured on
+// MI355X, 4 slots against 10 take the 131K-token context from 2.41 to 2.29 ms and the packed
+// 32 x 1024-token batch from 1.13 to 1.05 ms, while the 32-chunk 130M layer is 2.5 % slower with
+// them (and 3 or 2 slots are slower everywhere).
+constexpr int kAggSlotsLong = 4;
+constexpr int kLongChainChunks = 64;
 
 
 enum : int {
